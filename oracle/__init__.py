@@ -1,0 +1,43 @@
+"""Float64 CPU oracle of the speculative-sampling verifier.
+
+TEST INFRASTRUCTURE, not product code: only tests/, __graft_entry__.smoke()
+and bench.py's cpu_baseline leg may import, call or execute it. It shares no
+code with the HIP library or its binding, and imports nothing from them.
+
+Parity status of each function (what pins it to something other than itself):
+  philox4x64_10      pinned: NumPy's independent Philox implementation.
+  row_distribution   pinned: brute-force threshold search on small rows,
+                     math.fsum normaliser, top_k=1 == argmax.
+  verify_sample      pinned: three-token worked example of "Drafters and
+                     Speculative Decoding" (rejection mass 0.40, residual
+                     0.75/0.25/0, final law = p); alpha = 0.8 invariants;
+                     closed form (1 - a^(g+1)) / (1 - a) and the survival form by
+                     Monte Carlo; chi-square of emitted tokens against p.
+  verify_greedy      pinned: brute-force loop over small rows.
+  first_token_law    pinned: the worked example's printed numbers.
+Parity unpinned (fixed by convention only, not by anything the pages print):
+the uniform layout, the tie rules of top-k, top-p and greedy, and the actual
+numbers of the alpha = 0.8 example (only its invariants are printed).
+"""
+
+from .philox import philox4x64_10, uniform, uniforms, word_to_uniform  # noqa: F401
+from .verifier import (  # noqa: F401
+    BOUNDARY_EPS,
+    FLAG_EMPTY,
+    FLAG_NONFINITE,
+    FLAG_Q_ZERO,
+    FLAG_RESIDUAL_ZERO,
+    FLAG_TOKEN_RANGE,
+    GreedyResult,
+    RowDist,
+    SampleResult,
+    Sampler,
+    accept,
+    first_token_law,
+    residual_weights,
+    row_distribution,
+    sample_categorical,
+    verify_block,
+    verify_greedy,
+    verify_sample,
+)
