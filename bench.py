@@ -1,0 +1,251 @@
+"""Throughput of the speculative-sampling verifier on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5]
+
+One step is one spec_verify_sample call (or spec_verify_greedy for the greedy
+workload) over the whole batch: ban-list preparation, row statistics of every
+target and draft row, the acceptance walk and the final draw. Inputs are
+synthetic (lossless_draft_verification_sample_amd.synth) and already resident
+in HBM; the timed loop rotates four device copies of them so the 256 MB
+Infinity Cache cannot serve repeated reads. Draft tokens are the stored,
+oracle-drawn proposals of tests/golden/proposals.json.
+
+Prints one JSON line. `value` is verified logit rows per second
+(B*(2*gamma+1) rows per sampling call). `roofline` rates the dominant kernel
+(row_stats, or greedy_argmax) on algorithmic bytes (every logit read once)
+divided by its average duration, measured with HIP events recorded by the
+library around each of its launches on the launch stream. `cpu_baseline` times
+the float64 oracle on a bounded sample of the same workload on one host core.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+COPIES = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_label(cfg):
+    trunc = []
+    if cfg.top_k:
+        trunc.append(f"top-k {cfg.top_k}")
+    if cfg.top_p < 1:
+        trunc.append(f"top-p {cfg.top_p}")
+    if cfg.n_banned:
+        trunc.append(f"{cfg.n_banned} banned ids")
+    t = ", ".join(trunc) or "no truncation"
+    if cfg.mode == "greedy":
+        return f"{cfg.name}: greedy B={cfg.B} gamma={cfg.gamma} V={cfg.V} {cfg.dtype}"
+    return (f"{cfg.name}: B={cfg.B} gamma={cfg.gamma} V={cfg.V} {cfg.dtype} "
+            f"T={cfg.temperature} {t}")
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lossless_draft_verification_sample_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel, workload):
+    """Counter-measured HBM bytes per launch, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(f"{kernel}/{workload}")
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, xs, budget_s):
+    """The float64 oracle, as it stands, on the first requests of the workload."""
+    import oracle
+    cfg = wl.cfg
+    n = 1
+    rows_per_req = (2 * cfg.gamma + 1) if cfg.mode == "sample" else (cfg.gamma + 1)
+    t_total, done = 0.0, 0
+    u_all = (np.array(oracle.uniforms(cfg.philox_seed, cfg.philox_offset, cfg.B, cfg.gamma))
+             if cfg.mode == "sample" else None)
+    while t_total < budget_s and done < cfg.B:
+        take = min(n, cfg.B - done)
+        sl = slice(done, done + take)
+        tgt = wl.target[sl].astype(np.float64)
+        if cfg.mode == "sample":
+            dft = wl.draft[sl].astype(np.float64)
+            u = u_all[sl]
+            s = oracle.Sampler(cfg.temperature, cfg.top_k, cfg.top_p)
+            t0 = time.perf_counter()
+            oracle.verify_sample(tgt, dft, xs[sl], u, s, s,
+                                 None if wl.banned is None else wl.banned[sl])
+        else:
+            t0 = time.perf_counter()
+            oracle.verify_greedy(tgt, xs[sl])
+        t_total += time.perf_counter() - t0
+        done += take
+        n = min(2 * n, 8)
+    rows = done * rows_per_req
+    return {"value": rows / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {cfg.B} requests ({rows} rows), float64 NumPy on one "
+                      f"host core, {t_total:.1f} s; bf16->f64 upcast not timed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c5")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the verifier shards over requests with no "
+              "communication, and multi-GPU runs are not part of this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lossless_draft_verification_sample_amd as sv
+    from lossless_draft_verification_sample_amd import synth
+
+    sv._lib.load()
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.config)
+    log(f"[bench] generating {workload_label(cfg)}")
+    t0 = time.perf_counter()
+    wl = synth.make_workload(cfg)
+    with open(os.path.join(ROOT, "tests", "golden", "proposals.json")) as f:
+        xs = np.array(json.load(f)[cfg.name]["tokens"], dtype=np.int32)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    def to_dev(bits, vals):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(vals).to(dev)
+
+    tgt0 = to_dev(wl.target_bits, wl.target)
+    copies = [tgt0] + [tgt0.clone() for _ in range(COPIES - 1)]
+    if cfg.mode == "sample":
+        dft0 = to_dev(wl.draft_bits, wl.draft)
+        dcopies = [dft0] + [dft0.clone() for _ in range(COPIES - 1)]
+        rows = cfg.B * (2 * cfg.gamma + 1)
+    else:
+        dcopies = [None] * COPIES
+        rows = cfg.B * (cfg.gamma + 1)
+    toks = torch.from_numpy(xs).to(dev)
+    bans = None if wl.banned is None else torch.from_numpy(wl.banned).to(dev)
+    samp = (cfg.temperature, cfg.top_k, cfg.top_p)
+    if cfg.mode == "sample":
+        ws = torch.empty(sv.spec_verify_workspace_bytes(cfg.B, cfg.gamma, cfg.V,
+                                                        0 if bans is None else bans.shape[1]),
+                         dtype=torch.uint8, device=dev)
+        out = sv.SampleOut(torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev),
+                           torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+                           torch.empty((cfg.B,), dtype=torch.int32, device=dev), None, None)
+    else:
+        out = sv.GreedyOut(torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev),
+                           torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+                           torch.empty((cfg.B,), dtype=torch.int32, device=dev))
+
+    def step(k):
+        c = k % COPIES
+        if cfg.mode == "sample":
+            sv.spec_verify_sample(copies[c], dcopies[c], toks, samp, samp, bans,
+                                  seed=cfg.philox_seed, offset=cfg.philox_offset,
+                                  workspace=ws, out=out)
+        else:
+            sv.spec_verify_greedy(copies[c], toks, out=out)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    sv.spec_verify_profile_start(args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    stop.record()
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(stop)
+    prof = sv.spec_verify_profile_stop()
+    log(f"[bench] timed loop {elapsed_ms:.2f} ms")
+
+    ms_step = elapsed_ms / args.steps
+    value = rows * args.steps / (elapsed_ms / 1e3)
+    s = 2 if cfg.dtype == "bf16" else 4
+    algo_bytes = rows * cfg.V * s
+    dom = "row_stats" if cfg.mode == "sample" else "greedy_argmax"
+    dom_ms, dom_n = prof[dom]
+    dom_avg_ms = dom_ms / max(dom_n, 1)
+    achieved = algo_bytes / (dom_avg_ms / 1e3) / 1e9
+    traffic = traffic_record(dom, cfg.name)
+
+    n_acc = out.num_accepted.cpu().numpy()
+    flags = out.flags.cpu().numpy()
+    res = {
+        "metric": "verified logit rows/sec",
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload_label(cfg), "B": cfg.B, "gamma": cfg.gamma, "V": cfg.V,
+                   "rows_per_step": rows, "algorithmic_bytes_per_step": algo_bytes,
+                   "parallelism": "single GPU"},
+        "hbm_gbps_step": algo_bytes / (ms_step / 1e3) / 1e9,
+        "hbm_frac_step": algo_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "avg_kernel_ms": dom_avg_ms, "launches": dom_n, "traffic": traffic},
+        "kernel_ms_per_step": {k: v[0] / v[1] for k, v in prof.items() if v[1]},
+        "mean_accepted": float(n_acc.mean()),
+        "mean_emitted_per_request": float(n_acc.mean() + 1),
+        "flags_nonzero": int((flags != 0).sum()),
+    }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2**20 // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(wl, xs, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

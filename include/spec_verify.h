@@ -1,0 +1,168 @@
+/*
+ * spec_verify.h - C interface of a lossless speculative-sampling verifier for
+ * AMD MI355X (gfx950).
+ *
+ * The operation is one verification round of speculative decoding for a batch
+ * of B independent requests:
+ *   - "Speculative Decoding - Turn guesses into parallel work", section "One
+ *     round and shifted logits": the drafter proposes gamma tokens together with
+ *     their proposal distributions q; one target pass yields gamma+1 target
+ *     distributions p (row i judges proposal i, row gamma serves the bonus token).
+ *   - same page, section "Exact sampling: account for every probability", and
+ *     "Speculative Token Decoupling ..." Equation 3.1: proposal i is accepted with
+ *     probability min(1, p_i(x_i) / q_i(x_i)); here: accept iff u_i * q_i(x_i) <=
+ *     p_i(x_i) with u_i uniform on (0, 1].
+ *   - "Drafters and Speculative Decoding: Useful Tokens, Correct State", section
+ *     "Sampling needs a correction rule": at the first rejection the replacement
+ *     is drawn from norm(max(0, p - q)); every later proposal is discarded.
+ *   - "Speculative Decoding" (specdec fundamentals), section "The Loop": if all
+ *     gamma proposals survive, one bonus token is drawn from p_gamma; every round
+ *     emits between 1 and gamma+1 tokens.
+ *   - "Speculative Decoding - Turn guesses into parallel work", section "Greedy,
+ *     sampling and the real sampler": temperature, truncation and token bans are
+ *     part of p and q, and the greedy variant accepts while the proposal equals
+ *     the target argmax ("Drafters and Speculative Decoding", section "Greedy
+ *     verification").
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is caller-owned memory. Logits, tokens, outputs and
+ *     workspace are DEVICE pointers on the current HIP device; sampler structs
+ *     are passed by value. The library allocates no device memory, frees
+ *     nothing, and keeps no pointer after returning.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ *     and never synchronise. Outputs are valid once the stream has reached the
+ *     call. Outputs must not alias inputs; concurrent calls need distinct
+ *     outputs and workspaces.
+ *   - Argument errors are detected on the host before anything is launched and
+ *     return a negative SV_E* code; nothing is written in that case. Problems
+ *     that can only be seen in the data are reported per request through the
+ *     SV_FLAG_* bits of out_flags.
+ *   - Logit rows are contiguous with row stride V elements. A logit of -inf
+ *     marks a token as impossible. NaN and +inf are data errors (flag
+ *     SV_FLAG_NONFINITE); the tokens of such a request are unspecified.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Sampler settings of one distribution (target or draft may differ).
+ *   temperature: > 0 and finite; logits are divided by it.
+ *   top_k:       0 = off; otherwise keep every token whose logit is >= the
+ *                k-th largest admissible logit (ties kept, so more than k
+ *                tokens may survive). k >= number of admissible tokens is off.
+ *   top_p:       1.0 = off; otherwise in (0, 1): keep token x when the tempered
+ *                probability mass of tokens with a strictly larger logit is
+ *                < top_p (the crossing token and its exact ties are kept).
+ * Order of transforms: bans, temperature, top-k, top-p, renormalise. */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+} sv_sampler;
+
+/* Return codes. */
+#define SV_OK 0
+#define SV_EINVAL (-1)     /* null required pointer, bad size or sampler field */
+#define SV_EDTYPE (-2)     /* dtype not SV_F32 / SV_BF16 */
+#define SV_EWORKSPACE (-3) /* workspace NULL or smaller than spec_verify_workspace_bytes */
+#define SV_ESIZE (-4)      /* sizes overflow the supported index ranges */
+#define SV_EHIP (-5)       /* a HIP launch or runtime call failed */
+
+/* Per-request flag bits written to out_flags. */
+#define SV_FLAG_TOKEN_RANGE 1u    /* some draft token lies outside [0, V) */
+#define SV_FLAG_Q_ZERO 2u         /* the proposal that ended the walk has q(x) = 0 */
+#define SV_FLAG_NONFINITE 4u      /* NaN or +inf in one of the request's rows */
+#define SV_FLAG_EMPTY 8u          /* a row has no admissible token; see out_tokens */
+#define SV_FLAG_RESIDUAL_ZERO 16u /* residual mass was 0 at a rejection; drawn from p */
+
+#define SV_MAX_BANNED 2048 /* largest n_banned accepted */
+
+/* Workspace bytes needed by spec_verify_sample for these sizes (0 on bad sizes).
+ * The workspace needs no initialisation and may be reused by later calls. */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t n_banned);
+
+/* Speculative-sampling verification.
+ *   target_logits  [B][gamma+1][V] of dtype; row i is the target distribution
+ *                  after the prefix and proposals 0..i-1, row gamma the bonus row.
+ *   draft_logits   [B][gamma][V] of dtype; row i is the distribution proposal i
+ *                  was sampled from (it must be the distribution that actually
+ *                  produced the token, after the drafter's own transforms).
+ *   draft_tokens   [B][gamma] int32 proposals.
+ *   banned_ids     [B][n_banned] int32 token ids removed from p AND q of every
+ *                  row of the request; -1 or any id outside [0, V) is padding;
+ *                  duplicates are allowed. NULL only when n_banned == 0.
+ *   target, draft  sampler settings for p and q respectively.
+ *   seed, offset   select the uniforms when `uniforms` is NULL: for request b
+ *                  and slot j (j < gamma: acceptance of proposal j; j == gamma:
+ *                  the single final draw) u = ((r >> 11) + 1) * 2^-53 with r the
+ *                  first output word of Philox4x64-10 at counter (j, b, offset, 0)
+ *                  and key (seed, 0) (Salmon et al., SC'11).
+ *   uniforms       [B][gamma+1] double in (0, 1] used instead of Philox, or NULL.
+ * Outputs:
+ *   out_tokens       [B][gamma+1] int32: the n accepted proposals, then the
+ *                    correction (n < gamma) or bonus (n == gamma) token, then -1
+ *                    padding. The emitted token is -1 when the distribution it
+ *                    must be drawn from is empty (SV_FLAG_EMPTY).
+ *   out_num_accepted [B] int32 n in [0, gamma].
+ *   out_flags        [B] uint32 SV_FLAG_* bits, or NULL.
+ *   out_target_lse   [B][gamma+1] float log-normaliser of each tempered target
+ *                    row over its kept set (-inf if empty), or NULL.
+ *   out_draft_lse    [B][gamma] float, same for the draft rows, or NULL.
+ *   workspace        device scratch of at least spec_verify_workspace_bytes(...)
+ *                    bytes, 256-byte aligned.
+ * Limits: 1 <= B, 1 <= gamma <= 63, 1 <= V < 2^31, B*(2*gamma+1) < 2^31,
+ * n_banned <= SV_MAX_BANNED; logit pointers aligned to their element size. */
+int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                       const int32_t* draft_tokens, const int32_t* banned_ids,
+                       int32_t n_banned, int32_t B, int32_t gamma, int32_t V,
+                       sv_sampler target, sv_sampler draft, uint64_t seed, uint64_t offset,
+                       const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
+                       uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Greedy verification ("Drafters and Speculative Decoding", section "Greedy
+ * verification"): proposal i is kept while it equals the argmax of target row i
+ * (largest logit, lowest token id on exact ties, -0 == +0); the first mismatch
+ * emits that row's argmax, and if all gamma match the argmax of row gamma is
+ * appended. Needs no workspace: out_tokens doubles as scratch.
+ *   target_logits [B][gamma+1][V], draft_tokens [B][gamma];
+ *   out_tokens [B][gamma+1] (n matches, argmax, then -1), out_num_accepted [B],
+ *   out_flags [B] or NULL (SV_FLAG_TOKEN_RANGE, SV_FLAG_NONFINITE).
+ * NaN logits are ignored by the argmax and flagged. */
+int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,
+                       int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                       int32_t* out_num_accepted, uint32_t* out_flags, void* stream);
+
+/* Static description of a status code. */
+const char* spec_verify_strerror(int status);
+
+/* Kernel-time accounting for benchmarks (host side, not thread-safe).
+ * spec_verify_profile_start(n) creates event pairs for up to n launches of each
+ * kernel; while active, every launch of the library records a HIP event pair
+ * around it on the caller's stream. spec_verify_profile_stop synchronises on
+ * those events, writes the summed milliseconds and launch counts of each
+ * kernel (arrays of SV_NUM_KERNELS entries, indices SV_K_*), and releases them. */
+#define SV_K_BAN_PREP 0
+#define SV_K_ROW_STATS 1
+#define SV_K_ACCEPT 2
+#define SV_K_RESIDUAL_PARTIAL 3
+#define SV_K_RESIDUAL_SELECT 4
+#define SV_K_GREEDY_ARGMAX 5
+#define SV_K_GREEDY_SCAN 6
+#define SV_NUM_KERNELS 7
+int spec_verify_profile_start(int32_t max_launches_per_kernel);
+int spec_verify_profile_stop(double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,189 @@
+"""Lossless speculative-sampling verifier for AMD MI355X (gfx950).
+
+Thin Python binding over the C interface of include/spec_verify.h. The
+functions below only marshal arguments (device pointers of torch tensors, the
+current HIP stream) and allocate outputs; every step of verification runs in
+the HIP kernels of libspecverify.so. PyTorch supplies device memory and
+streams. If the library is missing, every call raises.
+"""
+
+from collections import namedtuple
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    SV_BF16,
+    SV_EDTYPE,
+    SV_EHIP,
+    SV_EINVAL,
+    SV_ESIZE,
+    SV_EWORKSPACE,
+    SV_F32,
+    SV_FLAG_EMPTY,
+    SV_FLAG_NONFINITE,
+    SV_FLAG_Q_ZERO,
+    SV_FLAG_RESIDUAL_ZERO,
+    SV_FLAG_TOKEN_RANGE,
+    SV_MAX_BANNED,
+    SV_OK,
+    SvSampler,
+)
+
+SampleOut = namedtuple("SampleOut", "tokens num_accepted flags target_lse draft_lse")
+GreedyOut = namedtuple("GreedyOut", "tokens num_accepted flags")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {spec_verify_strerror(status)} (status {status})")
+        self.status = status
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _sampler(s):
+    if isinstance(s, SvSampler):
+        return s
+    if isinstance(s, dict):
+        return SvSampler(float(s.get("temperature", 1.0)), int(s.get("top_k", 0)),
+                         float(s.get("top_p", 1.0)))
+    t, k, p = s
+    return SvSampler(float(t), int(k), float(p))
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def spec_verify_strerror(status):
+    return _lib.load().spec_verify_strerror(int(status)).decode()
+
+
+def spec_verify_workspace_bytes(B, gamma, V, n_banned=0):
+    return int(_lib.load().spec_verify_workspace_bytes(int(B), int(gamma), int(V), int(n_banned)))
+
+
+def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler=(1.0, 0, 1.0),
+                       draft_sampler=(1.0, 0, 1.0), banned_ids=None, seed=0, offset=0,
+                       uniforms=None, want_lse=True, workspace=None, out=None, stream=None):
+    """Speculative-sampling verification of a batch (see include/spec_verify.h).
+
+    target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (bf16 or fp32),
+    draft_tokens [B, gamma] int32, banned_ids [B, n] int32 or None,
+    uniforms [B, gamma+1] float64 or None (then Philox(seed, offset)).
+    Samplers are (temperature, top_k, top_p) tuples, dicts or SvSampler.
+    Returns SampleOut(tokens, num_accepted, flags, target_lse, draft_lse).
+    """
+    torch = _torch()
+    lib = _lib.load()
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    if tuple(draft_logits.shape) != (B, gamma, V):
+        raise ValueError("draft_logits must be [B, gamma, V]")
+    if draft_logits.dtype != target_logits.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    if tuple(draft_tokens.shape) != (B, gamma):
+        raise ValueError("draft_tokens must be [B, gamma]")
+    dt = _dtype_code(target_logits)
+    n_banned = 0 if banned_ids is None else int(banned_ids.shape[1])
+    if banned_ids is not None and tuple(banned_ids.shape) != (B, n_banned):
+        raise ValueError("banned_ids must be [B, n_banned]")
+    if uniforms is not None and tuple(uniforms.shape) != (B, G1):
+        raise ValueError("uniforms must be [B, gamma+1]")
+    dev = target_logits.device
+    if out is None:
+        out = SampleOut(
+            torch.empty((B, G1), dtype=torch.int32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev),
+            torch.empty((B, G1), dtype=torch.float32, device=dev) if want_lse else None,
+            torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_lse else None,
+        )
+    need = lib.spec_verify_workspace_bytes(B, gamma, V, n_banned)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib.spec_verify_sample(
+        _dev_ptr(target_logits, "target_logits"), _dev_ptr(draft_logits, "draft_logits"), dt,
+        _dev_ptr(draft_tokens, "draft_tokens", torch.int32),
+        _dev_ptr(banned_ids, "banned_ids", torch.int32), n_banned, B, gamma, V,
+        _sampler(target_sampler), _sampler(draft_sampler), int(seed), int(offset),
+        _dev_ptr(uniforms, "uniforms", torch.float64),
+        _dev_ptr(out.tokens, "out_tokens", torch.int32),
+        _dev_ptr(out.num_accepted, "out_num_accepted", torch.int32),
+        _dev_ptr(out.flags, "out_flags", torch.int32),
+        _dev_ptr(out.target_lse, "out_target_lse", torch.float32),
+        _dev_ptr(out.draft_lse, "out_draft_lse", torch.float32),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_sample")
+    return out
+
+
+def spec_verify_greedy(target_logits, draft_tokens, out=None, stream=None):
+    """Greedy verification (see include/spec_verify.h). Returns GreedyOut."""
+    torch = _torch()
+    lib = _lib.load()
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    if tuple(draft_tokens.shape) != (B, gamma):
+        raise ValueError("draft_tokens must be [B, gamma]")
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    if out is None:
+        out = GreedyOut(torch.empty((B, G1), dtype=torch.int32, device=dev),
+                        torch.empty((B,), dtype=torch.int32, device=dev),
+                        torch.empty((B,), dtype=torch.int32, device=dev))
+    rc = lib.spec_verify_greedy(
+        _dev_ptr(target_logits, "target_logits"), dt,
+        _dev_ptr(draft_tokens, "draft_tokens", torch.int32), B, gamma, V,
+        _dev_ptr(out.tokens, "out_tokens", torch.int32),
+        _dev_ptr(out.num_accepted, "out_num_accepted", torch.int32),
+        _dev_ptr(out.flags, "out_flags", torch.int32), _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_greedy")
+    return out
+
+
+def spec_verify_profile_start(max_launches_per_kernel):
+    rc = _lib.load().spec_verify_profile_start(int(max_launches_per_kernel))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_profile_start")
+
+
+def spec_verify_profile_stop():
+    """Returns {kernel name: (total_ms, launches)} since spec_verify_profile_start."""
+    import ctypes
+    ms = (ctypes.c_double * _lib.SV_NUM_KERNELS)()
+    n = (ctypes.c_int32 * _lib.SV_NUM_KERNELS)()
+    rc = _lib.load().spec_verify_profile_stop(ctypes.cast(ms, ctypes.c_void_p),
+                                              ctypes.cast(n, ctypes.c_void_p))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_profile_stop")
+    return {name: (ms[k], n[k]) for k, name in enumerate(_lib.KERNEL_NAMES)}

@@ -1,0 +1,82 @@
+"""ctypes declarations of the C interface in include/spec_verify.h.
+
+Loading fails loudly when the HIP library has not been built; there is no
+fallback implementation.
+"""
+
+import ctypes
+import os
+
+LIB_NAME = "libspecverify.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+SV_F32 = 0
+SV_BF16 = 1
+
+SV_OK = 0
+SV_EINVAL = -1
+SV_EDTYPE = -2
+SV_EWORKSPACE = -3
+SV_ESIZE = -4
+SV_EHIP = -5
+
+SV_FLAG_TOKEN_RANGE = 1
+SV_FLAG_Q_ZERO = 2
+SV_FLAG_NONFINITE = 4
+SV_FLAG_EMPTY = 8
+SV_FLAG_RESIDUAL_ZERO = 16
+
+SV_MAX_BANNED = 2048
+
+SV_K_BAN_PREP = 0
+SV_K_ROW_STATS = 1
+SV_K_ACCEPT = 2
+SV_K_RESIDUAL_PARTIAL = 3
+SV_K_RESIDUAL_SELECT = 4
+SV_K_GREEDY_ARGMAX = 5
+SV_K_GREEDY_SCAN = 6
+SV_NUM_KERNELS = 7
+KERNEL_NAMES = ["ban_prep", "row_stats", "accept", "residual_partial", "residual_select",
+                "greedy_argmax", "greedy_scan"]
+
+
+class SvSampler(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float)]
+
+
+_c = ctypes
+_vp = _c.c_void_p
+_i32 = _c.c_int32
+_u64 = _c.c_uint64
+
+SIGNATURES = {
+    "spec_verify_workspace_bytes": (_c.c_size_t, [_i32, _i32, _i32, _i32]),
+    "spec_verify_sample": (_c.c_int, [
+        _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
+        _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]),
+    "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "spec_verify_strerror": (_c.c_char_p, [_c.c_int]),
+    "spec_verify_profile_start": (_c.c_int, [_i32]),
+    "spec_verify_profile_stop": (_c.c_int, [_vp, _vp]),
+}
+
+_LIB = None
+
+
+def load(path=LIB_PATH):
+    """The loaded library with argument types set (cached)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{LIB_NAME} is not built ({path}); run "
+            "`python -m lossless_draft_verification_sample_amd.build` or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib

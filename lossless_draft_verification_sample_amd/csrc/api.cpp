@@ -1,0 +1,278 @@
+// Host side of the C interface declared in include/spec_verify.h: argument
+// validation (before anything touches the device), workspace carving and the
+// kernel launch sequence on the caller's stream.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/spec_verify.h"
+#include "sv_launch.hpp"
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+struct Layout {
+  size_t stats, req, sums, bans, banc, total;
+  int nchunk;
+};
+
+bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
+  if (B < 1 || gamma < 1 || gamma > 63 || V < 1 || n_banned < 0 || n_banned > SV_MAX_BANNED)
+    return false;
+  const int64_t rows = (int64_t)B * (2 * (int64_t)gamma + 1);
+  if (rows >= INT32_MAX) return false;
+  const int64_t nchunk = ((int64_t)V + sv::DRAW_CHUNK - 1) / sv::DRAW_CHUNK;
+  if ((int64_t)B * nchunk >= INT32_MAX) return false;
+  L->nchunk = (int)nchunk;
+  size_t off = 0;
+  L->stats = off;
+  off = align_up(off + (size_t)rows * sizeof(sv::RowStat));
+  L->req = off;
+  off = align_up(off + (size_t)B * sizeof(sv::ReqState));
+  L->sums = off;
+  off = align_up(off + (size_t)B * (size_t)nchunk * sizeof(sv::ChunkSums));
+  L->bans = off;
+  off = align_up(off + (size_t)B * (size_t)n_banned * sizeof(int32_t));
+  L->banc = off;
+  off = align_up(off + (size_t)B * sizeof(int32_t));
+  L->total = off;
+  return true;
+}
+
+bool sampler_ok(const sv_sampler& s) {
+  if (!(s.temperature > 0.0f) || !isfinite(s.temperature)) return false;
+  if (s.top_k < 0) return false;
+  if (!(s.top_p > 0.0f && s.top_p <= 1.0f)) return false;
+  return true;
+}
+
+sv::SamplerDev to_dev(const sv_sampler& s) {
+  sv::SamplerDev d;
+  d.temperature = s.temperature;
+  d.top_k = s.top_k;
+  d.top_p = s.top_p;
+  d.pad = 0.0f;
+  return d;
+}
+
+// ---------------------------------------------------------------- profiling
+
+struct Prof {
+  bool on = false;
+  int cap = 0;
+  std::vector<hipEvent_t> ev[SV_NUM_KERNELS];  // 2 per launch
+  int used[SV_NUM_KERNELS] = {0};
+};
+Prof g_prof;
+
+struct ProfScope {
+  int k;
+  hipStream_t s;
+  bool active;
+  ProfScope(int kernel, hipStream_t stream) : k(kernel), s(stream), active(false) {
+    if (g_prof.on && g_prof.used[k] < g_prof.cap) {
+      active = hipEventRecord(g_prof.ev[k][2 * g_prof.used[k]], s) == hipSuccess;
+    }
+  }
+  ~ProfScope() {
+    if (active) {
+      (void)hipEventRecord(g_prof.ev[k][2 * g_prof.used[k] + 1], s);
+      ++g_prof.used[k];
+    }
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t n_banned) {
+  Layout L;
+  if (!layout(B, gamma, V, n_banned, &L)) return 0;
+  return L.total;
+}
+
+const char* spec_verify_strerror(int status) {
+  switch (status) {
+    case SV_OK: return "success";
+    case SV_EINVAL: return "invalid argument (null pointer, size or sampler setting)";
+    case SV_EDTYPE: return "unsupported dtype (expected SV_F32 or SV_BF16)";
+    case SV_EWORKSPACE: return "workspace missing or smaller than spec_verify_workspace_bytes()";
+    case SV_ESIZE: return "sizes exceed the supported index ranges";
+    case SV_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                       const int32_t* draft_tokens, const int32_t* banned_ids,
+                       int32_t n_banned, int32_t B, int32_t gamma, int32_t V,
+                       sv_sampler target, sv_sampler draft, uint64_t seed, uint64_t offset,
+                       const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
+                       uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !draft_tokens || !out_tokens || !out_num_accepted)
+    return SV_EINVAL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
+  if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return SV_EINVAL;
+  if (n_banned < 0 || n_banned > SV_MAX_BANNED || (n_banned > 0 && !banned_ids)) return SV_EINVAL;
+  if (!sampler_ok(target) || !sampler_ok(draft)) return SV_EINVAL;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)target_logits % es) || ((uintptr_t)draft_logits % es)) return SV_EINVAL;
+  Layout L;
+  if (!layout(B, gamma, V, n_banned, &L)) return SV_ESIZE;
+  if (!workspace || ((uintptr_t)workspace % WS_ALIGN) || workspace_bytes < L.total)
+    return SV_EWORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  sv::RowStat* stats = (sv::RowStat*)(ws + L.stats);
+  sv::ReqState* req = (sv::ReqState*)(ws + L.req);
+  sv::ChunkSums* sums = (sv::ChunkSums*)(ws + L.sums);
+  int32_t* ban_sorted = n_banned ? (int32_t*)(ws + L.bans) : nullptr;
+  int32_t* ban_count = n_banned ? (int32_t*)(ws + L.banc) : nullptr;
+  const int bf16 = dtype == SV_BF16;
+  const int rows = B * (2 * gamma + 1);
+
+  if (n_banned) {
+    sv::BanPrepArgs a{banned_ids, n_banned, V, ban_sorted, ban_count};
+    ProfScope p(SV_K_BAN_PREP, st);
+    if (sv::launch_ban_prep(a, B, st)) return SV_EHIP;
+  }
+  {
+    sv::RowStatsArgs a{};
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.gamma = gamma;
+    a.V = V;
+    a.st = to_dev(target);
+    a.sd = to_dev(draft);
+    a.ban_sorted = ban_sorted;
+    a.ban_count = ban_count;
+    a.ban_stride = n_banned;
+    a.stats = stats;
+    a.out_tlse = out_target_lse;
+    a.out_dlse = out_draft_lse;
+    a.force_generic = 0;
+    ProfScope p(SV_K_ROW_STATS, st);
+    if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
+  }
+  {
+    sv::AcceptArgs a{};
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.bf16 = bf16;
+    a.gamma = gamma;
+    a.V = V;
+    a.t_temp = target.temperature;
+    a.d_temp = draft.temperature;
+    a.draft_tokens = draft_tokens;
+    a.ban_sorted = ban_sorted;
+    a.ban_count = ban_count;
+    a.ban_stride = n_banned;
+    a.stats = stats;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
+    a.out_tokens = out_tokens;
+    a.out_num_accepted = out_num_accepted;
+    a.req = req;
+    ProfScope p(SV_K_ACCEPT, st);
+    if (sv::launch_accept(a, B, st)) return SV_EHIP;
+  }
+  {
+    sv::DrawArgs a{};
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.bf16 = bf16;
+    a.gamma = gamma;
+    a.V = V;
+    a.nchunk = L.nchunk;
+    a.t_temp = target.temperature;
+    a.d_temp = draft.temperature;
+    a.ban_sorted = ban_sorted;
+    a.ban_count = ban_count;
+    a.ban_stride = n_banned;
+    a.stats = stats;
+    a.req = req;
+    a.sums = sums;
+    a.out_tokens = out_tokens;
+    a.out_flags = out_flags;
+    {
+      ProfScope p(SV_K_RESIDUAL_PARTIAL, st);
+      if (sv::launch_residual_partial(a, B, st)) return SV_EHIP;
+    }
+    {
+      ProfScope p(SV_K_RESIDUAL_SELECT, st);
+      if (sv::launch_residual_select(a, B, st)) return SV_EHIP;
+    }
+  }
+  return SV_OK;
+}
+
+int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,
+                       int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                       int32_t* out_num_accepted, uint32_t* out_flags, void* stream) {
+  if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
+  if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return SV_EINVAL;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if ((uintptr_t)target_logits % es) return SV_EINVAL;
+  if ((int64_t)B * (gamma + 1) >= INT32_MAX) return SV_ESIZE;
+  hipStream_t st = (hipStream_t)stream;
+  sv::GreedyArgs a{target_logits, dtype == SV_BF16, gamma, V, B, draft_tokens,
+                   out_tokens, out_num_accepted, out_flags};
+  {
+    ProfScope p(SV_K_GREEDY_ARGMAX, st);
+    if (sv::launch_greedy_argmax(a, st)) return SV_EHIP;
+  }
+  {
+    ProfScope p(SV_K_GREEDY_SCAN, st);
+    if (sv::launch_greedy_scan(a, st)) return SV_EHIP;
+  }
+  return SV_OK;
+}
+
+int spec_verify_profile_start(int32_t max_launches_per_kernel) {
+  if (g_prof.on || max_launches_per_kernel < 1) return SV_EINVAL;
+  for (int k = 0; k < SV_NUM_KERNELS; ++k) {
+    g_prof.ev[k].assign(2 * (size_t)max_launches_per_kernel, nullptr);
+    for (auto& e : g_prof.ev[k])
+      if (hipEventCreate(&e) != hipSuccess) return SV_EHIP;
+    g_prof.used[k] = 0;
+  }
+  g_prof.cap = max_launches_per_kernel;
+  g_prof.on = true;
+  return SV_OK;
+}
+
+int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
+  if (!g_prof.on) return SV_EINVAL;
+  int rc = SV_OK;
+  for (int k = 0; k < SV_NUM_KERNELS; ++k) {
+    double tot = 0.0;
+    for (int j = 0; j < g_prof.used[k]; ++j) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(g_prof.ev[k][2 * j + 1]) != hipSuccess ||
+          hipEventElapsedTime(&ms, g_prof.ev[k][2 * j], g_prof.ev[k][2 * j + 1]) != hipSuccess)
+        rc = SV_EHIP;
+      tot += ms;
+    }
+    if (total_ms) total_ms[k] = tot;
+    if (launches) launches[k] = g_prof.used[k];
+    for (auto& e : g_prof.ev[k]) (void)hipEventDestroy(e);
+    g_prof.ev[k].clear();
+    g_prof.used[k] = 0;
+  }
+  g_prof.on = false;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,467 @@
+// Row statistics of the sampler-transformed target and draft rows.
+//
+// For every one of the B*(2*gamma+1) logit rows this kernel computes what the
+// acceptance test and the final draw need to evaluate p(x) or q(x) of any token
+// of the row: the largest kept logit m, the truncation threshold tau and the
+// log-normaliser lse of the tempered kept logits (transforms: bans,
+// temperature, top-k, top-p - "Speculative Decoding - Turn guesses into
+// parallel work", section "Greedy, sampling and the real sampler").
+//
+// One workgroup owns one row and reads it from HBM exactly once.
+//
+// bf16 rows (count-histogram path). A bf16 logit has only 65536 possible
+// values, and p(x) depends on x only through its logit. The workgroup
+// therefore streams the row once and counts, in LDS, how often each logit
+// value occurs (one LDS atomic and a few packed 16-bit integer ops per logit;
+// no exp per logit). Counts cover every value with 2^-23 <= |z| < 2^9 (4096
+// values per sign) plus exact zeros. From the counts the epilogue gets
+//   m      = largest counted value,
+//   Z      = sum_v count(v) * exp((v - m) / T) in fp64 (one exp per distinct value),
+//   top-k  = the value where the running count from the top reaches k,
+//   top-p  = the last value whose strictly-larger mass is < top_p * Z,
+// all exact (integer counts, fp64 sums in a fixed order, so the result is also
+// bitwise reproducible). Banned ids are subtracted from the counts afterwards
+// (the ban list is sorted and de-duplicated beforehand). A row holding a finite
+// value outside the counted range falls back to the generic path.
+//
+// fp32 rows (generic path). One streaming pass keeps, per lane, the running
+// maximum and sum of exp2(z*log2e/T - ref) against an integer reference ref
+// that only ever increases, so rescaling is an exact power of two; the
+// per-lane sums are combined exactly at the end. Thresholds, when asked for,
+// come from a bisection over the order-preserving integer keys of the values,
+// one pass over the row per step. This path is exact in the same sense, only
+// slower for truncated rows.
+
+#include "sv_common.hpp"
+#include "sv_launch.hpp"
+
+namespace sv {
+
+constexpr int RS_THREADS = 512;
+constexpr int RS_UNROLL = 4;
+
+// Count-histogram window for bf16 logits.
+constexpr uint32_t HB_BASE = 104u << 7;       // bf16 |bits| of 2^-23
+constexpr uint32_t HB_WIN = 32u * 128u;       // 32 binades x 128 mantissas per sign
+constexpr uint32_t HB_NEG = HB_WIN + 1u;      // first bin of the negative half
+constexpr uint32_t HB_ZERO = HB_WIN;          // zero bin (a dump bin during the pass)
+constexpr uint32_t HB_BINS = 2u * HB_WIN + 2u;
+constexpr int HB_RANKS = 2 * HB_WIN + 1;      // value-ordered ranks: +window, zero, -window
+constexpr int HB_RPT = (HB_RANKS + RS_THREADS - 1) / RS_THREADS;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// rank 0 is the largest value; ranks ascend as values descend.
+__device__ __forceinline__ uint32_t hb_bin_of_rank(int r) {
+  return r < (int)HB_WIN ? (HB_WIN - 1u - (uint32_t)r) : (uint32_t)r;
+}
+__device__ __forceinline__ float hb_value_of_rank(int r) {
+  if (r < (int)HB_WIN) return bf16_to_f32(HB_WIN - 1u - (uint32_t)r + HB_BASE);
+  if (r == (int)HB_ZERO) return 0.0f;
+  return bf16_to_f32(0x8000u | ((uint32_t)r - HB_NEG + HB_BASE));
+}
+
+struct RowShared {
+  uint32_t hist[HB_BINS];
+  uint32_t zero_cnt;
+  uint32_t nonfinite;
+  uint32_t special;
+  int32_t sel;
+  double dscr[RS_THREADS / WAVE];
+  float fscr[RS_THREADS / WAVE];
+  uint32_t uscr[RS_THREADS / WAVE];
+  int32_t iscr[RS_THREADS / WAVE];
+};
+
+// Exact classification of one bf16 logit that fell outside the counted window.
+__device__ __forceinline__ void hb_classify_slow(uint32_t bits, RowShared& sh) {
+  const uint32_t ae = bits & 0x7FFFu;
+  if (ae - HB_BASE < HB_WIN) return;          // inside the window: already counted
+  if (ae == 0u) {
+    atomicAdd(&sh.zero_cnt, 1u);
+  } else if (bits == 0xFF80u) {
+    // -inf: an impossible token, not admissible
+  } else if ((ae & 0x7F80u) == 0x7F80u) {
+    sh.nonfinite = 1u;                        // NaN or +inf
+  } else {
+    sh.special = 1u;                          // tiny or huge finite value
+  }
+}
+
+// Count both bf16 halves of one dword; returns the out-of-window marker bits.
+__device__ __forceinline__ uint32_t hb_count_pair(uint32_t d, uint32_t* hist) {
+  const u16x2 x = __builtin_bit_cast(u16x2, d);
+  u16x2 t = (x & (unsigned short)0x7FFF) - (unsigned short)HB_BASE;
+  t = __builtin_elementwise_min(t, (u16x2)(unsigned short)HB_WIN);
+  const u16x2 s = x >> (unsigned short)15;
+  const u16x2 bin = s * (unsigned short)HB_NEG + t;
+  const uint32_t b2 = __builtin_bit_cast(uint32_t, bin);
+  atomicAdd(&hist[b2 & 0xFFFFu], 1u);
+  atomicAdd(&hist[b2 >> 16], 1u);
+  return __builtin_bit_cast(uint32_t, t) & 0x10001000u;
+}
+
+__device__ __forceinline__ void hb_count_one(uint32_t bits, RowShared& sh) {
+  const uint32_t ae = bits & 0x7FFFu;
+  const uint32_t t = ae - HB_BASE;
+  if (t < HB_WIN)
+    atomicAdd(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
+  else
+    hb_classify_slow(bits, sh);
+}
+
+// ------------------------------------------------------------------ generic path
+
+template <typename Elem>
+__device__ __forceinline__ float elem_value(Elem e);
+template <>
+__device__ __forceinline__ float elem_value<uint16_t>(uint16_t e) {
+  return bf16_to_f32(e);
+}
+template <>
+__device__ __forceinline__ float elem_value<float>(float e) {
+  return e;
+}
+
+// Calls f(z, id) for every element of the row, 16-byte vector loads in the body.
+template <typename Elem, typename F>
+__device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
+  constexpr int PER = 16 / sizeof(Elem);
+  const int tid = threadIdx.x;
+  const uintptr_t addr = (uintptr_t)rowp;
+  int head = (int)(((16u - (addr & 15u)) & 15u) / sizeof(Elem));
+  if (head > V) head = V;
+  const int nchunk = (V - head) / PER;
+  const int tail0 = head + nchunk * PER;
+  if (tid < head) f(elem_value<Elem>(rowp[tid]), tid);
+  if (tid < V - tail0) f(elem_value<Elem>(rowp[tail0 + tid]), tail0 + tid);
+  const u32x4* body = (const u32x4*)(rowp + head);
+  for (int k = tid; k < nchunk; k += RS_THREADS) {
+    const u32x4 v = body[k];
+    const int id0 = head + k * PER;
+    if constexpr (sizeof(Elem) == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f(bf16_to_f32(v[j] & 0xFFFFu), id0 + 2 * j);
+        f(bf16_to_f32(v[j] >> 16), id0 + 2 * j + 1);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f(__uint_as_float(v[j]), id0 + j);
+    }
+  }
+}
+
+struct GenericCtx {
+  const int32_t* bans;  // sorted unique ids in LDS
+  int nb;
+  __device__ __forceinline__ bool admissible(float z, int id) const {
+    // finite and not banned; NaN fails both comparisons
+    if (!(z > -INFINITY && z < INFINITY)) return false;
+    return nb == 0 || !in_sorted(bans, nb, id);
+  }
+};
+
+template <typename Elem>
+__device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const GenericCtx& g,
+                            RowShared& sh, RowStat& out) {
+  const int tid = threadIdx.x;
+  const double c2 = 1.4426950408889634 / (double)s.temperature;  // log2(e) / T
+  // pass 1: max, min, count and the exp-sum against per-lane integer references
+  float mx = -INFINITY, mn = INFINITY;
+  uint32_t cnt = 0, bad = 0;
+  double ref = -INFINITY, acc = 0.0;
+  for_each_elem<Elem>(rowp, V, [&](float z, int id) {
+    if (z != z || z == INFINITY) bad = 1u;
+    if (!g.admissible(z, id)) return;
+    ++cnt;
+    mn = fminf(mn, z);
+    if (z > mx) mx = z;
+    const double e = (double)z * c2;
+    if (e > ref) {
+      const double nr = ceil(e);
+      if (ref > -INFINITY) acc = ldexp(acc, (int)fmax(ref - nr, -2000.0));
+      ref = nr;
+    }
+    acc += (double)exp2f((float)(e - ref));
+  });
+  mx = block_max<RS_THREADS>(mx, sh.fscr);
+  mn = block_min<RS_THREADS>(mn, sh.fscr);
+  cnt = block_sum<RS_THREADS>(cnt, sh.uscr);
+  bad = block_max<RS_THREADS>(bad, sh.uscr);
+  const double rmax = block_max<RS_THREADS>(ref, sh.dscr);
+  out.flags |= bad ? FLAG_NONFINITE : 0u;
+  if (cnt == 0u) {
+    out.m = -INFINITY;
+    out.tau = -INFINITY;
+    out.lse = -INFINITY;
+    out.flags |= FLAG_EMPTY;
+    return;
+  }
+  double Z = block_sum<RS_THREADS>(ref > -INFINITY ? ldexp(acc, (int)fmax(ref - rmax, -2000.0)) : 0.0,
+                                   sh.dscr);
+  // mass of the admissible values >= thr (relative to 2^rmax)
+  auto mass_ge = [&](float thr) -> double {
+    double a = 0.0;
+    for_each_elem<Elem>(rowp, V, [&](float z, int id) {
+      if (z >= thr && g.admissible(z, id)) a += (double)exp2f((float)((double)z * c2 - rmax));
+    });
+    return block_sum<RS_THREADS>(a, sh.dscr);
+  };
+  auto count_ge = [&](float thr) -> uint32_t {
+    uint32_t a = 0;
+    for_each_elem<Elem>(rowp, V, [&](float z, int id) {
+      if (z >= thr && g.admissible(z, id)) ++a;
+    });
+    return block_sum<RS_THREADS>(a, sh.uscr);
+  };
+  float tau = -INFINITY;
+  bool trunc = false;
+  if (s.top_k > 0 && (uint32_t)s.top_k < cnt) {
+    // largest key t with count(z >= value(t)) >= k
+    uint32_t lo = f32_key(mn), hi = f32_key(mx) + 1u;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (count_ge(f32_from_key(mid)) >= (uint32_t)s.top_k)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    tau = f32_from_key(lo);
+    trunc = true;
+    Z = mass_ge(tau);
+  }
+  if (s.top_p < 1.0f) {
+    // largest key t with mass(z >= value(t)) >= top_p * Z (within the top-k set)
+    const double target = (double)s.top_p * Z;
+    const float lo_v = trunc ? fmaxf(tau, mn) : mn;
+    uint32_t lo = f32_key(lo_v), hi = f32_key(mx) + 1u;
+    double zlo = Z;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      const double mm = mass_ge(f32_from_key(mid));
+      if (mm >= target) {
+        lo = mid;
+        zlo = mm;
+      } else {
+        hi = mid;
+      }
+    }
+    tau = f32_from_key(lo);
+    trunc = true;
+    Z = zlo;
+  }
+  out.m = mx;
+  out.tau = trunc ? tau : -INFINITY;
+  out.lse = rmax * 0.6931471805599453 + log(Z);
+  out.path = 1u;
+}
+
+// ------------------------------------------------------------------ the kernel
+
+template <typename Elem>
+__global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
+  __shared__ RowShared sh;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int G1 = a.gamma + 1, RPR = 2 * a.gamma + 1;
+  const int b = row / RPR, i = row % RPR;
+  const bool is_target = i < G1;
+  const Elem* rowp = is_target
+                         ? (const Elem*)a.target + ((int64_t)b * G1 + i) * (int64_t)a.V
+                         : (const Elem*)a.draft + ((int64_t)b * a.gamma + (i - G1)) * (int64_t)a.V;
+  const SamplerDev s = is_target ? a.st : a.sd;
+  const int V = a.V;
+  const int nb = a.ban_count ? a.ban_count[b] : 0;
+  const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
+
+  RowStat out;
+  out.m = -INFINITY;
+  out.tau = -INFINITY;
+  out.lse = -INFINITY;
+  out.flags = 0u;
+  out.path = 0u;
+  out.pad[0] = out.pad[1] = 0u;
+
+  bool generic = (sizeof(Elem) == 4) || a.force_generic;
+
+  if (!generic) {
+    for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = 0u;
+    if (tid == 0) {
+      sh.zero_cnt = 0u;
+      sh.nonfinite = 0u;
+      sh.special = 0u;
+    }
+    __syncthreads();
+
+    const uint16_t* rp = (const uint16_t*)rowp;
+    const uintptr_t addr = (uintptr_t)rp;
+    int head = (int)(((16u - (addr & 15u)) & 15u) >> 1);
+    if (head > V) head = V;
+    const int nchunk = (V - head) >> 3;
+    const int tail0 = head + nchunk * 8;
+    if (tid < head) hb_count_one(rp[tid], sh);
+    if (tid < V - tail0) hb_count_one(rp[tail0 + tid], sh);
+    const u32x4* body = (const u32x4*)(rp + head);
+
+    for (int k0 = tid; k0 < nchunk; k0 += RS_THREADS * RS_UNROLL) {
+      u32x4 v[RS_UNROLL];
+#pragma unroll
+      for (int u = 0; u < RS_UNROLL; ++u) {
+        const int k = k0 + u * RS_THREADS;
+        if (k < nchunk) v[u] = __builtin_nontemporal_load(body + k);
+      }
+#pragma unroll
+      for (int u = 0; u < RS_UNROLL; ++u) {
+        const int k = k0 + u * RS_THREADS;
+        if (k < nchunk) {
+          uint32_t oow = hb_count_pair(v[u][0], sh.hist);
+          oow |= hb_count_pair(v[u][1], sh.hist);
+          oow |= hb_count_pair(v[u][2], sh.hist);
+          oow |= hb_count_pair(v[u][3], sh.hist);
+          if (oow) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              hb_classify_slow(v[u][j] & 0xFFFFu, sh);
+              hb_classify_slow(v[u][j] >> 16, sh);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // remove the banned ids (sorted, unique, all in [0, V))
+    for (int j = tid; j < nb; j += RS_THREADS) {
+      const uint32_t bits = rp[bans[j]];
+      const uint32_t ae = bits & 0x7FFFu;
+      const uint32_t t = ae - HB_BASE;
+      if (t < HB_WIN)
+        atomicSub(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
+      else if (ae == 0u)
+        atomicSub(&sh.zero_cnt, 1u);
+    }
+    __syncthreads();
+    if (sh.nonfinite) out.flags |= FLAG_NONFINITE;
+    if (sh.special) {
+      generic = true;
+    } else {
+      if (tid == 0) sh.hist[HB_ZERO] = sh.zero_cnt;
+      __syncthreads();
+
+      const int r0 = tid * HB_RPT;
+      uint32_t cloc = 0u;
+      int top = HB_RANKS;
+#pragma unroll
+      for (int j = 0; j < HB_RPT; ++j) {
+        const int r = r0 + j;
+        if (r < HB_RANKS) {
+          const uint32_t c = sh.hist[hb_bin_of_rank(r)];
+          cloc += c;
+          if (c && top == HB_RANKS) top = r;
+        }
+      }
+      const uint32_t N = block_sum<RS_THREADS>(cloc, sh.uscr);
+      const int rtop = block_min<RS_THREADS>(top, sh.iscr);
+      if (N == 0u) {
+        out.flags |= FLAG_EMPTY;
+      } else {
+        const float m = hb_value_of_rank(rtop);
+        const double md = (double)m;
+        const double invT = 1.0 / (double)s.temperature;
+        int rk = HB_RANKS - 1;
+        bool trunc = false;
+        if (s.top_k > 0 && (uint32_t)s.top_k < N) {
+          uint32_t tot;
+          const uint32_t before = block_excl_scan<RS_THREADS>(cloc, sh.uscr, &tot);
+          const uint32_t k = (uint32_t)s.top_k;
+          if (before < k && before + cloc >= k) {
+            uint32_t cum = before;
+#pragma unroll
+            for (int j = 0; j < HB_RPT; ++j) {
+              const int r = r0 + j;
+              if (r < HB_RANKS) {
+                cum += sh.hist[hb_bin_of_rank(r)];
+                if (cum >= k) {
+                  sh.sel = r;
+                  break;
+                }
+              }
+            }
+          }
+          __syncthreads();
+          rk = sh.sel;
+          trunc = true;
+        }
+        // masses of the kept-after-top-k values
+        double mloc = 0.0;
+#pragma unroll
+        for (int j = 0; j < HB_RPT; ++j) {
+          const int r = r0 + j;
+          if (r <= rk) {
+            const uint32_t c = sh.hist[hb_bin_of_rank(r)];
+            if (c) mloc += (double)c * exp(((double)hb_value_of_rank(r) - md) * invT);
+          }
+        }
+        double Z = block_sum<RS_THREADS>(mloc, sh.dscr);
+        int rp_last = rk;
+        if (s.top_p < 1.0f) {
+          double tot;
+          const double before = block_excl_scan<RS_THREADS>(mloc, sh.dscr, &tot);
+          const double target = (double)s.top_p * Z;
+          double above = before, zloc = 0.0;
+          int last = -1;
+          for (int j = 0; j < HB_RPT; ++j) {
+            const int r = r0 + j;
+            if (r > rk || !(above < target)) break;
+            const uint32_t c = sh.hist[hb_bin_of_rank(r)];
+            if (c) {
+              const double w = (double)c * exp(((double)hb_value_of_rank(r) - md) * invT);
+              last = r;
+              zloc += w;
+              above += w;
+            }
+          }
+          rp_last = block_max<RS_THREADS>(last, sh.iscr);
+          Z = block_sum<RS_THREADS>(zloc, sh.dscr);
+          trunc = true;
+        }
+        out.m = m;
+        out.tau = trunc ? hb_value_of_rank(rp_last) : -INFINITY;
+        out.lse = md * invT + log(Z);
+      }
+    }
+  }
+
+  if (generic) {
+    __syncthreads();
+    // the ban list moves into LDS (reusing the histogram storage)
+    int32_t* lbans = (int32_t*)sh.hist;
+    for (int j = tid; j < nb; j += RS_THREADS) lbans[j] = bans[j];
+    __syncthreads();
+    GenericCtx g{lbans, nb};
+    out.flags &= ~FLAG_EMPTY;
+    row_generic<Elem>(rowp, V, s, g, sh, out);
+  }
+
+  if (tid == 0) {
+    a.stats[row] = out;
+    if (is_target) {
+      if (a.out_tlse) a.out_tlse[(int64_t)b * G1 + i] = (float)out.lse;
+    } else {
+      if (a.out_dlse) a.out_dlse[(int64_t)b * a.gamma + (i - G1)] = (float)out.lse;
+    }
+  }
+}
+
+int launch_row_stats(const RowStatsArgs& a, int dtype_bf16, int rows, hipStream_t stream) {
+  if (dtype_bf16)
+    hipLaunchKernelGGL(row_stats_kernel<uint16_t>, dim3(rows), dim3(RS_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(row_stats_kernel<float>, dim3(rows), dim3(RS_THREADS), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace sv

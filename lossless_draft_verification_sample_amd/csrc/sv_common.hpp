@@ -1,0 +1,225 @@
+// Shared device-side definitions of the verifier kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr uint32_t FLAG_TOKEN_RANGE = 1u;
+constexpr uint32_t FLAG_Q_ZERO = 2u;
+constexpr uint32_t FLAG_NONFINITE = 4u;
+constexpr uint32_t FLAG_EMPTY = 8u;
+constexpr uint32_t FLAG_RESIDUAL_ZERO = 16u;
+
+constexpr int WAVE = 64;
+
+// Statistics of one sampler-transformed logit row, produced by row_stats and
+// consumed by the acceptance and final-draw kernels. A token x of the row is
+// kept iff it is not banned, its logit z is finite and z >= tau.
+struct alignas(16) RowStat {
+  float m;         // largest kept logit (-inf for an empty row)
+  float tau;       // truncation threshold on the logit value (-inf: none)
+  double lse;      // log sum_{kept} exp(z / T)   (-inf for an empty row)
+  uint32_t flags;  // FLAG_NONFINITE | FLAG_EMPTY
+  uint32_t path;   // 0 = count histogram, 1 = generic streaming path
+  uint32_t pad[2];
+};
+
+// Per-request state handed from the acceptance kernel to the final draw.
+struct alignas(16) ReqState {
+  int32_t n;       // accepted proposals; the final token goes to slot n
+  uint32_t flags;  // flags gathered so far
+  double u_final;  // uniform of the final draw
+};
+
+// Partial sums of one vocabulary chunk for the final draw.
+struct alignas(16) ChunkSums {
+  double w;  // sum of max(0, p - q) (bonus draw: sum of p)
+  double p;  // sum of p (fallback when the residual mass is zero)
+};
+
+// Sampler settings as the kernels use them.
+struct SamplerDev {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float pad;
+};
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Order-preserving unsigned keys: a < b  <=>  key(a) < key(b) for non-NaN values,
+// with -0 and +0 given the key of +0 so that they tie.
+__device__ __forceinline__ uint32_t f32_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_key(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(b);
+}
+
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11): ten rounds of two 64x64->128-bit products with the
+// published multipliers, the key bumped by the published Weyl constants between
+// rounds. Returns output word 0 of the block.
+__device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                     uint64_t c3, uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+
+// Uniform in (0, 1] for request b, slot j: counter (j, b, offset, 0), key (seed, 0).
+__device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t offset, uint32_t b,
+                                                 uint32_t j) {
+  const uint64_t r = philox4x64_10_w0(j, b, offset, 0, seed, 0);
+  return (double)((r >> 11) + 1) * 0x1.0p-53;
+}
+
+// ---------------------------------------------------------------- reductions
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = WAVE / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int off = WAVE / 2; off > 0; off >>= 1) {
+    T o = __shfl_xor(v, off, WAVE);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int off = WAVE / 2; off > 0; off >>= 1) {
+    T o = __shfl_xor(v, off, WAVE);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+// Inclusive prefix sum over the wave in lane order.
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    T o = __shfl_up(v, off, WAVE);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Block-wide reductions for NT threads; `scratch` holds at least NT/WAVE
+// elements of T. All threads get the result. Fixed combination order, so the
+// result does not depend on timing.
+template <int NT, typename T>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+  constexpr int NW = NT / WAVE;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T s = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) s += scratch[i];
+  return s;
+}
+template <int NT, typename T>
+__device__ __forceinline__ T block_max(T v, T* scratch) {
+  constexpr int NW = NT / WAVE;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T s = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) s = scratch[i] > s ? scratch[i] : s;
+  return s;
+}
+template <int NT, typename T>
+__device__ __forceinline__ T block_min(T v, T* scratch) {
+  constexpr int NW = NT / WAVE;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  v = wave_min(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T s = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) s = scratch[i] < s ? scratch[i] : s;
+  return s;
+}
+// Exclusive prefix sum over the block in thread order; *total gets the sum.
+template <int NT, typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T* scratch, T* total) {
+  constexpr int NW = NT / WAVE;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  T incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == WAVE - 1) scratch[w] = incl;
+  __syncthreads();
+  T before = T(0), all = T(0);
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if (i < w) before += scratch[i];
+    all += scratch[i];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Sorted, de-duplicated ban list of one request (ids in [0, V)).
+__device__ __forceinline__ bool in_sorted(const int32_t* list, int n, int32_t id) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int32_t v = list[mid];
+    if (v < id)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo < n && list[lo] == id;
+}
+// First index with list[i] >= id.
+__device__ __forceinline__ int lower_bound(const int32_t* list, int n, int32_t id) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] < id)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace sv

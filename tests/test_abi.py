@@ -1,0 +1,133 @@
+"""The C interface on the CPU: the library loads, exports every function the
+header declares, sizes its workspace, and rejects bad arguments before any
+launch (so these calls never need a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from lossless_draft_verification_sample_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from lossless_draft_verification_sample_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert {"spec_verify_sample", "spec_verify_greedy", "spec_verify_workspace_bytes",
+            "spec_verify_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_names_match_header():
+    import lossless_draft_verification_sample_amd as sv
+    for n in _declared_functions():
+        assert callable(getattr(sv, n)), n
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.spec_verify_strerror(code)
+    assert b"unknown" in lib.spec_verify_strerror(42)
+
+
+def test_workspace_bytes(lib):
+    ws = lib.spec_verify_workspace_bytes
+    a = ws(128, 8, 151936, 64)
+    assert a > 0 and a % 256 == 0
+    assert ws(128, 8, 151936, 0) < a
+    assert ws(1, 4, 1000, 0) > 0
+    for bad in [(0, 4, 10, 0), (1, 0, 10, 0), (1, 64, 10, 0), (1, 4, 0, 0), (1, 4, 10, -1),
+                (1, 4, 10, 2049), (2**30, 63, 10, 0)]:
+        assert ws(*bad) == 0, bad
+
+
+FAKE = 4096  # non-null, aligned; never dereferenced because validation fails first
+
+
+def _sample(lib, **kw):
+    from lossless_draft_verification_sample_amd._lib import SvSampler
+    a = dict(target=FAKE, draft=FAKE, dtype=1, tokens=FAKE, banned=None, n_banned=0, B=2,
+             gamma=3, V=100, ts=SvSampler(1.0, 0, 1.0), ds=SvSampler(1.0, 0, 1.0), seed=0,
+             offset=0, uniforms=None, out_tokens=FAKE, out_n=FAKE, out_flags=None,
+             out_tl=None, out_dl=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.spec_verify_sample(
+        a["target"], a["draft"], a["dtype"], a["tokens"], a["banned"], a["n_banned"], a["B"],
+        a["gamma"], a["V"], a["ts"], a["ds"], a["seed"], a["offset"], a["uniforms"],
+        a["out_tokens"], a["out_n"], a["out_flags"], a["out_tl"], a["out_dl"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+def test_sample_argument_errors(lib):
+    from lossless_draft_verification_sample_amd import _lib as L
+    S = L.SvSampler
+    # everything valid except the workspace: rejected before launching
+    assert _sample(lib) == L.SV_EWORKSPACE
+    need = lib.spec_verify_workspace_bytes(2, 3, 100, 0)
+    assert _sample(lib, ws=FAKE, ws_bytes=need - 1) == L.SV_EWORKSPACE
+    assert _sample(lib, ws=FAKE + 8, ws_bytes=need) == L.SV_EWORKSPACE   # misaligned
+    cases = {
+        "target": dict(target=None), "draft": dict(draft=None), "tokens": dict(tokens=None),
+        "out_tokens": dict(out_tokens=None), "out_n": dict(out_n=None),
+        "B": dict(B=0), "gamma0": dict(gamma=0), "gamma64": dict(gamma=64), "V": dict(V=0),
+        "n_banned<0": dict(n_banned=-1), "n_banned big": dict(n_banned=2049, banned=FAKE),
+        "banned null": dict(n_banned=3), "T=0": dict(ts=S(0.0, 0, 1.0)),
+        "T<0": dict(ds=S(-1.0, 0, 1.0)), "T nan": dict(ts=S(float("nan"), 0, 1.0)),
+        "T inf": dict(ts=S(float("inf"), 0, 1.0)), "top_k<0": dict(ds=S(1.0, -1, 1.0)),
+        "top_p=0": dict(ts=S(1.0, 0, 0.0)), "top_p>1": dict(ts=S(1.0, 0, 1.5)),
+        "top_p nan": dict(ds=S(1.0, 0, float("nan"))), "misaligned": dict(target=FAKE + 1),
+    }
+    for name, kw in cases.items():
+        assert _sample(lib, **kw) == L.SV_EINVAL, name
+    assert _sample(lib, dtype=2) == L.SV_EDTYPE
+    assert _sample(lib, dtype=0, target=FAKE + 2) == L.SV_EINVAL   # fp32 needs 4-byte alignment
+    assert _sample(lib, B=2**30, gamma=63) == L.SV_ESIZE
+
+
+def test_greedy_argument_errors(lib):
+    from lossless_draft_verification_sample_amd import _lib as L
+    g = lib.spec_verify_greedy
+    assert g(None, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, None, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 3, 10, None, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 3, 10, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 5, FAKE, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EDTYPE
+    assert g(FAKE, 1, FAKE, 0, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 0, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 3, 0, FAKE, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE + 1, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2**30, 3, 10, FAKE, FAKE, None, None) == L.SV_ESIZE
+
+
+def test_profile_stop_without_start(lib):
+    from lossless_draft_verification_sample_amd import _lib as L
+    assert lib.spec_verify_profile_stop(None, None) == L.SV_EINVAL
+    assert lib.spec_verify_profile_start(0) == L.SV_EINVAL
+
+
+def test_product_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "lossless_draft_verification_sample_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

@@ -1,0 +1,320 @@
+"""Parity of the HIP verifier with the float64 oracle, through the C interface.
+
+Tokens, accept counts and flags must be bit-exact except for requests where a
+uniform lies within 1e-6 of a decision edge (the oracle classifies those and
+they are counted); log-normalisers agree within 1e-5. Inputs follow the
+benchmark workload recipes (synth), at reduced sizes that span several tiles
+with ragged tails and at full size on sampled requests.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import lossless_draft_verification_sample_amd._lib as L
+    L.load()   # fails loudly when the library was not built
+
+
+SMALL = {
+    "c1": dict(),
+    "c2s": dict(name="c2", B=4),
+    "c3as": dict(name="c3a", B=4, V=20011),
+    "c3bs": dict(name="c3b", B=4, V=20011),
+    "c5s": dict(name="c5", B=4, V=20011),
+    "c5s_g1": dict(name="c5", B=6, gamma=1, V=4099),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("rng_mode", ["philox", "explicit"])
+def test_small_configs(case, rng_mode):
+    over = dict(SMALL[case])
+    name = over.pop("name", case)
+    wl = pu.make(name, **over)
+    cfg = wl.cfg
+    xs = pu.oracle_proposals(wl)
+    u = pu.philox_uniforms(cfg.philox_seed, cfg.philox_offset, cfg.B, cfg.gamma)
+    if rng_mode == "explicit":
+        u = 1.0 - np.random.default_rng(5).random((cfg.B, cfg.gamma + 1))
+    got = pu.run_gpu_sample(wl, xs, uniforms=u if rng_mode == "explicit" else None)
+    ref = pu.run_oracle_sample(wl, xs, u, range(cfg.B))
+    nb = pu.compare_sample(got, ref, range(cfg.B), where=case)
+    assert nb <= max(1, cfg.B // 100)
+
+
+FULL = ["c2", "c3a", "c3b", "c5"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_requests(name):
+    wl = pu.make(name)
+    cfg = wl.cfg
+    xs = pu.stored_proposals(name)
+    assert xs.shape == (cfg.B, cfg.gamma)
+    got = pu.run_gpu_sample(wl, xs)
+    u = pu.philox_uniforms(cfg.philox_seed, cfg.philox_offset, cfg.B, cfg.gamma)
+    rng = np.random.default_rng(17)
+    reqs = sorted({0, 1, cfg.B - 2, cfg.B - 1, *rng.choice(cfg.B, min(cfg.B, 4), replace=False).tolist()})
+    ref = pu.run_oracle_sample(wl, xs, u, reqs)
+    pu.compare_sample(got, ref, reqs, where=name)
+    # properties that hold for every request
+    n = got["num_accepted"]
+    assert np.all((n >= 0) & (n <= cfg.gamma))
+    for b in range(cfg.B):
+        row = got["tokens"][b]
+        assert np.array_equal(row[: n[b]], xs[b, : n[b]])
+        assert 0 <= row[n[b]] < cfg.V
+        assert np.all(row[n[b] + 1:] == -1)
+        if wl.banned is not None:
+            assert row[n[b]] not in set(wl.banned[b].tolist())
+    assert np.all(got["flags"] == 0)
+
+
+def test_greedy_full_c4():
+    import torch
+    wl = pu.make("c4")
+    cfg = wl.cfg
+    xs = pu.stored_proposals("c4")
+    t = pu.logits_tensor(wl.target, wl.target_bits, cfg.dtype, torch.device("cuda:0"))
+    tok, n, fl = pu.run_gpu_greedy(t, xs)
+    ref = oracle.verify_greedy(wl.target_f64(), xs)
+    assert np.array_equal(tok, ref.tokens)
+    assert np.array_equal(n, ref.num_accepted)
+    assert np.array_equal(fl, ref.flags)
+    # the planted ties: lowest index wins
+    rows = wl.target.reshape(-1, cfg.V)
+    for r in wl.extra["tie_rows"]:
+        assert ref.argmax.reshape(-1)[r] == int(np.flatnonzero(rows[r] == rows[r].max())[0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 2, 7, 63, 64, 65, 1000, 4097])
+def test_greedy_shapes_and_ties(dtype, V):
+    import torch
+    rng = np.random.default_rng(V)
+    B, gamma = 5, 3
+    vals = rng.choice(np.array([-2.0, -0.0, 0.0, 0.5, 1.5, 1.5, 3.0, -np.inf], np.float32),
+                      size=(B, gamma + 1, V))
+    vals[0, 1, :] = -np.inf                     # a row of -inf: argmax is id 0
+    from lossless_draft_verification_sample_amd import synth
+    bits = synth.f32_to_bf16_bits(vals)
+    t = pu.logits_tensor(vals, bits, dtype, torch.device("cuda:0"))
+    ref0 = oracle.verify_greedy(vals.astype(np.float64), np.zeros((B, gamma), np.int32))
+    xs = np.where(rng.random((B, gamma)) < 0.6, ref0.argmax[:, :gamma],
+                  rng.integers(-1, V + 1, (B, gamma))).astype(np.int32)
+    tok, n, fl = pu.run_gpu_greedy(t, xs)
+    ref = oracle.verify_greedy(vals.astype(np.float64), xs)
+    assert np.array_equal(tok, ref.tokens)
+    assert np.array_equal(n, ref.num_accepted)
+    assert np.array_equal(fl, ref.flags)
+
+
+def test_greedy_nonfinite_flag():
+    import torch
+    B, gamma, V = 3, 2, 300
+    vals = np.random.default_rng(0).normal(size=(B, gamma + 1, V)).astype(np.float32)
+    vals[1, 2, 17] = np.nan
+    vals[2, 0, 5] = np.inf
+    t = torch.from_numpy(vals).cuda()
+    tok, n, fl = pu.run_gpu_greedy(t, np.zeros((B, gamma), np.int32))
+    assert fl[0] == 0 and fl[1] & oracle.FLAG_NONFINITE and fl[2] & oracle.FLAG_NONFINITE
+
+
+def _edge_workload(V, gamma, B, dtype, seed, sd=2.0):
+    from lossless_draft_verification_sample_amd import synth
+    return pu.make("c3a", B=B, gamma=gamma, V=V, dtype=dtype, target_sd=sd, draft_sd=1.0,
+                   boost="none", seed=seed)
+
+
+SAMPLERS = {
+    "plain": ((1.0, 0, 1.0), (1.0, 0, 1.0)),
+    "topk1": ((0.9, 1, 1.0), (0.9, 1, 1.0)),
+    "topk_big": ((1.0, 100000, 1.0), (1.0, 5, 1.0)),
+    "topp_small": ((0.6, 0, 0.05), (1.2, 0, 0.3)),
+    "topk_topp": ((0.8, 40, 0.7), (0.8, 20, 0.95)),
+    "differ": ((1.3, 0, 0.9), (0.5, 7, 1.0)),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 7, 63, 64, 65, 1000])
+@pytest.mark.parametrize("samp", sorted(SAMPLERS))
+def test_edge_shapes_and_samplers(dtype, V, samp):
+    wl = _edge_workload(V, 3, 6, dtype, seed=V * 7 + len(samp))
+    ts, ds = SAMPLERS[samp]
+    xs = pu.oracle_proposals(wl, draft_sampler=ds)
+    u = pu.philox_uniforms(0, 3, wl.cfg.B, wl.cfg.gamma)
+    got = pu.run_gpu_sample(wl, xs, tsamp=ts, dsamp=ds, offset=3)
+    ref = pu.run_oracle_sample(wl, xs, u, range(wl.cfg.B), tsamp=ts, dsamp=ds)
+    pu.compare_sample(got, ref, range(wl.cfg.B), where=f"{dtype}/{V}/{samp}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bans_padding_duplicates_and_invalid_proposals(dtype):
+    V, gamma, B = 500, 4, 8
+    wl = _edge_workload(V, gamma, B, dtype, seed=3)
+    rng = np.random.default_rng(3)
+    banned = rng.integers(0, 40, (B, 30)).astype(np.int32)   # many duplicates
+    banned[:, 25:] = -1                                      # padding
+    banned[1, 0] = V + 5                                     # outside [0, V): ignored
+    banned[2, :] = np.arange(V, V + 30)                      # nothing effective
+    s = (1.0, 0, 1.0)
+    wl.banned = banned
+    xs = pu.oracle_proposals(wl, draft_sampler=s)
+    xs[3, 1] = V          # out of range
+    xs[4, 0] = -7         # out of range
+    xs[5, 0] = banned[5, 0]   # banned proposal: q(x) = 0
+    u = pu.philox_uniforms(9, 0, B, gamma)
+    got = pu.run_gpu_sample(wl, xs, tsamp=s, dsamp=s, banned=banned, seed=9)
+    ref = pu.run_oracle_sample(wl, xs, u, range(B), tsamp=s, dsamp=s, banned=banned)
+    pu.compare_sample(got, ref, range(B), where="bans")
+    assert got["flags"][3] & oracle.FLAG_TOKEN_RANGE and got["flags"][4] & oracle.FLAG_TOKEN_RANGE
+    assert got["flags"][5] & oracle.FLAG_Q_ZERO
+
+
+def test_all_banned_and_masked_rows():
+    V, gamma, B = 64, 2, 3
+    wl = _edge_workload(V, gamma, B, "bf16", seed=11)
+    banned = np.full((B, V), -1, dtype=np.int32)
+    banned[0] = np.arange(V)                    # everything banned: empty rows
+    from lossless_draft_verification_sample_amd import synth
+    t = wl.target.copy()
+    t[1, 0, :] = -np.inf                        # an empty target row 0
+    wl.target = t
+    wl.target_bits = synth.f32_to_bf16_bits(t)
+    s = (1.0, 0, 1.0)
+    xs = np.zeros((B, gamma), np.int32)
+    xs[2] = pu.oracle_proposals(wl, draft_sampler=s)[2]
+    u = pu.philox_uniforms(0, 0, B, gamma)
+    got = pu.run_gpu_sample(wl, xs, tsamp=s, dsamp=s, banned=banned)
+    ref = pu.run_oracle_sample(wl, xs, u, range(B), tsamp=s, dsamp=s, banned=banned)
+    pu.compare_sample(got, ref, range(B), where="empty")
+    assert got["flags"][0] & oracle.FLAG_EMPTY and got["tokens"][0, 0] == -1
+    assert got["flags"][1] & oracle.FLAG_EMPTY
+
+
+def test_special_values_take_the_generic_path():
+    from lossless_draft_verification_sample_amd import synth
+    V, gamma, B = 3000, 3, 4
+    wl = _edge_workload(V, gamma, B, "bf16", seed=21)
+    t, d = wl.target.copy(), wl.draft.copy()
+    t[0, 0, 10] = 700.0          # huge: outside the counted window
+    d[1, 1, 20] = 1e-30          # tiny
+    t[2, :, :100] = 0.0          # many exact zeros (counted path)
+    t[3, 2, 5] = -np.inf
+    wl.target, wl.draft = t, d
+    wl.target_bits, wl.draft_bits = synth.f32_to_bf16_bits(t), synth.f32_to_bf16_bits(d)
+    wl.target = synth.bf16_bits_to_f32(wl.target_bits)
+    wl.draft = synth.bf16_bits_to_f32(wl.draft_bits)
+    for s in [(1.0, 0, 1.0), (0.7, 30, 0.8)]:
+        xs = pu.oracle_proposals(wl, draft_sampler=s)
+        u = pu.philox_uniforms(1, 2, B, gamma)
+        got = pu.run_gpu_sample(wl, xs, tsamp=s, dsamp=s, seed=1, offset=2)
+        ref = pu.run_oracle_sample(wl, xs, u, range(B), tsamp=s, dsamp=s)
+        pu.compare_sample(got, ref, range(B), where=f"special {s}")
+
+
+def test_nonfinite_rows_are_flagged():
+    from lossless_draft_verification_sample_amd import synth
+    V, gamma, B = 257, 2, 3
+    wl = _edge_workload(V, gamma, B, "bf16", seed=5)
+    t = wl.target.copy()
+    t[1, 2, 3] = np.nan
+    t[2, 0, 100] = np.inf
+    wl.target = t
+    wl.target_bits = synth.f32_to_bf16_bits(t)
+    xs = np.zeros((B, gamma), np.int32)
+    got = pu.run_gpu_sample(wl, xs, tsamp=(1.0, 0, 1.0), dsamp=(1.0, 0, 1.0))
+    assert not (got["flags"][0] & oracle.FLAG_NONFINITE)
+    assert got["flags"][1] & oracle.FLAG_NONFINITE and got["flags"][2] & oracle.FLAG_NONFINITE
+
+
+def test_p_equals_q_accepts_everything():
+    wl = _edge_workload(5000, 6, 8, "bf16", seed=8)
+    wl.draft = wl.target[:, :6].copy()
+    wl.draft_bits = wl.target_bits[:, :6].copy()
+    s = (0.9, 50, 0.9)
+    xs = pu.oracle_proposals(wl, draft_sampler=s)
+    got = pu.run_gpu_sample(wl, xs, tsamp=s, dsamp=s)
+    assert np.all(got["num_accepted"] == 6)
+
+
+def test_deterministic_bitwise():
+    wl = pu.make("c5", B=8, V=30011)
+    xs = pu.oracle_proposals(wl)
+    a = pu.run_gpu_sample(wl, xs)
+    b = pu.run_gpu_sample(wl, xs)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_device_philox_equals_oracle_philox():
+    # bonus draws from a uniform p over 1024 tokens reveal ten bits of each u
+    B, gamma, V = 512, 2, 1024
+    wl = _edge_workload(V, gamma, B, "f32", seed=1)
+    wl.target[:] = 0.0
+    wl.draft[:] = 0.0
+    xs = np.zeros((B, gamma), np.int32)
+    for seed, offset in [(0, 0), (12345, 7), (2**63 + 5, 2**40 + 3)]:
+        got = pu.run_gpu_sample(wl, xs, tsamp=(1.0, 0, 1.0), dsamp=(1.0, 0, 1.0), seed=seed,
+                                offset=offset)
+        u = pu.philox_uniforms(seed, offset, B, gamma)
+        assert np.all(got["num_accepted"] == gamma)
+        expect = np.ceil(u[:, gamma] * V).astype(np.int64) - 1
+        assert np.array_equal(got["tokens"][:, gamma], expect)
+        exp_u = pu.run_gpu_sample(wl, xs, tsamp=(1.0, 0, 1.0), dsamp=(1.0, 0, 1.0), uniforms=u)
+        assert np.array_equal(exp_u["tokens"], got["tokens"])
+
+
+@pytest.mark.parametrize("V", [3, 8, 16])
+def test_gpu_output_law_is_p(V):
+    """Lossless in distribution on the device: emitted tokens follow p."""
+    import torch
+    from scipy import stats
+    rng = np.random.default_rng(100 + V)
+    B, gamma = 40000, 2
+    zt = rng.normal(0, 1.5, (gamma + 1, V)).astype(np.float32)
+    zd = (zt[:gamma] + rng.normal(0, 1.0, (gamma, V))).astype(np.float32)
+    zd[0, int(np.argmax(zt[0]))] = -np.inf          # q = 0 where p is largest
+    s = oracle.Sampler(1.0)
+    p = [oracle.row_distribution(zt[i].astype(np.float64), s).p for i in range(gamma + 1)]
+    q = [oracle.row_distribution(zd[i].astype(np.float64), s).p for i in range(gamma)]
+    xs = np.stack([rng.choice(V, B, p=q[i]) for i in range(gamma)], axis=1).astype(np.int32)
+    dev = torch.device("cuda:0")
+    import lossless_draft_verification_sample_amd as sv
+    out = sv.spec_verify_sample(
+        torch.from_numpy(np.broadcast_to(zt, (B, gamma + 1, V)).copy()).to(dev),
+        torch.from_numpy(np.broadcast_to(zd, (B, gamma, V)).copy()).to(dev),
+        torch.from_numpy(xs).to(dev), seed=V, offset=1)
+    torch.cuda.synchronize()
+    tok = out.tokens.cpu().numpy()
+    n = out.num_accepted.cpu().numpy()
+    for i in range(gamma + 1):
+        reached = n >= i
+        counts = np.bincount(tok[reached, i], minlength=V)
+        exp = p[i] * reached.sum()
+        assert stats.chisquare(counts, exp).pvalue > 1e-4, i
+    assert np.bincount(tok[:, 0], minlength=V)[int(np.argmax(zt[0]))] > 0
+
+
+def test_boundary_fraction_many_decisions():
+    wl = pu.make("c1", B=4096, seed=2024)
+    cfg = wl.cfg
+    xs = pu.oracle_proposals(wl)
+    u = pu.philox_uniforms(cfg.philox_seed, 11, cfg.B, cfg.gamma)
+    got = pu.run_gpu_sample(wl, xs, offset=11)
+    ref = pu.run_oracle_sample(wl, xs, u, range(cfg.B))
+    nb = pu.compare_sample(got, ref, range(cfg.B), where="c1x4096")
+    decisions = cfg.B * (cfg.gamma + 1)
+    assert nb / decisions < 1e-4
