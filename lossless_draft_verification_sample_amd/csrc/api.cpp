@@ -192,6 +192,8 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.target = target_logits;
     a.draft = draft_logits;
     a.bf16 = bf16;
+    a.vec = ((uintptr_t)target_logits % 16 == 0) && ((uintptr_t)draft_logits % 16 == 0) &&
+            ((size_t)V * es) % 16 == 0;
     a.gamma = gamma;
     a.V = V;
     a.nchunk = L.nchunk;

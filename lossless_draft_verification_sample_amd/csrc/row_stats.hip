@@ -21,16 +21,21 @@
 //   top-p  = the last value whose strictly-larger mass is < top_p * Z,
 // all exact (integer counts, fp64 sums in a fixed order, so the result is also
 // bitwise reproducible). Banned ids are subtracted from the counts afterwards
-// (the ban list is sorted and de-duplicated beforehand). A row holding a finite
-// value outside the counted range falls back to the generic path.
+// (the ban list is sorted and de-duplicated beforehand). Nonzero values below
+// 2^-23 in magnitude are rare but do occur in large rows; they are counted with
+// the zero bin and kept, up to TINY_MAX of them, in a small list whose exact
+// contribution is added in a fixed (sorted) order. A row holding a value of
+// magnitude >= 2^9, more tiny values than the list holds, or a truncation cut
+// that falls among the tiny values is handed to the generic path.
 //
 // fp32 rows (generic path). One streaming pass keeps, per lane, the running
-// maximum and sum of exp2(z*log2e/T - ref) against an integer reference ref
-// that only ever increases, so rescaling is an exact power of two; the
-// per-lane sums are combined exactly at the end. Thresholds, when asked for,
-// come from a bisection over the order-preserving integer keys of the values,
-// one pass over the row per step. This path is exact in the same sense, only
-// slower for truncated rows.
+// maximum and the fp64 sum of exp2(z*log2e/T - ref) against an integer
+// reference ref that only ever increases, so rescaling is an exact power of
+// two; the per-lane sums are combined exactly at the end. Thresholds, when
+// asked for, come from a bisection over the order-preserving integer keys of
+// the values (16-bit keys for bf16 rows, 32-bit for fp32), one pass over the
+// row per step. Bans are tested against an LDS bitmap. Exact in the same
+// sense as the histogram path, only slower for truncated rows.
 
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
@@ -48,6 +53,8 @@ constexpr uint32_t HB_ZERO = HB_WIN;          // zero bin (a dump bin during the
 constexpr uint32_t HB_BINS = 2u * HB_WIN + 2u;
 constexpr int HB_RANKS = 2 * HB_WIN + 1;      // value-ordered ranks: +window, zero, -window
 constexpr int HB_RPT = (HB_RANKS + RS_THREADS - 1) / RS_THREADS;
+constexpr uint32_t TINY_MAX = 64;             // tiny values tracked exactly per row
+constexpr int BM_MAX_BITS = (int)HB_BINS * 32; // largest V whose ban bitmap fits the LDS
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,9 +72,13 @@ __device__ __forceinline__ float hb_value_of_rank(int r) {
 
 struct RowShared {
   uint32_t hist[HB_BINS];
-  uint32_t zero_cnt;
+  uint32_t zero_cnt;   // exact zeros and tiny values
   uint32_t nonfinite;
   uint32_t special;
+  uint32_t tiny_n;
+  uint16_t tiny[TINY_MAX];
+  double tiny_mass;
+  float tiny_top;
   int32_t sel;
   double dscr[RS_THREADS / WAVE];
   float fscr[RS_THREADS / WAVE];
@@ -80,13 +91,18 @@ __device__ __forceinline__ void hb_classify_slow(uint32_t bits, RowShared& sh) {
   const uint32_t ae = bits & 0x7FFFu;
   if (ae - HB_BASE < HB_WIN) return;          // inside the window: already counted
   if (ae == 0u) {
-    atomicAdd(&sh.zero_cnt, 1u);
-  } else if (bits == 0xFF80u) {
-    // -inf: an impossible token, not admissible
+    atomicAdd(&sh.zero_cnt, 1u);              // +0 and -0
   } else if ((ae & 0x7F80u) == 0x7F80u) {
-    sh.nonfinite = 1u;                        // NaN or +inf
+    if (bits != 0xFF80u) sh.nonfinite = 1u;   // NaN or +inf; -inf is a masked token
+  } else if (ae < HB_BASE) {
+    atomicAdd(&sh.zero_cnt, 1u);              // tiny: counted with zero, listed exactly
+    const uint32_t k = atomicAdd(&sh.tiny_n, 1u);
+    if (k < TINY_MAX)
+      sh.tiny[k] = (uint16_t)bits;
+    else
+      sh.special = 1u;
   } else {
-    sh.special = 1u;                          // tiny or huge finite value
+    sh.special = 1u;                          // |z| >= 2^9
   }
 }
 
@@ -154,20 +170,39 @@ __device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
   }
 }
 
+// Ban test of the generic path: an LDS bitmap when it fits, else a binary
+// search of the sorted list (also in LDS).
 struct GenericCtx {
-  const int32_t* bans;  // sorted unique ids in LDS
+  const uint32_t* bm;   // bitmap over [0, V) or nullptr
+  const int32_t* bans;  // sorted unique ids when bm == nullptr
   int nb;
   __device__ __forceinline__ bool admissible(float z, int id) const {
     // finite and not banned; NaN fails both comparisons
     if (!(z > -INFINITY && z < INFINITY)) return false;
-    return nb == 0 || !in_sorted(bans, nb, id);
+    if (nb == 0) return true;
+    if (bm) return !((bm[id >> 5] >> (id & 31)) & 1u);
+    return !in_sorted(bans, nb, id);
   }
 };
+
+// Order-preserving keys for the bisection: 16 bits for bf16 rows, 32 for fp32.
+template <typename Elem>
+__device__ __forceinline__ uint32_t gkey(float v) {
+  return sizeof(Elem) == 2 ? (f32_key(v) >> 16) : f32_key(v);
+}
+// The smallest float whose key is k (so z >= gval(k) <=> key(z) >= k for row values).
+template <typename Elem>
+__device__ __forceinline__ float gval(uint32_t k) {
+  if (sizeof(Elem) == 2) {
+    const uint32_t k32 = k << 16;
+    return f32_from_key((k32 & 0x80000000u) ? k32 : (k32 | 0xFFFFu));
+  }
+  return f32_from_key(k);
+}
 
 template <typename Elem>
 __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const GenericCtx& g,
                             RowShared& sh, RowStat& out) {
-  const int tid = threadIdx.x;
   const double c2 = 1.4426950408889634 / (double)s.temperature;  // log2(e) / T
   // pass 1: max, min, count and the exp-sum against per-lane integer references
   float mx = -INFINITY, mn = INFINITY;
@@ -185,7 +220,7 @@ __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const G
       if (ref > -INFINITY) acc = ldexp(acc, (int)fmax(ref - nr, -2000.0));
       ref = nr;
     }
-    acc += (double)exp2f((float)(e - ref));
+    acc += exp2(e - ref);
   });
   mx = block_max<RS_THREADS>(mx, sh.fscr);
   mn = block_min<RS_THREADS>(mn, sh.fscr);
@@ -198,15 +233,16 @@ __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const G
     out.tau = -INFINITY;
     out.lse = -INFINITY;
     out.flags |= FLAG_EMPTY;
+    out.path = 1u;
     return;
   }
-  double Z = block_sum<RS_THREADS>(ref > -INFINITY ? ldexp(acc, (int)fmax(ref - rmax, -2000.0)) : 0.0,
-                                   sh.dscr);
-  // mass of the admissible values >= thr (relative to 2^rmax)
+  double Z = block_sum<RS_THREADS>(
+      ref > -INFINITY ? ldexp(acc, (int)fmax(ref - rmax, -2000.0)) : 0.0, sh.dscr);
+  // mass (relative to 2^rmax) and count of the admissible values >= thr
   auto mass_ge = [&](float thr) -> double {
     double a = 0.0;
     for_each_elem<Elem>(rowp, V, [&](float z, int id) {
-      if (z >= thr && g.admissible(z, id)) a += (double)exp2f((float)((double)z * c2 - rmax));
+      if (z >= thr && g.admissible(z, id)) a += exp2((double)z * c2 - rmax);
     });
     return block_sum<RS_THREADS>(a, sh.dscr);
   };
@@ -221,27 +257,26 @@ __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const G
   bool trunc = false;
   if (s.top_k > 0 && (uint32_t)s.top_k < cnt) {
     // largest key t with count(z >= value(t)) >= k
-    uint32_t lo = f32_key(mn), hi = f32_key(mx) + 1u;
+    uint32_t lo = gkey<Elem>(mn), hi = gkey<Elem>(mx) + 1u;
     while (hi - lo > 1u) {
       const uint32_t mid = lo + (hi - lo) / 2u;
-      if (count_ge(f32_from_key(mid)) >= (uint32_t)s.top_k)
+      if (count_ge(gval<Elem>(mid)) >= (uint32_t)s.top_k)
         lo = mid;
       else
         hi = mid;
     }
-    tau = f32_from_key(lo);
+    tau = gval<Elem>(lo);
     trunc = true;
     Z = mass_ge(tau);
   }
   if (s.top_p < 1.0f) {
     // largest key t with mass(z >= value(t)) >= top_p * Z (within the top-k set)
     const double target = (double)s.top_p * Z;
-    const float lo_v = trunc ? fmaxf(tau, mn) : mn;
-    uint32_t lo = f32_key(lo_v), hi = f32_key(mx) + 1u;
+    uint32_t lo = gkey<Elem>(trunc ? fmaxf(tau, mn) : mn), hi = gkey<Elem>(mx) + 1u;
     double zlo = Z;
     while (hi - lo > 1u) {
       const uint32_t mid = lo + (hi - lo) / 2u;
-      const double mm = mass_ge(f32_from_key(mid));
+      const double mm = mass_ge(gval<Elem>(mid));
       if (mm >= target) {
         lo = mid;
         zlo = mm;
@@ -249,7 +284,7 @@ __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const G
         hi = mid;
       }
     }
-    tau = f32_from_key(lo);
+    tau = gval<Elem>(lo);
     trunc = true;
     Z = zlo;
   }
@@ -257,6 +292,140 @@ __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const G
   out.tau = trunc ? tau : -INFINITY;
   out.lse = rmax * 0.6931471805599453 + log(Z);
   out.path = 1u;
+}
+
+// ------------------------------------------------------------------ histogram epilogue
+
+// Exact statistics from the counts; false when the row must go to the generic
+// path (a truncation cut among the tiny values). Called by the whole block.
+__device__ bool hb_epilogue(const SamplerDev s, RowShared& sh, RowStat& out) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sh.hist[HB_ZERO] = sh.zero_cnt;
+    // tiny values in ascending order: a fixed summation order below
+    const int n = (int)min(sh.tiny_n, TINY_MAX);
+    for (int i = 1; i < n; ++i) {
+      const uint16_t v = sh.tiny[i];
+      const float fv = bf16_to_f32(v);
+      int j = i - 1;
+      while (j >= 0 && bf16_to_f32(sh.tiny[j]) > fv) {
+        sh.tiny[j + 1] = sh.tiny[j];
+        --j;
+      }
+      sh.tiny[j + 1] = v;
+    }
+  }
+  __syncthreads();
+  const uint32_t tn = min(sh.tiny_n, TINY_MAX);
+
+  const int r0 = tid * HB_RPT;
+  uint32_t cloc = 0u;
+  int top = HB_RANKS;
+#pragma unroll
+  for (int j = 0; j < HB_RPT; ++j) {
+    const int r = r0 + j;
+    if (r < HB_RANKS) {
+      const uint32_t c = sh.hist[hb_bin_of_rank(r)];
+      cloc += c;
+      if (c && top == HB_RANKS) top = r;
+    }
+  }
+  const uint32_t N = block_sum<RS_THREADS>(cloc, sh.uscr);
+  const int rtop = block_min<RS_THREADS>(top, sh.iscr);
+  if (N == 0u) {
+    out.flags |= FLAG_EMPTY;
+    return true;
+  }
+  // reference logit md: the largest counted value (0 when the top rank is the
+  // zero bin, whose tiny members are weighed exactly below)
+  const float m = hb_value_of_rank(rtop);
+  const double md = (double)m;
+  const double invT = 1.0 / (double)s.temperature;
+  if (tid == 0) {
+    double tm = 0.0;
+    float top_tiny = -INFINITY;
+    for (uint32_t i = 0; i < tn; ++i) {
+      const float v = bf16_to_f32(sh.tiny[i]);
+      tm += exp(((double)v - md) * invT);
+      top_tiny = fmaxf(top_tiny, v);
+    }
+    sh.tiny_mass = tm;
+    sh.tiny_top = top_tiny;
+  }
+  __syncthreads();
+  const double tiny_mass = sh.tiny_mass;
+  auto rank_mass = [&](int r, uint32_t c) -> double {
+    if (r == (int)HB_ZERO)
+      return (double)(c - tn) * exp(-md * invT) + tiny_mass;
+    return (double)c * exp(((double)hb_value_of_rank(r) - md) * invT);
+  };
+
+  int rk = HB_RANKS - 1;
+  bool trunc = false;
+  if (s.top_k > 0 && (uint32_t)s.top_k < N) {
+    uint32_t tot;
+    const uint32_t before = block_excl_scan<RS_THREADS>(cloc, sh.uscr, &tot);
+    const uint32_t k = (uint32_t)s.top_k;
+    if (before < k && before + cloc >= k) {
+      uint32_t cum = before;
+#pragma unroll
+      for (int j = 0; j < HB_RPT; ++j) {
+        const int r = r0 + j;
+        if (r < HB_RANKS) {
+          cum += sh.hist[hb_bin_of_rank(r)];
+          if (cum >= k) {
+            sh.sel = r;
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    rk = sh.sel;
+    trunc = true;
+    if (rk == (int)HB_ZERO && tn > 0u) return false;
+  }
+  // masses of the values kept by top-k
+  double mloc = 0.0;
+#pragma unroll
+  for (int j = 0; j < HB_RPT; ++j) {
+    const int r = r0 + j;
+    if (r <= rk) {
+      const uint32_t c = sh.hist[hb_bin_of_rank(r)];
+      if (c) mloc += rank_mass(r, c);
+    }
+  }
+  double Z = block_sum<RS_THREADS>(mloc, sh.dscr);
+  int rp_last = rk;
+  if (s.top_p < 1.0f) {
+    double tot;
+    const double before = block_excl_scan<RS_THREADS>(mloc, sh.dscr, &tot);
+    const double target = (double)s.top_p * Z;
+    double above = before, zloc = 0.0;
+    int last = -1;
+    for (int j = 0; j < HB_RPT; ++j) {
+      const int r = r0 + j;
+      if (r > rk || !(above < target)) break;
+      const uint32_t c = sh.hist[hb_bin_of_rank(r)];
+      if (c) {
+        const double w = rank_mass(r, c);
+        last = r;
+        zloc += w;
+        above += w;
+      }
+    }
+    rp_last = block_max<RS_THREADS>(last, sh.iscr);
+    Z = block_sum<RS_THREADS>(zloc, sh.dscr);
+    trunc = true;
+    if (rp_last == (int)HB_ZERO && tn > 0u) return false;
+  }
+  // the largest kept logit (a tiny positive can top the zero bin)
+  out.m = (rtop == (int)HB_ZERO && tn > 0u)
+              ? ((sh.zero_cnt > tn) ? fmaxf(0.0f, sh.tiny_top) : sh.tiny_top)
+              : m;
+  out.tau = trunc ? hb_value_of_rank(rp_last) : -INFINITY;
+  out.lse = md * invT + log(Z);
+  return true;
 }
 
 // ------------------------------------------------------------------ the kernel
@@ -293,6 +462,7 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
       sh.zero_cnt = 0u;
       sh.nonfinite = 0u;
       sh.special = 0u;
+      sh.tiny_n = 0u;
     }
     __syncthreads();
 
@@ -342,106 +512,35 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
         atomicSub(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
       else if (ae == 0u)
         atomicSub(&sh.zero_cnt, 1u);
+      else if (ae < HB_BASE)
+        sh.special = 1u;   // a banned tiny value: the generic path sorts it out
     }
     __syncthreads();
     if (sh.nonfinite) out.flags |= FLAG_NONFINITE;
-    if (sh.special) {
-      generic = true;
-    } else {
-      if (tid == 0) sh.hist[HB_ZERO] = sh.zero_cnt;
-      __syncthreads();
-
-      const int r0 = tid * HB_RPT;
-      uint32_t cloc = 0u;
-      int top = HB_RANKS;
-#pragma unroll
-      for (int j = 0; j < HB_RPT; ++j) {
-        const int r = r0 + j;
-        if (r < HB_RANKS) {
-          const uint32_t c = sh.hist[hb_bin_of_rank(r)];
-          cloc += c;
-          if (c && top == HB_RANKS) top = r;
-        }
-      }
-      const uint32_t N = block_sum<RS_THREADS>(cloc, sh.uscr);
-      const int rtop = block_min<RS_THREADS>(top, sh.iscr);
-      if (N == 0u) {
-        out.flags |= FLAG_EMPTY;
-      } else {
-        const float m = hb_value_of_rank(rtop);
-        const double md = (double)m;
-        const double invT = 1.0 / (double)s.temperature;
-        int rk = HB_RANKS - 1;
-        bool trunc = false;
-        if (s.top_k > 0 && (uint32_t)s.top_k < N) {
-          uint32_t tot;
-          const uint32_t before = block_excl_scan<RS_THREADS>(cloc, sh.uscr, &tot);
-          const uint32_t k = (uint32_t)s.top_k;
-          if (before < k && before + cloc >= k) {
-            uint32_t cum = before;
-#pragma unroll
-            for (int j = 0; j < HB_RPT; ++j) {
-              const int r = r0 + j;
-              if (r < HB_RANKS) {
-                cum += sh.hist[hb_bin_of_rank(r)];
-                if (cum >= k) {
-                  sh.sel = r;
-                  break;
-                }
-              }
-            }
-          }
-          __syncthreads();
-          rk = sh.sel;
-          trunc = true;
-        }
-        // masses of the kept-after-top-k values
-        double mloc = 0.0;
-#pragma unroll
-        for (int j = 0; j < HB_RPT; ++j) {
-          const int r = r0 + j;
-          if (r <= rk) {
-            const uint32_t c = sh.hist[hb_bin_of_rank(r)];
-            if (c) mloc += (double)c * exp(((double)hb_value_of_rank(r) - md) * invT);
-          }
-        }
-        double Z = block_sum<RS_THREADS>(mloc, sh.dscr);
-        int rp_last = rk;
-        if (s.top_p < 1.0f) {
-          double tot;
-          const double before = block_excl_scan<RS_THREADS>(mloc, sh.dscr, &tot);
-          const double target = (double)s.top_p * Z;
-          double above = before, zloc = 0.0;
-          int last = -1;
-          for (int j = 0; j < HB_RPT; ++j) {
-            const int r = r0 + j;
-            if (r > rk || !(above < target)) break;
-            const uint32_t c = sh.hist[hb_bin_of_rank(r)];
-            if (c) {
-              const double w = (double)c * exp(((double)hb_value_of_rank(r) - md) * invT);
-              last = r;
-              zloc += w;
-              above += w;
-            }
-          }
-          rp_last = block_max<RS_THREADS>(last, sh.iscr);
-          Z = block_sum<RS_THREADS>(zloc, sh.dscr);
-          trunc = true;
-        }
-        out.m = m;
-        out.tau = trunc ? hb_value_of_rank(rp_last) : -INFINITY;
-        out.lse = md * invT + log(Z);
-      }
-    }
+    if (sh.special || !hb_epilogue(s, sh, out)) generic = true;
   }
 
   if (generic) {
     __syncthreads();
-    // the ban list moves into LDS (reusing the histogram storage)
-    int32_t* lbans = (int32_t*)sh.hist;
-    for (int j = tid; j < nb; j += RS_THREADS) lbans[j] = bans[j];
-    __syncthreads();
-    GenericCtx g{lbans, nb};
+    // bans move into LDS (reusing the histogram storage): a bitmap if it fits
+    GenericCtx g{nullptr, nullptr, nb};
+    if (nb > 0) {
+      if (V <= BM_MAX_BITS) {
+        const int words = (V + 31) >> 5;
+        for (int k = tid; k < words; k += RS_THREADS) sh.hist[k] = 0u;
+        __syncthreads();
+        for (int j = tid; j < nb; j += RS_THREADS) {
+          const int id = bans[j];
+          atomicOr(&sh.hist[id >> 5], 1u << (id & 31));
+        }
+        g.bm = sh.hist;
+      } else {
+        int32_t* lbans = (int32_t*)sh.hist;
+        for (int j = tid; j < nb; j += RS_THREADS) lbans[j] = bans[j];
+        g.bans = lbans;
+      }
+      __syncthreads();
+    }
     out.flags &= ~FLAG_EMPTY;
     row_generic<Elem>(rowp, V, s, g, sh, out);
   }

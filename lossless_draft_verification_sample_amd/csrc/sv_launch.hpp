@@ -55,6 +55,7 @@ struct DrawArgs {
   const void* target;
   const void* draft;
   int bf16;
+  int vec;                    // rows 16-byte aligned and V*size a multiple of 16
   int gamma, V, nchunk;
   float t_temp, d_temp;
   const int32_t* ban_sorted;

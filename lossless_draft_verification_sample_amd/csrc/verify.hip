@@ -150,12 +150,16 @@ int launch_accept(const AcceptArgs& a, int B, hipStream_t st) {
 // ------------------------------------------------------------------ final draw
 
 constexpr int DR_THREADS = 256;
+constexpr int GRP = 8;                                   // logits per group
+constexpr int GPT = DRAW_CHUNK / GRP / DR_THREADS;       // groups per thread
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct DrawRow {
   const void* trow;
-  const void* drow;  // nullptr for the bonus draw
+  const void* drow;   // nullptr for the bonus draw
   RowStat ts, ds;
-  double tc2, tl2, dc2, dl2;  // log2(e)/T and lse*log2(e) of both rows
+  double tinv, dinv;  // 1/T of both rows
 };
 
 __device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n) {
@@ -165,28 +169,65 @@ __device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n) {
   const size_t es = a.bf16 ? 2 : 4;
   r.trow = (const char*)a.target + ((int64_t)b * G1 + n) * V * es;
   r.ts = a.stats[(int64_t)b * RPR + n];
-  r.tc2 = 1.4426950408889634 / (double)a.t_temp;
-  r.tl2 = r.ts.lse * 1.4426950408889634;
+  r.tinv = 1.0 / (double)a.t_temp;
   if (n < g) {
     r.drow = (const char*)a.draft + ((int64_t)b * g + n) * V * es;
     r.ds = a.stats[(int64_t)b * RPR + G1 + n];
-    r.dc2 = 1.4426950408889634 / (double)a.d_temp;
-    r.dl2 = r.ds.lse * 1.4426950408889634;
+    r.dinv = 1.0 / (double)a.d_temp;
   } else {
     r.drow = nullptr;
   }
   return r;
 }
 
-// Weight of token x: w = max(0, p - q) (residual) or p (bonus), and p itself.
-__device__ __forceinline__ void token_weights(const DrawArgs& a, const DrawRow& r, int x,
-                                              bool banned, float& w, float& p) {
-  const float zt = load_logit(r.trow, a.bf16, x);
-  p = is_kept(zt, r.ts, banned) ? exp2f((float)((double)zt * r.tc2 - r.tl2)) : 0.0f;
+// Eight consecutive logits starting at x0, as raw bits (-inf beyond the row).
+template <typename Elem>
+struct Group {
+  u32x4 w[sizeof(Elem) == 2 ? 1 : 2];
+};
+
+template <typename Elem>
+__device__ __forceinline__ void load_group(const void* row, int x0, int V, bool vec, Group<Elem>& g) {
+  const Elem* e = (const Elem*)row;
+  if constexpr (sizeof(Elem) == 2) {
+    if (vec) {
+      g.w[0] = *(const u32x4*)(e + x0);   // V % 8 == 0 on this path
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = x0 + 2 * j < V ? (uint32_t)e[x0 + 2 * j] : 0xFF80u;
+        const uint32_t hi = x0 + 2 * j + 1 < V ? (uint32_t)e[x0 + 2 * j + 1] : 0xFF80u;
+        g.w[0][j] = lo | (hi << 16);
+      }
+    }
+  } else {
+    if (vec) {
+      const u32x4* p = (const u32x4*)(e + x0);
+      g.w[0] = p[0];                       // V % 4 == 0 on this path
+      g.w[1] = x0 + 4 < V ? p[1] : (u32x4)(0xFF800000u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        g.w[j >> 2][j & 3] = x0 + j < V ? __float_as_uint(e[x0 + j]) : 0xFF800000u;
+    }
+  }
+}
+
+template <typename Elem>
+__device__ __forceinline__ float group_val(const Group<Elem>& g, int j) {
+  if constexpr (sizeof(Elem) == 2) return bf16_to_f32((g.w[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+  return __uint_as_float(g.w[j >> 2][j & 3]);
+}
+
+// p(x) and the draw weight of token x: max(0, p - q) at a rejection, p for the
+// bonus draw. fp64 throughout (exp of an fp64 argument), so the running sums
+// of the inverse CDF carry no fp32 error.
+__device__ __forceinline__ void pair_weight(const DrawRow& r, float zt, float zd, bool banned,
+                                            double& w, double& p) {
+  p = is_kept(zt, r.ts, banned) ? exp((double)zt * r.tinv - r.ts.lse) : 0.0;
   if (r.drow) {
-    const float zd = load_logit(r.drow, a.bf16, x);
-    const float q = is_kept(zd, r.ds, banned) ? exp2f((float)((double)zd * r.dc2 - r.dl2)) : 0.0f;
-    w = p > q ? p - q : 0.0f;
+    const double q = is_kept(zd, r.ds, banned) ? exp((double)zd * r.dinv - r.ds.lse) : 0.0;
+    w = p > q ? p - q : 0.0;
   } else {
     w = p;
   }
@@ -207,29 +248,51 @@ __device__ __forceinline__ void chunk_bans(uint32_t* bm, const int32_t* bans, in
   __syncthreads();
 }
 
+__device__ __forceinline__ bool bm_test(const uint32_t* bm, int o) {
+  return (bm[o >> 5] >> (o & 31)) & 1u;
+}
+
+template <typename Elem>
 __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a) {
   __shared__ uint32_t bm[DRAW_CHUNK / 32];
   __shared__ double scr[DR_THREADS / WAVE];
+  const int tid = threadIdx.x;
   const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
   const ReqState rs = a.req[b];
   const DrawRow r = draw_row(a, b, rs.n);
   const int nb = a.ban_count ? a.ban_count[b] : 0;
   const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
   const int c0 = c * DRAW_CHUNK;
-  const int c1 = min(a.V, c0 + DRAW_CHUNK);
+  const bool vec = a.vec;
+  // every load of this thread in flight before any use
+  Group<Elem> tg[GPT], dg[GPT];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int x0 = c0 + (j * DR_THREADS + tid) * GRP;
+    if (x0 < a.V) {
+      load_group<Elem>(r.trow, x0, a.V, vec, tg[j]);
+      if (r.drow) load_group<Elem>(r.drow, x0, a.V, vec, dg[j]);
+    }
+  }
   chunk_bans(bm, bans, nb, c0);
   double sw = 0.0, sp = 0.0;
-  for (int x = c0 + threadIdx.x; x < c1; x += DR_THREADS) {
-    const int o = x - c0;
-    const bool banned = (bm[o >> 5] >> (o & 31)) & 1u;
-    float w, p;
-    token_weights(a, r, x, banned, w, p);
-    sw += (double)w;
-    sp += (double)p;
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int x0 = c0 + (j * DR_THREADS + tid) * GRP;
+    if (x0 < a.V) {
+#pragma unroll
+      for (int e = 0; e < GRP; ++e) {
+        double w, p;
+        pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
+                    bm_test(bm, x0 - c0 + e), w, p);
+        sw += w;
+        sp += p;
+      }
+    }
   }
   sw = block_sum<DR_THREADS>(sw, scr);
   sp = block_sum<DR_THREADS>(sp, scr);
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     ChunkSums cs;
     cs.w = sw;
     cs.p = sp;
@@ -238,10 +301,14 @@ __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a
 }
 
 int launch_residual_partial(const DrawArgs& a, int B, hipStream_t st) {
-  hipLaunchKernelGGL(residual_partial_kernel, dim3(a.nchunk * B), dim3(DR_THREADS), 0, st, a);
+  if (a.bf16)
+    hipLaunchKernelGGL(residual_partial_kernel<uint16_t>, dim3(a.nchunk * B), dim3(DR_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(residual_partial_kernel<float>, dim3(a.nchunk * B), dim3(DR_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+template <typename Elem>
 __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a) {
   __shared__ uint32_t bm[DRAW_CHUNK / 32];
   __shared__ double scr[DR_THREADS / WAVE];
@@ -321,17 +388,31 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
     const int nb = a.ban_count ? a.ban_count[b] : 0;
     const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
     const int c0 = c * DRAW_CHUNK;
-    const int c1 = min(a.V, c0 + DRAW_CHUNK);
+    // each thread owns GPT consecutive groups: tokens [x0, x0 + GPT*GRP) in id order
+    const int x0 = c0 + tid * GPT * GRP;
+    Group<Elem> tg[GPT], dg[GPT];
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int xg = x0 + j * GRP;
+      if (xg < a.V) {
+        load_group<Elem>(r.trow, xg, a.V, a.vec, tg[j]);
+        if (r.drow) load_group<Elem>(r.drow, xg, a.V, a.vec, dg[j]);
+      }
+    }
     chunk_bans(bm, bans, nb, c0);
-    // contiguous runs of DRAW_CHUNK / DR_THREADS tokens per thread, in id order
-    constexpr int RUN = DRAW_CHUNK / DR_THREADS;
-    const int x0 = c0 + tid * RUN;
     double lsum = 0.0;
-    for (int x = x0; x < x0 + RUN && x < c1; ++x) {
-      const int o = x - c0;
-      float w, p;
-      token_weights(a, r, x, (bm[o >> 5] >> (o & 31)) & 1u, w, p);
-      lsum += (double)(use_p ? p : w);
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int xg = x0 + j * GRP;
+      if (xg < a.V) {
+#pragma unroll
+        for (int e = 0; e < GRP; ++e) {
+          double w, p;
+          pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
+                      bm_test(bm, xg - c0 + e), w, p);
+          lsum += use_p ? p : w;
+        }
+      }
     }
     double ctot;
     const double cb = block_excl_scan<DR_THREADS>(lsum, scr, &ctot);
@@ -343,16 +424,24 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
     __syncthreads();
     if (tid == who) {
       double run = cb;
-      for (int x = x0; x < x0 + RUN && x < c1; ++x) {
-        const int o = x - c0;
-        float w, p;
-        token_weights(a, r, x, (bm[o >> 5] >> (o & 31)) & 1u, w, p);
-        const float v = use_p ? p : w;
-        if (v > 0.0f) {
-          sel_x = x;                // the last token with weight unless one reaches tl
-          if (run + (double)v >= tl) break;
+      bool done = false;
+#pragma unroll
+      for (int j = 0; j < GPT; ++j) {
+        const int xg = x0 + j * GRP;
+#pragma unroll
+        for (int e = 0; e < GRP; ++e) {
+          if (!done && xg + e < a.V) {
+            double w, p;
+            pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
+                        bm_test(bm, xg - c0 + e), w, p);
+            const double v = use_p ? p : w;
+            if (v > 0.0) {
+              sel_x = xg + e;       // the last token with weight unless one reaches tl
+              if (run + v >= tl) done = true;
+            }
+            run += v;
+          }
         }
-        run += (double)v;
       }
     }
     __syncthreads();
@@ -366,7 +455,10 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
 }
 
 int launch_residual_select(const DrawArgs& a, int B, hipStream_t st) {
-  hipLaunchKernelGGL(residual_select_kernel, dim3(B), dim3(DR_THREADS), 0, st, a);
+  if (a.bf16)
+    hipLaunchKernelGGL(residual_select_kernel<uint16_t>, dim3(B), dim3(DR_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(residual_select_kernel<float>, dim3(B), dim3(DR_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -170,6 +170,7 @@ class SampleResult:
     draft_lse: np.ndarray         # [B, gamma] float64
     boundary: np.ndarray          # [B] bool: some decision lay within BOUNDARY_EPS
     accept_prob: np.ndarray = field(default=None)   # [B, gamma] min(1, p/q), nan if not reached
+    margin: np.ndarray = field(default=None)        # [B] smallest distance of any decision to its edge
 
 
 def verify_sample(target, draft, draft_tokens, uniforms, target_sampler, draft_sampler,
@@ -205,30 +206,32 @@ def verify_sample(target, draft, draft_tokens, uniforms, target_sampler, draft_s
     dlse = np.zeros((B, gamma))
     boundary = np.zeros(B, dtype=bool)
     acc_prob = np.full((B, gamma), np.nan)
+    margin = np.full(B, math.inf)
 
     for b in range(B):
         bans = () if banned is None else [t for t in np.asarray(banned[b]).tolist() if t >= 0]
         pt = [row_distribution(target[b, i], target_sampler, bans) for i in range(gamma + 1)]
         qd = [row_distribution(draft[b, i], draft_sampler, bans) for i in range(gamma)]
         f = 0
+        mg = math.inf
         for d in pt + qd:
             if d.nonfinite:
                 f |= FLAG_NONFINITE
             if d.empty:
                 f |= FLAG_EMPTY
-            if d.topp_margin <= BOUNDARY_EPS:
-                boundary[b] = True
+            mg = min(mg, d.topp_margin)
         tlse[b] = [d.lse for d in pt]
         dlse[b] = [d.lse for d in qd]
-        out, n, fb, bnd, ap = verify_block([d.p for d in pt], [d.p for d in qd],
+        out, n, fb, bmg, ap = verify_block([d.p for d in pt], [d.p for d in qd],
                                            draft_tokens[b], uniforms[b])
         tokens[b] = out
         num_acc[b] = n
         flags[b] = f | fb
-        boundary[b] |= bnd
+        margin[b] = min(mg, bmg)
+        boundary[b] = margin[b] <= BOUNDARY_EPS
         acc_prob[b] = ap
 
-    return SampleResult(tokens, num_acc, flags, tlse, dlse, boundary, acc_prob)
+    return SampleResult(tokens, num_acc, flags, tlse, dlse, boundary, acc_prob, margin)
 
 
 def accept(u, p_x, q_x):
@@ -252,7 +255,10 @@ def verify_block(p_rows, q_rows, xs, u):
 
     p_rows: gamma+1 target distributions; q_rows: gamma draft distributions;
     xs: gamma proposals; u: gamma+1 uniforms. Returns
-    (tokens[gamma+1], n_accepted, flags, boundary, accept_prob[gamma]).
+    (tokens[gamma+1], n_accepted, flags, margin, accept_prob[gamma]), where
+    margin is the smallest distance, in units of u, between a uniform the walk
+    consumed and the edge of the decision it took (the acceptance threshold
+    p/q, or either cumulative edge of the drawn token's cell).
     """
     gamma = len(q_rows)
     V = len(p_rows[0])
@@ -260,7 +266,7 @@ def verify_block(p_rows, q_rows, xs, u):
     tokens = np.full(gamma + 1, -1, dtype=np.int32)
     acc_prob = np.full(gamma, np.nan)
     f = 0
-    boundary = False
+    margin = math.inf
     if any(x < 0 or x >= V for x in xs):
         f |= FLAG_TOKEN_RANGE
 
@@ -279,8 +285,7 @@ def verify_block(p_rows, q_rows, xs, u):
             break
         ratio = p_x / q_x
         acc_prob[i] = min(1.0, ratio)
-        if abs(u[i] - ratio) <= BOUNDARY_EPS:
-            boundary = True
+        margin = min(margin, abs(u[i] - ratio))
         if accept(u[i], p_x, q_x):
             tokens[i] = x
         else:
@@ -298,10 +303,9 @@ def verify_block(p_rows, q_rows, xs, u):
         x, S, dist = sample_categorical(p_rows[n], u[gamma])
     if x < 0:
         f |= FLAG_EMPTY
-    if dist <= BOUNDARY_EPS:
-        boundary = True
+    margin = min(margin, dist)
     tokens[n] = x
-    return tokens, n, f, boundary, acc_prob
+    return tokens, n, f, margin, acc_prob
 
 
 @dataclass

@@ -90,11 +90,23 @@ def philox_uniforms(seed, offset, B, gamma):
     return np.array(oracle.uniforms(seed, offset, B, gamma), dtype=np.float64)
 
 
+# A request is excluded from the bit-exact comparison only when one of its
+# uniforms lies within EXACT_BAND of the edge of a decision the oracle took.
+# The stated tolerance is 1e-6; the HIP path computes every decision quantity
+# in fp64, so the much tighter band below is sound and is what the tests use.
+# Counts under the stated band are reported alongside.
+STATED_BAND = 1e-6
+EXACT_BAND = 1e-10
+
+
 def compare_sample(got, ref, reqs, lse_tol=1e-5, check_flags=True, where=""):
     """Bit-exact tokens/accept counts/flags outside boundary cases; lse within
-    lse_tol (absolute, relative to max(1, |lse|)). Returns the boundary count."""
+    lse_tol (absolute, relative to max(1, |lse|)). Returns the number of
+    requests excluded (margin <= EXACT_BAND); the count under STATED_BAND is
+    stored in compare_sample.last_stated."""
     reqs = list(reqs)
-    bnd = ref.boundary
+    bnd = ref.margin <= EXACT_BAND
+    compare_sample.last_stated = int((ref.margin <= STATED_BAND).sum())
     for k, b in enumerate(reqs):
         if ref.flags[k] & oracle.FLAG_NONFINITE:
             assert got["flags"][b] & oracle.FLAG_NONFINITE, (where, b)
