@@ -20,7 +20,7 @@ size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
   size_t stats, req, sums, bans, banc, total;
-  int nchunk;
+  int nchunk, nsub;
 };
 
 bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
@@ -31,13 +31,14 @@ bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
   const int64_t nchunk = ((int64_t)V + sv::DRAW_CHUNK - 1) / sv::DRAW_CHUNK;
   if ((int64_t)B * nchunk >= INT32_MAX) return false;
   L->nchunk = (int)nchunk;
+  L->nsub = (int)(((int64_t)V + sv::DRAW_SUB - 1) / sv::DRAW_SUB);
   size_t off = 0;
   L->stats = off;
   off = align_up(off + (size_t)rows * sizeof(sv::RowStat));
   L->req = off;
   off = align_up(off + (size_t)B * sizeof(sv::ReqState));
   L->sums = off;
-  off = align_up(off + (size_t)B * (size_t)nchunk * sizeof(sv::ChunkSums));
+  off = align_up(off + (size_t)B * (size_t)L->nsub * sizeof(sv::ChunkSums));
   L->bans = off;
   off = align_up(off + (size_t)B * (size_t)n_banned * sizeof(int32_t));
   L->banc = off;
@@ -197,6 +198,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.gamma = gamma;
     a.V = V;
     a.nchunk = L.nchunk;
+    a.nsub = L.nsub;
     a.t_temp = target.temperature;
     a.d_temp = draft.temperature;
     a.ban_sorted = ban_sorted;

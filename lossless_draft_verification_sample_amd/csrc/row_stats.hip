@@ -80,6 +80,7 @@ struct RowShared {
   double tiny_mass;
   float tiny_top;
   int32_t sel;
+  double T[64];        // exp_tab table
   double dscr[RS_THREADS / WAVE];
   float fscr[RS_THREADS / WAVE];
   uint32_t uscr[RS_THREADS / WAVE];
@@ -346,7 +347,7 @@ __device__ bool hb_epilogue(const SamplerDev s, RowShared& sh, RowStat& out) {
     float top_tiny = -INFINITY;
     for (uint32_t i = 0; i < tn; ++i) {
       const float v = bf16_to_f32(sh.tiny[i]);
-      tm += exp(((double)v - md) * invT);
+      tm += exp_tab(((double)v - md) * invT, sh.T);
       top_tiny = fmaxf(top_tiny, v);
     }
     sh.tiny_mass = tm;
@@ -356,8 +357,8 @@ __device__ bool hb_epilogue(const SamplerDev s, RowShared& sh, RowStat& out) {
   const double tiny_mass = sh.tiny_mass;
   auto rank_mass = [&](int r, uint32_t c) -> double {
     if (r == (int)HB_ZERO)
-      return (double)(c - tn) * exp(-md * invT) + tiny_mass;
-    return (double)c * exp(((double)hb_value_of_rank(r) - md) * invT);
+      return (double)(c - tn) * exp_tab(-md * invT, sh.T) + tiny_mass;
+    return (double)c * exp_tab(((double)hb_value_of_rank(r) - md) * invT, sh.T);
   };
 
   int rk = HB_RANKS - 1;
@@ -458,6 +459,7 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
 
   if (!generic) {
     for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = 0u;
+    exp_table_init(sh.T);
     if (tid == 0) {
       sh.zero_cnt = 0u;
       sh.nonfinite = 0u;

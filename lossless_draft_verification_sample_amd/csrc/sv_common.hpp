@@ -97,6 +97,31 @@ __device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t offset,
   return (double)((r >> 11) + 1) * 0x1.0p-53;
 }
 
+// exp(a) in fp64 for a <= about 0 (log-probabilities), to a few ulp.
+// Cody-Waite reduction a = k * (ln2 / 64) + r with |r| <= ln2 / 128 (ln2/64
+// split into a head and a tail so that r is exact to ~1e-17); e^r - 1 from its
+// degree-5 Taylor polynomial (remainder below 4e-17 relative); then
+// 2^(k/64) = 2^(k >> 6) * T[k & 63]. T holds 2^(j/64), j = 0..63, filled by
+// exp_table_init at workgroup start.
+__device__ __forceinline__ double exp_tab(double a, const double* T) {
+  a = fmax(a, -1000.0);                                   // exp(-1000) is 0 in fp64
+  const double kf = rint(a * 0x1.71547652b82fep+6);       // 64 / ln2
+  double r = fma(-kf, 0x1.62e42fefa39efp-7, a);           // head of ln2 / 64
+  r = fma(-kf, 0x1.abc9e3b39803fp-62, r);                 // tail of ln2 / 64
+  double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  q = fma(q, r, 1.0 / 6.0);
+  q = fma(q, r, 0.5);
+  q = fma(q, r, 1.0);
+  q *= r;                                                 // e^r - 1
+  const int k = (int)kf;
+  const double t = T[k & 63];
+  return ldexp(fma(t, q, t), k >> 6);
+}
+// Threads 0..63 fill T; the caller synchronises before use.
+__device__ __forceinline__ void exp_table_init(double* T) {
+  if (threadIdx.x < 64) T[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
+
 // ---------------------------------------------------------------- reductions
 
 template <typename T>

@@ -8,8 +8,11 @@
 
 namespace sv {
 
-// Vocabulary chunk handled by one workgroup of the final draw.
+// Final draw: one workgroup sums the weights of DRAW_CHUNK tokens, reported per
+// DRAW_SUB tokens; the selection then rescans a single sub-chunk.
 constexpr int DRAW_CHUNK = 8192;
+constexpr int DRAW_SUB = 2048;
+constexpr int SUB_PER_CHUNK = DRAW_CHUNK / DRAW_SUB;
 
 struct BanPrepArgs {
   const int32_t* banned;  // [B][n_banned]
@@ -56,14 +59,14 @@ struct DrawArgs {
   const void* draft;
   int bf16;
   int vec;                    // rows 16-byte aligned and V*size a multiple of 16
-  int gamma, V, nchunk;
+  int gamma, V, nchunk, nsub;
   float t_temp, d_temp;
   const int32_t* ban_sorted;
   const int32_t* ban_count;
   int ban_stride;
   const RowStat* stats;
   const ReqState* req;
-  ChunkSums* sums;            // [B][nchunk]
+  ChunkSums* sums;            // [B][nsub]
   int32_t* out_tokens;
   uint32_t* out_flags;
 };

@@ -221,25 +221,26 @@ __device__ __forceinline__ float group_val(const Group<Elem>& g, int j) {
 
 // p(x) and the draw weight of token x: max(0, p - q) at a rejection, p for the
 // bonus draw. fp64 throughout (exp of an fp64 argument), so the running sums
-// of the inverse CDF carry no fp32 error.
+// of the inverse CDF carry no fp32 error. T is the exp_tab table.
 __device__ __forceinline__ void pair_weight(const DrawRow& r, float zt, float zd, bool banned,
-                                            double& w, double& p) {
-  p = is_kept(zt, r.ts, banned) ? exp((double)zt * r.tinv - r.ts.lse) : 0.0;
+                                            const double* T, double& w, double& p) {
+  p = is_kept(zt, r.ts, banned) ? exp_tab((double)zt * r.tinv - r.ts.lse, T) : 0.0;
   if (r.drow) {
-    const double q = is_kept(zd, r.ds, banned) ? exp((double)zd * r.dinv - r.ds.lse) : 0.0;
+    const double q = is_kept(zd, r.ds, banned) ? exp_tab((double)zd * r.dinv - r.ds.lse, T) : 0.0;
     w = p > q ? p - q : 0.0;
   } else {
     w = p;
   }
 }
 
-// Marks the banned ids of [c0, c0 + DRAW_CHUNK) in an LDS bitmap.
-__device__ __forceinline__ void chunk_bans(uint32_t* bm, const int32_t* bans, int nb, int c0) {
-  for (int k = threadIdx.x; k < DRAW_CHUNK / 32; k += blockDim.x) bm[k] = 0u;
+// Marks the banned ids of [c0, c0 + len) in an LDS bitmap of len / 32 words.
+__device__ __forceinline__ void range_bans(uint32_t* bm, int len, const int32_t* bans, int nb,
+                                           int c0) {
+  for (int k = threadIdx.x; k < len / 32; k += blockDim.x) bm[k] = 0u;
   __syncthreads();
   if (nb > 0) {
     const int lo = lower_bound(bans, nb, c0);
-    const int hi = lower_bound(bans, nb, c0 + DRAW_CHUNK);
+    const int hi = lower_bound(bans, nb, c0 + len);
     for (int j = lo + (int)threadIdx.x; j < hi; j += blockDim.x) {
       const int o = bans[j] - c0;
       atomicOr(&bm[o >> 5], 1u << (o & 31));
@@ -252,10 +253,15 @@ __device__ __forceinline__ bool bm_test(const uint32_t* bm, int o) {
   return (bm[o >> 5] >> (o & 31)) & 1u;
 }
 
+// One workgroup per (request, DRAW_CHUNK tokens): weight sums per DRAW_SUB.
+// Group j of thread t covers tokens c0 + j*DRAW_SUB + 8t .. +8, so sub-chunk j
+// is exactly the j-th group of every thread and the loads are coalesced.
 template <typename Elem>
 __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a) {
+  static_assert(DRAW_SUB == DR_THREADS * GRP && GPT == SUB_PER_CHUNK, "draw tiling");
   __shared__ uint32_t bm[DRAW_CHUNK / 32];
-  __shared__ double scr[DR_THREADS / WAVE];
+  __shared__ double T[64];
+  __shared__ double scr[2 * SUB_PER_CHUNK][DR_THREADS / WAVE];
   const int tid = threadIdx.x;
   const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
   const ReqState rs = a.req[b];
@@ -268,35 +274,56 @@ __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a
   Group<Elem> tg[GPT], dg[GPT];
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
-    const int x0 = c0 + (j * DR_THREADS + tid) * GRP;
+    const int x0 = c0 + j * DRAW_SUB + tid * GRP;
     if (x0 < a.V) {
       load_group<Elem>(r.trow, x0, a.V, vec, tg[j]);
       if (r.drow) load_group<Elem>(r.drow, x0, a.V, vec, dg[j]);
     }
   }
-  chunk_bans(bm, bans, nb, c0);
-  double sw = 0.0, sp = 0.0;
+  exp_table_init(T);
+  range_bans(bm, DRAW_CHUNK, bans, nb, c0);
+  double sw[GPT], sp[GPT];
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
-    const int x0 = c0 + (j * DR_THREADS + tid) * GRP;
+    sw[j] = 0.0;
+    sp[j] = 0.0;
+    const int x0 = c0 + j * DRAW_SUB + tid * GRP;
     if (x0 < a.V) {
 #pragma unroll
       for (int e = 0; e < GRP; ++e) {
         double w, p;
         pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
-                    bm_test(bm, x0 - c0 + e), w, p);
-        sw += w;
-        sp += p;
+                    bm_test(bm, x0 - c0 + e), T, w, p);
+        sw[j] += w;
+        sp[j] += p;
       }
     }
   }
-  sw = block_sum<DR_THREADS>(sw, scr);
-  sp = block_sum<DR_THREADS>(sp, scr);
-  if (tid == 0) {
-    ChunkSums cs;
-    cs.w = sw;
-    cs.p = sp;
-    a.sums[(int64_t)b * a.nchunk + c] = cs;
+  // per-sub-chunk block sums in a fixed order
+  const int wv = tid / WAVE, lane = tid & (WAVE - 1);
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const double a0 = wave_sum(sw[j]), a1 = wave_sum(sp[j]);
+    if (lane == 0) {
+      scr[2 * j][wv] = a0;
+      scr[2 * j + 1][wv] = a1;
+    }
+  }
+  __syncthreads();
+  if (tid < GPT) {
+    const int sub = c * SUB_PER_CHUNK + tid;
+    if (sub < a.nsub) {
+      double w = 0.0, p = 0.0;
+#pragma unroll
+      for (int k = 0; k < DR_THREADS / WAVE; ++k) {
+        w += scr[2 * tid][k];
+        p += scr[2 * tid + 1][k];
+      }
+      ChunkSums cs;
+      cs.w = w;
+      cs.p = p;
+      a.sums[(int64_t)b * a.nsub + sub] = cs;
+    }
   }
 }
 
@@ -308,22 +335,26 @@ int launch_residual_partial(const DrawArgs& a, int B, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// One workgroup per request: locate the sub-chunk holding u * S from the
+// partial sums, then rescan those DRAW_SUB tokens (8 per thread, in id order).
 template <typename Elem>
 __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a) {
-  __shared__ uint32_t bm[DRAW_CHUNK / 32];
+  __shared__ uint32_t bm[DRAW_SUB / 32];
+  __shared__ double T[64];
   __shared__ double scr[DR_THREADS / WAVE];
-  __shared__ int32_t sel_chunk, sel_x;
+  __shared__ int32_t sel_sub, sel_x;
   __shared__ double sel_before;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int g = a.gamma, G1 = g + 1;
   const ReqState rs = a.req[b];
   const int n = rs.n;
   uint32_t flags = rs.flags;
-  const ChunkSums* cs = a.sums + (int64_t)b * a.nchunk;
+  const ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
+  exp_table_init(T);
 
   // totals; fall back to p when the residual has no mass
   double tw = 0.0, tp = 0.0;
-  for (int c = tid; c < a.nchunk; c += DR_THREADS) {
+  for (int c = tid; c < a.nsub; c += DR_THREADS) {
     tw += cs[c].w;
     tp += cs[c].p;
   }
@@ -341,27 +372,27 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
     flags |= FLAG_EMPTY;
   } else {
     const double t = rs.u_final * S;
-    // chunk holding t: per-thread contiguous runs of chunks, a block scan, and
-    // the first thread whose run reaches t searches its run
-    const int per = (a.nchunk + DR_THREADS - 1) / DR_THREADS;
+    // sub-chunk holding t: per-thread contiguous runs, a block scan, and the
+    // first thread whose run reaches t searches its run
+    const int per = (a.nsub + DR_THREADS - 1) / DR_THREADS;
     const int k0 = tid * per;
     double loc = 0.0;
-    for (int c = k0; c < k0 + per && c < a.nchunk; ++c) loc += use_p ? cs[c].p : cs[c].w;
+    for (int c = k0; c < k0 + per && c < a.nsub; ++c) loc += use_p ? cs[c].p : cs[c].w;
     double tot;
     const double before = block_excl_scan<DR_THREADS>(loc, scr, &tot);
     const int cand = block_min<DR_THREADS>((loc > 0.0 && before + loc >= t) ? tid : DR_THREADS,
                                            (int*)scr);
     if (tid == 0) {
-      sel_chunk = -1;
+      sel_sub = -1;
       sel_before = 0.0;
     }
     __syncthreads();
     if (tid == cand) {
       double run = before;
-      for (int c = k0; c < k0 + per && c < a.nchunk; ++c) {
+      for (int c = k0; c < k0 + per && c < a.nsub; ++c) {
         const double v = use_p ? cs[c].p : cs[c].w;
         if (v > 0.0) {
-          sel_chunk = c;            // the last chunk with weight unless one reaches t
+          sel_sub = c;              // the last sub-chunk with weight unless one reaches t
           sel_before = run;
           if (run + v >= t) break;
         }
@@ -369,80 +400,63 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
       }
     }
     __syncthreads();
-    if (sel_chunk < 0 && tid == 0) {
-      // t above every prefix through rounding: the last chunk with weight
+    if (sel_sub < 0 && tid == 0) {
+      // t above every prefix through rounding: the last sub-chunk with weight
       double run = 0.0;
-      for (int c = 0; c < a.nchunk; ++c) {
+      for (int c = 0; c < a.nsub; ++c) {
         const double v = use_p ? cs[c].p : cs[c].w;
         if (v > 0.0) {
-          sel_chunk = c;
+          sel_sub = c;
           sel_before = run;
         }
         run += v;
       }
     }
     __syncthreads();
-    const int c = sel_chunk;
+    const int s0 = sel_sub * DRAW_SUB;
     const double tl = t - sel_before;
     const DrawRow r = draw_row(a, b, n);
     const int nb = a.ban_count ? a.ban_count[b] : 0;
     const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
-    const int c0 = c * DRAW_CHUNK;
-    // each thread owns GPT consecutive groups: tokens [x0, x0 + GPT*GRP) in id order
-    const int x0 = c0 + tid * GPT * GRP;
-    Group<Elem> tg[GPT], dg[GPT];
-#pragma unroll
-    for (int j = 0; j < GPT; ++j) {
-      const int xg = x0 + j * GRP;
-      if (xg < a.V) {
-        load_group<Elem>(r.trow, xg, a.V, a.vec, tg[j]);
-        if (r.drow) load_group<Elem>(r.drow, xg, a.V, a.vec, dg[j]);
-      }
+    const int x0 = s0 + tid * GRP;
+    Group<Elem> tg, dg;
+    if (x0 < a.V) {
+      load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
+      if (r.drow) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
     }
-    chunk_bans(bm, bans, nb, c0);
+    range_bans(bm, DRAW_SUB, bans, nb, s0);
+    double v[GRP];
     double lsum = 0.0;
 #pragma unroll
-    for (int j = 0; j < GPT; ++j) {
-      const int xg = x0 + j * GRP;
-      if (xg < a.V) {
-#pragma unroll
-        for (int e = 0; e < GRP; ++e) {
-          double w, p;
-          pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
-                      bm_test(bm, xg - c0 + e), w, p);
-          lsum += use_p ? p : w;
-        }
+    for (int e = 0; e < GRP; ++e) {
+      v[e] = 0.0;
+      if (x0 + e < a.V) {
+        double w, p;
+        pair_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f,
+                    bm_test(bm, x0 - s0 + e), T, w, p);
+        v[e] = use_p ? p : w;
       }
+      lsum += v[e];
     }
     double ctot;
     const double cb = block_excl_scan<DR_THREADS>(lsum, scr, &ctot);
     const int xc = block_min<DR_THREADS>((lsum > 0.0 && cb + lsum >= tl) ? tid : DR_THREADS,
                                          (int*)scr);
     const int xl = block_max<DR_THREADS>(lsum > 0.0 ? tid : -1, (int*)scr);
-    const int who = xc < DR_THREADS ? xc : xl;   // a chunk chosen here has weight
+    const int who = xc < DR_THREADS ? xc : xl;   // a sub-chunk chosen here has weight
     if (tid == 0) sel_x = -1;
     __syncthreads();
     if (tid == who) {
       double run = cb;
-      bool done = false;
-#pragma unroll
-      for (int j = 0; j < GPT; ++j) {
-        const int xg = x0 + j * GRP;
-#pragma unroll
-        for (int e = 0; e < GRP; ++e) {
-          if (!done && xg + e < a.V) {
-            double w, p;
-            pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
-                        bm_test(bm, xg - c0 + e), w, p);
-            const double v = use_p ? p : w;
-            if (v > 0.0) {
-              sel_x = xg + e;       // the last token with weight unless one reaches tl
-              if (run + v >= tl) done = true;
-            }
-            run += v;
-          }
+      int pick = -1;
+      for (int e = 0; e < GRP; ++e) {
+        if (v[e] > 0.0) {
+          pick = x0 + e;            // the last token with weight unless one reaches tl
+          if (run + v[e] >= tl) break;
         }
+        run += v[e];
       }
+      sel_x = pick;
     }
     __syncthreads();
     token = sel_x;
