@@ -42,17 +42,24 @@
 
 namespace sv {
 
-constexpr int RS_THREADS = 512;
-constexpr int RS_UNROLL = 4;
+#ifndef SV_RS_THREADS
+#define SV_RS_THREADS 512
+#endif
+#ifndef SV_RS_UNROLL
+#define SV_RS_UNROLL 4
+#endif
+// One workgroup per row, four per CU; each thread keeps four 16-byte loads in
+// flight.
+constexpr int RS_THREADS = SV_RS_THREADS;
+constexpr int RS_UNROLL = SV_RS_UNROLL;
 
 // Count-histogram window for bf16 logits.
 constexpr uint32_t HB_BASE = 104u << 7;       // bf16 |bits| of 2^-23
 constexpr uint32_t HB_WIN = 32u * 128u;       // 32 binades x 128 mantissas per sign
-constexpr uint32_t HB_NEG = HB_WIN + 1u;      // first bin of the negative half
-constexpr uint32_t HB_ZERO = HB_WIN;          // zero bin (a dump bin during the pass)
-constexpr uint32_t HB_BINS = 2u * HB_WIN + 2u;
+constexpr uint32_t HB_NEG = HB_WIN + 4u;      // first bin of the negative half (16-byte aligned)
+constexpr uint32_t HB_ZERO = HB_WIN;          // rank of zero; bin HB_WIN is a dump bin
+constexpr uint32_t HB_BINS = HB_NEG + HB_WIN + 1u;
 constexpr int HB_RANKS = 2 * HB_WIN + 1;      // value-ordered ranks: +window, zero, -window
-constexpr int HB_RPT = (HB_RANKS + RS_THREADS - 1) / RS_THREADS;
 constexpr uint32_t TINY_MAX = 64;             // tiny values tracked exactly per row
 constexpr int BM_MAX_BITS = (int)HB_BINS * 32; // largest V whose ban bitmap fits the LDS
 
@@ -60,18 +67,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// rank 0 is the largest value; ranks ascend as values descend.
-__device__ __forceinline__ uint32_t hb_bin_of_rank(int r) {
-  return r < (int)HB_WIN ? (HB_WIN - 1u - (uint32_t)r) : (uint32_t)r;
-}
+// Ranks order the counted values from the largest down: ranks 0..4095 are the
+// positive window (bin 4095 - r), rank 4096 is zero, ranks 4097..8192 the
+// negative window (bin HB_NEG + r - 4097).
 __device__ __forceinline__ float hb_value_of_rank(int r) {
   if (r < (int)HB_WIN) return bf16_to_f32(HB_WIN - 1u - (uint32_t)r + HB_BASE);
   if (r == (int)HB_ZERO) return 0.0f;
-  return bf16_to_f32(0x8000u | ((uint32_t)r - HB_NEG + HB_BASE));
+  return bf16_to_f32(0x8000u | ((uint32_t)r - (HB_WIN + 1u) + HB_BASE));
 }
 
+struct alignas(16) WaveSlot {
+  uint32_t n;     // admissible count of the wave  | exchange 2/3: selected rank
+  int32_t top;    // top rank of the wave           | (unused)
+  double z;       // mass of the wave (rel. to its top value) | prefix mass
+};
+
 struct RowShared {
-  uint32_t hist[HB_BINS];
+  alignas(16) uint32_t hist[HB_BINS];
   uint32_t zero_cnt;   // exact zeros and tiny values
   uint32_t nonfinite;
   uint32_t special;
@@ -79,8 +91,7 @@ struct RowShared {
   uint16_t tiny[TINY_MAX];
   double tiny_mass;
   float tiny_top;
-  int32_t sel;
-  double T[64];        // exp_tab table
+  WaveSlot x1[RS_THREADS / WAVE], x2[RS_THREADS / WAVE], x3[RS_THREADS / WAVE];
   double dscr[RS_THREADS / WAVE];
   float fscr[RS_THREADS / WAVE];
   uint32_t uscr[RS_THREADS / WAVE];
@@ -202,7 +213,7 @@ __device__ __forceinline__ float gval(uint32_t k) {
 }
 
 template <typename Elem>
-__device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const GenericCtx& g,
+__device__ __forceinline__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const GenericCtx& g,
                             RowShared& sh, RowStat& out) {
   const double c2 = 1.4426950408889634 / (double)s.temperature;  // log2(e) / T
   // pass 1: max, min, count and the exp-sum against per-lane integer references
@@ -296,134 +307,260 @@ __device__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const G
 }
 
 // ------------------------------------------------------------------ histogram epilogue
+//
+// While one workgroup derives its statistics, the other workgroups of the CU
+// keep the LDS saturated with histogram atomics, so every LDS round trip of the
+// epilogue waits in that queue. The epilogue is therefore built around few
+// dependent LDS round trips: each thread loads its HB_TPR counts in one batch
+// and keeps them in registers, wave-level scans use DPP lane moves, and the
+// waves meet in one exchange (two to four with truncation).
+//
+// Thread t < NT/2 owns ranks HB_TPR*t .. (positive values, descending), thread
+// NT/2 + t owns ranks 4097 + HB_TPR*t .. (negative values), and thread NT/2
+// also owns the zero rank, which precedes its ranks. Ranks are thus contiguous
+// in thread order. A thread's ranks lie in one binade, where bf16 values are
+// equally spaced by delta = 2^(e - 134): the mass per unit count
+// exp((v - ref) / T) of consecutive ranks differs by the factor exp(-delta / T),
+// so each thread needs two exps. Masses are taken relative to the largest value
+// of the thread's wave and rescaled exactly once the row maximum is known.
 
-// Exact statistics from the counts; false when the row must go to the generic
-// path (a truncation cut among the tiny values). Called by the whole block.
-__device__ bool hb_epilogue(const SamplerDev s, RowShared& sh, RowStat& out) {
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    sh.hist[HB_ZERO] = sh.zero_cnt;
-    // tiny values in ascending order: a fixed summation order below
-    const int n = (int)min(sh.tiny_n, TINY_MAX);
-    for (int i = 1; i < n; ++i) {
-      const uint16_t v = sh.tiny[i];
-      const float fv = bf16_to_f32(v);
-      int j = i - 1;
-      while (j >= 0 && bf16_to_f32(sh.tiny[j]) > fv) {
-        sh.tiny[j + 1] = sh.tiny[j];
-        --j;
-      }
-      sh.tiny[j + 1] = v;
+constexpr int HB_TPR = 2 * (int)HB_WIN / RS_THREADS;   // ranks per thread
+static_assert(HB_TPR % 4 == 0 && 128 % HB_TPR == 0, "epilogue rank tiling");
+
+// A slot read from LDS is the same for every lane: keep it in scalar registers.
+__device__ __forceinline__ WaveSlot slot_uniform(const WaveSlot& src) {
+  const u32x4 v = *(const u32x4*)&src;
+  WaveSlot r;
+  r.n = (uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]);
+  r.top = __builtin_amdgcn_readfirstlane((int)v[1]);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)v[2]);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)v[3]);
+  r.z = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  return r;
+}
+
+// The counts of ranks r0 .. r0 + HB_TPR - 1 in rank order.
+__device__ __forceinline__ void hb_load_counts(const uint32_t* hist, int r0, bool pos,
+                                               uint32_t (&c)[HB_TPR]) {
+#pragma unroll
+  for (int i = 0; i < HB_TPR / 4; ++i) {
+    if (pos) {
+      const u32x4 v = *(const u32x4*)(hist + (HB_WIN - 4) - r0 - 4 * i);
+      c[4 * i] = v[3];
+      c[4 * i + 1] = v[2];
+      c[4 * i + 2] = v[1];
+      c[4 * i + 3] = v[0];
+    } else {
+      const u32x4 v = *(const u32x4*)(hist + HB_NEG + (r0 - (int)HB_WIN - 1) + 4 * i);
+      c[4 * i] = v[0];
+      c[4 * i + 1] = v[1];
+      c[4 * i + 2] = v[2];
+      c[4 * i + 3] = v[3];
     }
+  }
+}
+
+__device__ __forceinline__ int hb_thread_rank0(int t) {
+  return t < RS_THREADS / 2 ? HB_TPR * t : (int)HB_WIN + 1 + HB_TPR * (t - RS_THREADS / 2);
+}
+
+// Exact statistics from the counts, computed by the whole block; false when the
+// row must go to the generic path (a truncation cut among the tiny values).
+__device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, RowStat& out) {
+  constexpr int NW = RS_THREADS / WAVE;
+  const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
+  const int r0 = hb_thread_rank0(tid);
+  const bool pos = tid < RS_THREADS / 2;
+  const bool zown = tid == RS_THREADS / 2;
+
+  // counts of the thread's ranks, in rank order, in one batch of LDS loads
+  uint32_t c[HB_TPR];
+  hb_load_counts(sh.hist, r0, pos, c);
+  const uint32_t zc = zown ? sh.zero_cnt : 0u;
+  const uint32_t tn = min(sh.tiny_n, TINY_MAX);
+  uint32_t cl = zc, nz = 0u;
+#pragma unroll
+  for (int j = 0; j < HB_TPR; ++j) {
+    cl += c[j];
+    nz |= (c[j] != 0u ? 1u : 0u) << j;
+  }
+  const int top = zc ? (int)HB_ZERO : (nz ? r0 + __ffs(nz) - 1 : HB_RANKS);
+  const uint32_t cnt_incl = wave_scan_dpp(cl, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+  const int top_w = lane63(wave_scan_dpp(top, (int32_t)HB_RANKS,
+                                         [](int32_t x, int32_t y) { return x < y ? x : y; }));
+  const double invT = 1.0 / (double)s.temperature;
+  const double mw = top_w < HB_RANKS ? (double)hb_value_of_rank(top_w) : 0.0;
+  // masses relative to the wave's top value, anchored at the thread's first
+  // nonzero rank (its value is <= the wave's top, so no exp overflows)
+  const uint32_t bits0 = pos ? (HB_WIN - 1u - (uint32_t)r0 + HB_BASE)
+                             : ((uint32_t)r0 - (HB_WIN + 1u) + HB_BASE);
+  const double ratio = exp_neg(-ldexp(1.0, (int)(bits0 >> 7) - 134) * invT);
+  const int jtop = nz ? __ffs(nz) - 1 : HB_TPR;
+  const double e0 = nz ? exp_neg(((double)hb_value_of_rank(r0 + jtop) - mw) * invT) : 0.0;
+  double zmass = 0.0;                 // zero rank and the tiny values listed with it
+  if (zc) {
+    zmass = (double)(zc - tn) * exp_neg(-mw * invT);
+    for (uint32_t k = 0; k < tn; ++k)   // sorted beforehand: a fixed order
+      zmass += exp_neg(((double)bf16_to_f32(sh.tiny[k]) - mw) * invT);
+  }
+  double ml = zmass;
+  {
+    double e = e0;
+#pragma unroll
+    for (int j = 0; j < HB_TPR; ++j) {
+      if (j > jtop) e *= ratio;
+      if (c[j]) ml += (double)c[j] * e;
+    }
+  }
+  const double mass_incl = wave_scan_dpp(ml, 0.0, [](double x, double y) { return x + y; });
+
+  // exchange 1: per-wave count, top rank and mass
+  if (lane == WAVE - 1) {
+    WaveSlot ws;
+    ws.n = cnt_incl;
+    ws.top = top_w;
+    ws.z = mass_incl;
+    sh.x1[w] = ws;
   }
   __syncthreads();
-  const uint32_t tn = min(sh.tiny_n, TINY_MAX);
-
-  const int r0 = tid * HB_RPT;
-  uint32_t cloc = 0u;
-  int top = HB_RANKS;
+  WaveSlot x[NW];
 #pragma unroll
-  for (int j = 0; j < HB_RPT; ++j) {
-    const int r = r0 + j;
-    if (r < HB_RANKS) {
-      const uint32_t c = sh.hist[hb_bin_of_rank(r)];
-      cloc += c;
-      if (c && top == HB_RANKS) top = r;
-    }
+  for (int k = 0; k < NW; ++k) x[k] = slot_uniform(sh.x1[k]);
+  uint32_t N = 0u;
+  int rtop = HB_RANKS;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    N += x[k].n;
+    rtop = min(rtop, x[k].top);
   }
-  const uint32_t N = block_sum<RS_THREADS>(cloc, sh.uscr);
-  const int rtop = block_min<RS_THREADS>(top, sh.iscr);
   if (N == 0u) {
     out.flags |= FLAG_EMPTY;
     return true;
   }
-  // reference logit md: the largest counted value (0 when the top rank is the
-  // zero bin, whose tiny members are weighed exactly below)
   const float m = hb_value_of_rank(rtop);
   const double md = (double)m;
-  const double invT = 1.0 / (double)s.temperature;
-  if (tid == 0) {
-    double tm = 0.0;
-    float top_tiny = -INFINITY;
-    for (uint32_t i = 0; i < tn; ++i) {
-      const float v = bf16_to_f32(sh.tiny[i]);
-      tm += exp_tab(((double)v - md) * invT, sh.T);
-      top_tiny = fmaxf(top_tiny, v);
+  // rescale every wave to the row maximum; prefixes before this thread
+  double Z0 = 0.0, mass_before = 0.0, scale_w = 0.0;
+  uint32_t cnt_before = cnt_incl - cl;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const double sc = x[k].top < HB_RANKS
+                          ? exp_neg(((double)hb_value_of_rank(x[k].top) - md) * invT) : 0.0;
+    const double zk = x[k].z * sc;
+    Z0 += zk;
+    if (k < w) {
+      mass_before += zk;
+      cnt_before += x[k].n;
     }
-    sh.tiny_mass = tm;
-    sh.tiny_top = top_tiny;
+    if (k == w) scale_w = sc;
   }
-  __syncthreads();
-  const double tiny_mass = sh.tiny_mass;
-  auto rank_mass = [&](int r, uint32_t c) -> double {
-    if (r == (int)HB_ZERO)
-      return (double)(c - tn) * exp_tab(-md * invT, sh.T) + tiny_mass;
-    return (double)c * exp_tab(((double)hb_value_of_rank(r) - md) * invT, sh.T);
+  mass_before += (mass_incl - ml) * scale_w;
+
+  // visit the thread's nonzero ranks <= rlim in order: fn(rank, count, mass rel.
+  // to md). Only threads at a truncation cut walk; they reload their counts.
+  auto walk = [&](int rlim, auto&& fn) {
+    if (zc && rlim >= (int)HB_ZERO) fn((int)HB_ZERO, zc, zmass * scale_w);
+    uint32_t cc[HB_TPR];
+    hb_load_counts(sh.hist, r0, pos, cc);
+    const int jlim = rlim - r0;
+    double e = e0;
+#pragma unroll
+    for (int j = 0; j < HB_TPR; ++j) {
+      if (j > jtop) e *= ratio;
+      if (j <= jlim && cc[j]) fn(r0 + j, cc[j], (double)cc[j] * e * scale_w);
+    }
   };
 
   int rk = HB_RANKS - 1;
+  double Z = Z0;
   bool trunc = false;
   if (s.top_k > 0 && (uint32_t)s.top_k < N) {
-    uint32_t tot;
-    const uint32_t before = block_excl_scan<RS_THREADS>(cloc, sh.uscr, &tot);
-    const uint32_t k = (uint32_t)s.top_k;
-    if (before < k && before + cloc >= k) {
-      uint32_t cum = before;
-#pragma unroll
-      for (int j = 0; j < HB_RPT; ++j) {
-        const int r = r0 + j;
-        if (r < HB_RANKS) {
-          cum += sh.hist[hb_bin_of_rank(r)];
-          if (cum >= k) {
-            sh.sel = r;
-            break;
-          }
+    // exchange 2: the thread holding the k-th largest count reports its rank
+    // and the mass up to it (integer prefixes: exactly one such thread)
+    const uint32_t kk = (uint32_t)s.top_k;
+    const bool mine = cnt_before < kk && cnt_before + cl >= kk;
+    int rsel = -1;
+    double zsel = 0.0;
+    if (mine) {
+      uint32_t cum = cnt_before;
+      double zz = mass_before;
+      walk(HB_RANKS - 1, [&](int r, uint32_t cc, double mass) {
+        if (cum < kk) {
+          rsel = r;
+          zz += mass;
         }
-      }
+        cum += cc;
+      });
+      zsel = zz;
+    }
+    const uint64_t bal = __ballot(mine);
+    if (lane == (bal ? __ffsll((unsigned long long)bal) - 1 : 0)) {
+      WaveSlot ws;
+      ws.n = (uint32_t)rsel;
+      ws.top = 0;
+      ws.z = zsel;
+      sh.x2[w] = ws;
     }
     __syncthreads();
-    rk = sh.sel;
+#pragma unroll
+    for (int k = NW - 1; k >= 0; --k) {
+      const WaveSlot ws = slot_uniform(sh.x2[k]);
+      if ((int32_t)ws.n >= 0) {
+        rk = (int)ws.n;
+        Z = ws.z;
+      }
+    }
     trunc = true;
     if (rk == (int)HB_ZERO && tn > 0u) return false;
   }
-  // masses of the values kept by top-k
-  double mloc = 0.0;
-#pragma unroll
-  for (int j = 0; j < HB_RPT; ++j) {
-    const int r = r0 + j;
-    if (r <= rk) {
-      const uint32_t c = sh.hist[hb_bin_of_rank(r)];
-      if (c) mloc += rank_mass(r, c);
-    }
-  }
-  double Z = block_sum<RS_THREADS>(mloc, sh.dscr);
   int rp_last = rk;
   if (s.top_p < 1.0f) {
-    double tot;
-    const double before = block_excl_scan<RS_THREADS>(mloc, sh.dscr, &tot);
+    // exchange 3: keep rank r while the mass strictly above it is < top_p * Z;
+    // the first thread whose ranks reach the target reports the last kept rank
+    // and the kept mass
     const double target = (double)s.top_p * Z;
-    double above = before, zloc = 0.0;
     int last = -1;
-    for (int j = 0; j < HB_RPT; ++j) {
-      const int r = r0 + j;
-      if (r > rk || !(above < target)) break;
-      const uint32_t c = sh.hist[hb_bin_of_rank(r)];
-      if (c) {
-        const double w = rank_mass(r, c);
-        last = r;
-        zloc += w;
-        above += w;
+    double above = mass_before;
+    const bool cand = mass_before < target && r0 <= rk + (zown ? 1 : 0) &&
+                      (mass_before + ml * scale_w >= target || r0 + HB_TPR - 1 > rk);
+    if (cand) {
+      walk(rk, [&](int r, uint32_t, double mass) {
+        if (above < target) {
+          last = r;
+          above += mass;
+        }
+      });
+    }
+    const bool crosses = cand && last >= 0 && above >= target;
+    const uint64_t bal = __ballot(crosses);
+    if (lane == (bal ? __ffsll((unsigned long long)bal) - 1 : 0)) {
+      WaveSlot ws;
+      ws.n = crosses ? (uint32_t)last : 0xFFFFFFFFu;
+      ws.top = 0;
+      ws.z = above;
+      sh.x3[w] = ws;
+    }
+    __syncthreads();
+    // the first wave with a crossing; none (rounding at the very end): keep rk
+#pragma unroll
+    for (int k = NW - 1; k >= 0; --k) {
+      const WaveSlot ws = slot_uniform(sh.x3[k]);
+      if ((int32_t)ws.n >= 0) {
+        rp_last = (int)ws.n;
+        Z = ws.z;
       }
     }
-    rp_last = block_max<RS_THREADS>(last, sh.iscr);
-    Z = block_sum<RS_THREADS>(zloc, sh.dscr);
     trunc = true;
     if (rp_last == (int)HB_ZERO && tn > 0u) return false;
   }
   // the largest kept logit (a tiny positive can top the zero bin)
-  out.m = (rtop == (int)HB_ZERO && tn > 0u)
-              ? ((sh.zero_cnt > tn) ? fmaxf(0.0f, sh.tiny_top) : sh.tiny_top)
-              : m;
+  if (rtop == (int)HB_ZERO && tn > 0u) {
+    float tt = -INFINITY;
+    for (uint32_t k = 0; k < tn; ++k) tt = fmaxf(tt, bf16_to_f32(sh.tiny[k]));
+    out.m = sh.zero_cnt > tn ? fmaxf(0.0f, tt) : tt;
+  } else {
+    out.m = m;
+  }
   out.tau = trunc ? hb_value_of_rank(rp_last) : -INFINITY;
   out.lse = md * invT + log(Z);
   return true;
@@ -431,8 +568,10 @@ __device__ bool hb_epilogue(const SamplerDev s, RowShared& sh, RowStat& out) {
 
 // ------------------------------------------------------------------ the kernel
 
+// Two 1024-thread workgroups per CU need 8 waves per SIMD, i.e. <= 64 VGPRs.
 template <typename Elem>
-__global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
+__global__ __launch_bounds__(RS_THREADS) __attribute__((amdgpu_waves_per_eu(2048 / RS_THREADS * RS_THREADS / 256)))
+void row_stats_kernel(RowStatsArgs a) {
   __shared__ RowShared sh;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -459,7 +598,6 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
 
   if (!generic) {
     for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = 0u;
-    exp_table_init(sh.T);
     if (tid == 0) {
       sh.zero_cnt = 0u;
       sh.nonfinite = 0u;
@@ -469,6 +607,8 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
     __syncthreads();
 
     const uint16_t* rp = (const uint16_t*)rowp;
+    // the banned logits are gathered now and subtracted after the stream
+    const uint32_t ban_bits = tid < nb ? (uint32_t)rp[bans[tid]] : 0xFF80u;
     const uintptr_t addr = (uintptr_t)rp;
     int head = (int)(((16u - (addr & 15u)) & 15u) >> 1);
     if (head > V) head = V;
@@ -507,7 +647,7 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
 
     // remove the banned ids (sorted, unique, all in [0, V))
     for (int j = tid; j < nb; j += RS_THREADS) {
-      const uint32_t bits = rp[bans[j]];
+      const uint32_t bits = j == tid ? ban_bits : (uint32_t)rp[bans[j]];
       const uint32_t ae = bits & 0x7FFFu;
       const uint32_t t = ae - HB_BASE;
       if (t < HB_WIN)
@@ -516,6 +656,20 @@ __global__ __launch_bounds__(RS_THREADS) void row_stats_kernel(RowStatsArgs a) {
         atomicSub(&sh.zero_cnt, 1u);
       else if (ae < HB_BASE)
         sh.special = 1u;   // a banned tiny value: the generic path sorts it out
+    }
+    if (tid == 0) {
+      // tiny values in ascending order: the epilogue sums them in this order
+      const int n = (int)min(sh.tiny_n, TINY_MAX);
+      for (int k = 1; k < n; ++k) {
+        const uint16_t v = sh.tiny[k];
+        const float fv = bf16_to_f32(v);
+        int j = k - 1;
+        while (j >= 0 && bf16_to_f32(sh.tiny[j]) > fv) {
+          sh.tiny[j + 1] = sh.tiny[j];
+          --j;
+        }
+        sh.tiny[j + 1] = v;
+      }
     }
     __syncthreads();
     if (sh.nonfinite) out.flags |= FLAG_NONFINITE;

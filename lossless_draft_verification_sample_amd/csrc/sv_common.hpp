@@ -97,32 +97,75 @@ __device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t offset,
   return (double)((r >> 11) + 1) * 0x1.0p-53;
 }
 
-// exp(a) in fp64 for a <= about 0 (log-probabilities), to a few ulp.
-// Cody-Waite reduction a = k * (ln2 / 64) + r with |r| <= ln2 / 128 (ln2/64
-// split into a head and a tail so that r is exact to ~1e-17); e^r - 1 from its
-// degree-5 Taylor polynomial (remainder below 4e-17 relative); then
-// 2^(k/64) = 2^(k >> 6) * T[k & 63]. T holds 2^(j/64), j = 0..63, filled by
-// exp_table_init at workgroup start.
-__device__ __forceinline__ double exp_tab(double a, const double* T) {
+// exp(a) in fp64 for a <= about 0 (log-probabilities), to a few ulp, with no
+// table and no memory access. Cody-Waite reduction a = k * (ln2 / 2) + r with
+// |r| <= ln2 / 4 (ln2/2 split into a head and a tail); e^r - 1 from its
+// degree-10 Taylor polynomial (remainder ~1e-16 relative); then
+// e^a = 2^(k >> 1) * (k odd ? sqrt 2 : 1) * e^r.
+__device__ __forceinline__ double exp_neg(double a) {
   a = fmax(a, -1000.0);                                   // exp(-1000) is 0 in fp64
-  const double kf = rint(a * 0x1.71547652b82fep+6);       // 64 / ln2
-  double r = fma(-kf, 0x1.62e42fefa39efp-7, a);           // head of ln2 / 64
-  r = fma(-kf, 0x1.abc9e3b39803fp-62, r);                 // tail of ln2 / 64
-  double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  const double kf = rint(a * 0x1.71547652b82fep+1);       // 2 / ln2
+  double r = fma(-kf, 0x1.62e42fefa39efp-2, a);           // head of ln2 / 2
+  r = fma(-kf, 0x1.abc9e3b39803fp-57, r);                 // tail of ln2 / 2
+  double q = fma(r, 1.0 / 3628800.0, 1.0 / 362880.0);
+  q = fma(q, r, 1.0 / 40320.0);
+  q = fma(q, r, 1.0 / 5040.0);
+  q = fma(q, r, 1.0 / 720.0);
+  q = fma(q, r, 1.0 / 120.0);
+  q = fma(q, r, 1.0 / 24.0);
   q = fma(q, r, 1.0 / 6.0);
   q = fma(q, r, 0.5);
   q = fma(q, r, 1.0);
   q *= r;                                                 // e^r - 1
   const int k = (int)kf;
-  const double t = T[k & 63];
-  return ldexp(fma(t, q, t), k >> 6);
-}
-// Threads 0..63 fill T; the caller synchronises before use.
-__device__ __forceinline__ void exp_table_init(double* T) {
-  if (threadIdx.x < 64) T[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+  const double t = (k & 1) ? 0x1.6a09e667f3bcdp+0 : 1.0;  // sqrt 2
+  return ldexp(fma(t, q, t), k >> 1);
 }
 
 // ---------------------------------------------------------------- reductions
+
+// Wave64 scans through DPP lane moves, which stay in the VALU and never queue
+// behind LDS traffic. Inclusive scan: Hillis-Steele inside each row of 16 lanes
+// (row_shr 1, 2, 4, 8), then lane 15 of rows 0 and 2 is broadcast into rows 1
+// and 3 (row_bcast:15, row mask 0xA) and lane 31 into rows 2 and 3
+// (row_bcast:31, row mask 0xC). Lanes whose source is outside the row, or whose
+// row is masked, receive `ident`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v, uint32_t ident) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int32_t dpp_move(int32_t v, int32_t ident) {
+  return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_move(double v, double ident) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v), o = (uint64_t)__double_as_longlong(ident);
+  const uint32_t lo = dpp_move<CTRL, ROWMASK>((uint32_t)b, (uint32_t)o);
+  const uint32_t hi = dpp_move<CTRL, ROWMASK>((uint32_t)(b >> 32), (uint32_t)(o >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan_dpp(T x, T ident, Op op) {
+  x = op(x, dpp_move<0x111, 0xF>(x, ident));
+  x = op(x, dpp_move<0x112, 0xF>(x, ident));
+  x = op(x, dpp_move<0x114, 0xF>(x, ident));
+  x = op(x, dpp_move<0x118, 0xF>(x, ident));
+  x = op(x, dpp_move<0x142, 0xA>(x, ident));
+  x = op(x, dpp_move<0x143, 0xC>(x, ident));
+  return x;
+}
+// Value of lane 63 (the wave total after an inclusive scan).
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ int32_t lane63(int32_t v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ double lane63(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {

@@ -221,12 +221,12 @@ __device__ __forceinline__ float group_val(const Group<Elem>& g, int j) {
 
 // p(x) and the draw weight of token x: max(0, p - q) at a rejection, p for the
 // bonus draw. fp64 throughout (exp of an fp64 argument), so the running sums
-// of the inverse CDF carry no fp32 error. T is the exp_tab table.
+// of the inverse CDF carry no fp32 error.
 __device__ __forceinline__ void pair_weight(const DrawRow& r, float zt, float zd, bool banned,
-                                            const double* T, double& w, double& p) {
-  p = is_kept(zt, r.ts, banned) ? exp_tab((double)zt * r.tinv - r.ts.lse, T) : 0.0;
+                                            double& w, double& p) {
+  p = is_kept(zt, r.ts, banned) ? exp_neg((double)zt * r.tinv - r.ts.lse) : 0.0;
   if (r.drow) {
-    const double q = is_kept(zd, r.ds, banned) ? exp_tab((double)zd * r.dinv - r.ds.lse, T) : 0.0;
+    const double q = is_kept(zd, r.ds, banned) ? exp_neg((double)zd * r.dinv - r.ds.lse) : 0.0;
     w = p > q ? p - q : 0.0;
   } else {
     w = p;
@@ -260,7 +260,6 @@ template <typename Elem>
 __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a) {
   static_assert(DRAW_SUB == DR_THREADS * GRP && GPT == SUB_PER_CHUNK, "draw tiling");
   __shared__ uint32_t bm[DRAW_CHUNK / 32];
-  __shared__ double T[64];
   __shared__ double scr[2 * SUB_PER_CHUNK][DR_THREADS / WAVE];
   const int tid = threadIdx.x;
   const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
@@ -280,7 +279,6 @@ __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a
       if (r.drow) load_group<Elem>(r.drow, x0, a.V, vec, dg[j]);
     }
   }
-  exp_table_init(T);
   range_bans(bm, DRAW_CHUNK, bans, nb, c0);
   double sw[GPT], sp[GPT];
 #pragma unroll
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a
       for (int e = 0; e < GRP; ++e) {
         double w, p;
         pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
-                    bm_test(bm, x0 - c0 + e), T, w, p);
+                    bm_test(bm, x0 - c0 + e), w, p);
         sw[j] += w;
         sp[j] += p;
       }
@@ -340,7 +338,6 @@ int launch_residual_partial(const DrawArgs& a, int B, hipStream_t st) {
 template <typename Elem>
 __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a) {
   __shared__ uint32_t bm[DRAW_SUB / 32];
-  __shared__ double T[64];
   __shared__ double scr[DR_THREADS / WAVE];
   __shared__ int32_t sel_sub, sel_x;
   __shared__ double sel_before;
@@ -350,7 +347,6 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
   const int n = rs.n;
   uint32_t flags = rs.flags;
   const ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
-  exp_table_init(T);
 
   // totals; fall back to p when the residual has no mass
   double tw = 0.0, tp = 0.0;
@@ -433,7 +429,7 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
       if (x0 + e < a.V) {
         double w, p;
         pair_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f,
-                    bm_test(bm, x0 - s0 + e), T, w, p);
+                    bm_test(bm, x0 - s0 + e), w, p);
         v[e] = use_p ? p : w;
       }
       lsum += v[e];
