@@ -85,8 +85,10 @@ typedef struct {
 
 #define SV_MAX_BANNED 2048 /* largest n_banned accepted */
 
-/* Workspace bytes needed by spec_verify_sample for these sizes (0 on bad sizes).
- * The workspace needs no initialisation and may be reused by later calls. */
+/* Workspace bytes needed by spec_verify_sample for these sizes (0 on bad sizes;
+ * n_banned is validated but does not change the size). The workspace needs no
+ * initialisation and may be reused by later calls on the same stream; calls
+ * that run concurrently need separate workspaces. */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t n_banned);
 
 /* Speculative-sampling verification.
@@ -150,14 +152,11 @@ const char* spec_verify_strerror(int status);
  * around it on the caller's stream. spec_verify_profile_stop synchronises on
  * those events, writes the summed milliseconds and launch counts of each
  * kernel (arrays of SV_NUM_KERNELS entries, indices SV_K_*), and releases them. */
-#define SV_K_BAN_PREP 0
-#define SV_K_ROW_STATS 1
-#define SV_K_ACCEPT 2
-#define SV_K_RESIDUAL_PARTIAL 3
-#define SV_K_RESIDUAL_SELECT 4
-#define SV_K_GREEDY_ARGMAX 5
-#define SV_K_GREEDY_SCAN 6
-#define SV_NUM_KERNELS 7
+#define SV_K_ROW_STATS 0
+#define SV_K_DRAW 1
+#define SV_K_GREEDY_ARGMAX 2
+#define SV_K_GREEDY_SCAN 3
+#define SV_NUM_KERNELS 4
 int spec_verify_profile_start(int32_t max_launches_per_kernel);
 int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 

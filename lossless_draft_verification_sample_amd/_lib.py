@@ -28,16 +28,12 @@ SV_FLAG_RESIDUAL_ZERO = 16
 
 SV_MAX_BANNED = 2048
 
-SV_K_BAN_PREP = 0
-SV_K_ROW_STATS = 1
-SV_K_ACCEPT = 2
-SV_K_RESIDUAL_PARTIAL = 3
-SV_K_RESIDUAL_SELECT = 4
-SV_K_GREEDY_ARGMAX = 5
-SV_K_GREEDY_SCAN = 6
-SV_NUM_KERNELS = 7
-KERNEL_NAMES = ["ban_prep", "row_stats", "accept", "residual_partial", "residual_select",
-                "greedy_argmax", "greedy_scan"]
+SV_K_ROW_STATS = 0
+SV_K_DRAW = 1
+SV_K_GREEDY_ARGMAX = 2
+SV_K_GREEDY_SCAN = 3
+SV_NUM_KERNELS = 4
+KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan"]
 
 
 class SvSampler(ctypes.Structure):

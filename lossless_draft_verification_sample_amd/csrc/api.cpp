@@ -19,8 +19,8 @@ constexpr size_t WS_ALIGN = 256;
 size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
-  size_t stats, req, sums, bans, banc, total;
-  int nchunk, nsub;
+  size_t stats, sums, tickets, total;
+  int nsub, spw, nwg;
 };
 
 bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
@@ -28,20 +28,24 @@ bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
     return false;
   const int64_t rows = (int64_t)B * (2 * (int64_t)gamma + 1);
   if (rows >= INT32_MAX) return false;
-  const int64_t nchunk = ((int64_t)V + sv::DRAW_CHUNK - 1) / sv::DRAW_CHUNK;
-  if ((int64_t)B * nchunk >= INT32_MAX) return false;
-  L->nchunk = (int)nchunk;
-  L->nsub = (int)(((int64_t)V + sv::DRAW_SUB - 1) / sv::DRAW_SUB);
+  const int64_t nsub = ((int64_t)V + sv::DRAW_SUB - 1) / sv::DRAW_SUB;
+  // draw workgroups: about DRAW_TARGET_WGS in total, each over at most
+  // DRAW_SPW_MAX sub-chunks of one request
+  int64_t nwg = (sv::DRAW_TARGET_WGS + B - 1) / B;
+  if (nwg > nsub) nwg = nsub;
+  int64_t spw = (nsub + nwg - 1) / nwg;
+  if (spw > sv::DRAW_SPW_MAX) spw = sv::DRAW_SPW_MAX;
+  nwg = (nsub + spw - 1) / spw;
+  if ((int64_t)B * nwg >= INT32_MAX) return false;
+  L->nsub = (int)nsub;
+  L->spw = (int)spw;
+  L->nwg = (int)nwg;
   size_t off = 0;
   L->stats = off;
   off = align_up(off + (size_t)rows * sizeof(sv::RowStat));
-  L->req = off;
-  off = align_up(off + (size_t)B * sizeof(sv::ReqState));
   L->sums = off;
-  off = align_up(off + (size_t)B * (size_t)L->nsub * sizeof(sv::ChunkSums));
-  L->bans = off;
-  off = align_up(off + (size_t)B * (size_t)n_banned * sizeof(int32_t));
-  L->banc = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sizeof(sv::ChunkSums));
+  L->tickets = off;
   off = align_up(off + (size_t)B * sizeof(int32_t));
   L->total = off;
   return true;
@@ -135,18 +139,12 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   sv::RowStat* stats = (sv::RowStat*)(ws + L.stats);
-  sv::ReqState* req = (sv::ReqState*)(ws + L.req);
   sv::ChunkSums* sums = (sv::ChunkSums*)(ws + L.sums);
-  int32_t* ban_sorted = n_banned ? (int32_t*)(ws + L.bans) : nullptr;
-  int32_t* ban_count = n_banned ? (int32_t*)(ws + L.banc) : nullptr;
+  int32_t* tickets = (int32_t*)(ws + L.tickets);
   const int bf16 = dtype == SV_BF16;
   const int rows = B * (2 * gamma + 1);
+  const int32_t* bans = n_banned ? banned_ids : nullptr;
 
-  if (n_banned) {
-    sv::BanPrepArgs a{banned_ids, n_banned, V, ban_sorted, ban_count};
-    ProfScope p(SV_K_BAN_PREP, st);
-    if (sv::launch_ban_prep(a, B, st)) return SV_EHIP;
-  }
   {
     sv::RowStatsArgs a{};
     a.target = target_logits;
@@ -155,38 +153,16 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.V = V;
     a.st = to_dev(target);
     a.sd = to_dev(draft);
-    a.ban_sorted = ban_sorted;
-    a.ban_count = ban_count;
-    a.ban_stride = n_banned;
+    a.draft_tokens = draft_tokens;
+    a.banned = bans;
+    a.n_banned = n_banned;
     a.stats = stats;
+    a.tickets = tickets;
     a.out_tlse = out_target_lse;
     a.out_dlse = out_draft_lse;
     a.force_generic = 0;
     ProfScope p(SV_K_ROW_STATS, st);
     if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
-  }
-  {
-    sv::AcceptArgs a{};
-    a.target = target_logits;
-    a.draft = draft_logits;
-    a.bf16 = bf16;
-    a.gamma = gamma;
-    a.V = V;
-    a.t_temp = target.temperature;
-    a.d_temp = draft.temperature;
-    a.draft_tokens = draft_tokens;
-    a.ban_sorted = ban_sorted;
-    a.ban_count = ban_count;
-    a.ban_stride = n_banned;
-    a.stats = stats;
-    a.uniforms = uniforms;
-    a.seed = seed;
-    a.offset = offset;
-    a.out_tokens = out_tokens;
-    a.out_num_accepted = out_num_accepted;
-    a.req = req;
-    ProfScope p(SV_K_ACCEPT, st);
-    if (sv::launch_accept(a, B, st)) return SV_EHIP;
   }
   {
     sv::DrawArgs a{};
@@ -197,26 +173,25 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
             ((size_t)V * es) % 16 == 0;
     a.gamma = gamma;
     a.V = V;
-    a.nchunk = L.nchunk;
     a.nsub = L.nsub;
+    a.spw = L.spw;
+    a.nwg = L.nwg;
     a.t_temp = target.temperature;
     a.d_temp = draft.temperature;
-    a.ban_sorted = ban_sorted;
-    a.ban_count = ban_count;
-    a.ban_stride = n_banned;
+    a.draft_tokens = draft_tokens;
+    a.banned = bans;
+    a.n_banned = n_banned;
     a.stats = stats;
-    a.req = req;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
     a.sums = sums;
+    a.tickets = tickets;
     a.out_tokens = out_tokens;
+    a.out_num_accepted = out_num_accepted;
     a.out_flags = out_flags;
-    {
-      ProfScope p(SV_K_RESIDUAL_PARTIAL, st);
-      if (sv::launch_residual_partial(a, B, st)) return SV_EHIP;
-    }
-    {
-      ProfScope p(SV_K_RESIDUAL_SELECT, st);
-      if (sv::launch_residual_select(a, B, st)) return SV_EHIP;
-    }
+    ProfScope p(SV_K_DRAW, st);
+    if (sv::launch_draw(a, B, st)) return SV_EHIP;
   }
   return SV_OK;
 }

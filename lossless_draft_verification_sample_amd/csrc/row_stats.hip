@@ -20,8 +20,9 @@
 //   top-k  = the value where the running count from the top reaches k,
 //   top-p  = the last value whose strictly-larger mass is < top_p * Z,
 // all exact (integer counts, fp64 sums in a fixed order, so the result is also
-// bitwise reproducible). Banned ids are subtracted from the counts afterwards
-// (the ban list is sorted and de-duplicated beforehand). Nonzero values below
+// bitwise reproducible). Banned ids are subtracted from the counts afterwards;
+// the raw ban list is first de-duplicated through a hash set in LDS (the space
+// of the histogram, before it is cleared). Nonzero values below
 // 2^-23 in magnitude are rare but do occur in large rows; they are counted with
 // the zero bin and kept, up to TINY_MAX of them, in a small list whose exact
 // contribution is added in a fixed (sorted) order. A row holding a value of
@@ -34,8 +35,12 @@
 // two; the per-lane sums are combined exactly at the end. Thresholds, when
 // asked for, come from a bisection over the order-preserving integer keys of
 // the values (16-bit keys for bf16 rows, 32-bit for fp32), one pass over the
-// row per step. Bans are tested against an LDS bitmap. Exact in the same
+// row per step. Bans are looked up in the LDS hash set. Exact in the same
 // sense as the histogram path, only slower for truncated rows.
+//
+// Each row also evaluates the probability of its proposal token (target row
+// i < gamma: p_i(x_i); draft row i: q_i(x_i)), which is all the acceptance walk
+// needs from the row.
 
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
@@ -48,8 +53,7 @@ namespace sv {
 #ifndef SV_RS_UNROLL
 #define SV_RS_UNROLL 4
 #endif
-// One workgroup per row, four per CU; each thread keeps four 16-byte loads in
-// flight.
+// One workgroup per row; each thread keeps four 16-byte loads in flight.
 constexpr int RS_THREADS = SV_RS_THREADS;
 constexpr int RS_UNROLL = SV_RS_UNROLL;
 
@@ -61,7 +65,11 @@ constexpr uint32_t HB_ZERO = HB_WIN;          // rank of zero; bin HB_WIN is a d
 constexpr uint32_t HB_BINS = HB_NEG + HB_WIN + 1u;
 constexpr int HB_RANKS = 2 * HB_WIN + 1;      // value-ordered ranks: +window, zero, -window
 constexpr uint32_t TINY_MAX = 64;             // tiny values tracked exactly per row
-constexpr int BM_MAX_BITS = (int)HB_BINS * 32; // largest V whose ban bitmap fits the LDS
+
+// LDS hash set of a request's banned ids (linear probing, at most half full).
+constexpr uint32_t HT_SLOTS = 4096;
+constexpr uint32_t HT_EMPTY = 0xFFFFFFFFu;
+static_assert(HT_SLOTS >= 2 * 2048 && HT_SLOTS <= HB_BINS, "ban hash set size");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -92,6 +100,7 @@ struct RowShared {
   double tiny_mass;
   float tiny_top;
   WaveSlot x1[RS_THREADS / WAVE], x2[RS_THREADS / WAVE], x3[RS_THREADS / WAVE];
+  uint32_t xban;       // the row's proposal token is banned
   double dscr[RS_THREADS / WAVE];
   float fscr[RS_THREADS / WAVE];
   uint32_t uscr[RS_THREADS / WAVE];
@@ -140,6 +149,49 @@ __device__ __forceinline__ void hb_count_one(uint32_t bits, RowShared& sh) {
     hb_classify_slow(bits, sh);
 }
 
+// ------------------------------------------------------------------ banned ids
+
+__device__ __forceinline__ uint32_t ht_slot(int32_t id) {
+  return ((uint32_t)id * 0x9E3779B1u) >> 20;   // multiplicative hash, 12 bits
+}
+
+// Inserts the valid ids of a raw ban list into the LDS hash set `tab` (all
+// slots HT_EMPTY beforehand). Bit k of the result is set when this thread's
+// k-th id (list index threadIdx.x + k * RS_THREADS) was the copy that entered
+// the set, so every distinct id has exactly one owner. `first` is list element
+// threadIdx.x, loaded by the caller. Sets *xban when the list holds `x`.
+__device__ __forceinline__ uint32_t ht_build(uint32_t* tab, const int32_t* bl, int nb, int V,
+                                             int32_t first, int32_t x, uint32_t* xban) {
+  uint32_t own = 0u;
+  int k = 0;
+  for (int j = threadIdx.x; j < nb; j += RS_THREADS, ++k) {
+    const int32_t id = j == (int)threadIdx.x ? first : bl[j];
+    if (id < 0 || id >= V) continue;
+    if (id == x) *xban = 1u;
+    uint32_t slot = ht_slot(id);
+    while (true) {
+      const uint32_t old = atomicCAS(&tab[slot], HT_EMPTY, (uint32_t)id);
+      if (old == HT_EMPTY) {
+        own |= 1u << k;
+        break;
+      }
+      if (old == (uint32_t)id) break;
+      slot = (slot + 1u) & (HT_SLOTS - 1u);
+    }
+  }
+  return own;
+}
+
+__device__ __forceinline__ bool ht_has(const uint32_t* tab, int32_t id) {
+  uint32_t slot = ht_slot(id);
+  while (true) {
+    const uint32_t v = tab[slot];
+    if (v == (uint32_t)id) return true;
+    if (v == HT_EMPTY) return false;
+    slot = (slot + 1u) & (HT_SLOTS - 1u);
+  }
+}
+
 // ------------------------------------------------------------------ generic path
 
 template <typename Elem>
@@ -182,18 +234,13 @@ __device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
   }
 }
 
-// Ban test of the generic path: an LDS bitmap when it fits, else a binary
-// search of the sorted list (also in LDS).
+// Admissibility test of the generic path: finite and not in the ban set.
 struct GenericCtx {
-  const uint32_t* bm;   // bitmap over [0, V) or nullptr
-  const int32_t* bans;  // sorted unique ids when bm == nullptr
-  int nb;
+  const uint32_t* tab;   // LDS hash set, or nullptr when the request bans nothing
   __device__ __forceinline__ bool admissible(float z, int id) const {
     // finite and not banned; NaN fails both comparisons
     if (!(z > -INFINITY && z < INFINITY)) return false;
-    if (nb == 0) return true;
-    if (bm) return !((bm[id >> 5] >> (id & 31)) & 1u);
-    return !in_sorted(bans, nb, id);
+    return !tab || !ht_has(tab, id);
   }
 };
 
@@ -568,9 +615,13 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
 
 // ------------------------------------------------------------------ the kernel
 
-// Two 1024-thread workgroups per CU need 8 waves per SIMD, i.e. <= 64 VGPRs.
+// Three 512-thread workgroups per CU (6 waves per SIMD, up to 80 VGPRs). The
+// streaming loop is bound by the CU's LDS atomic rate, which the resident
+// workgroups share, so a fourth one would not stream faster; it would only
+// force register spills in the epilogue and make the last round of rows
+// coarser (rows / (3 * CUs) is closer to a whole number for large batches).
 template <typename Elem>
-__global__ __launch_bounds__(RS_THREADS) __attribute__((amdgpu_waves_per_eu(2048 / RS_THREADS * RS_THREADS / 256)))
+__global__ __launch_bounds__(RS_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 void row_stats_kernel(RowStatsArgs a) {
   __shared__ RowShared sh;
   const int tid = threadIdx.x;
@@ -583,8 +634,15 @@ void row_stats_kernel(RowStatsArgs a) {
                          : (const Elem*)a.draft + ((int64_t)b * a.gamma + (i - G1)) * (int64_t)a.V;
   const SamplerDev s = is_target ? a.st : a.sd;
   const int V = a.V;
-  const int nb = a.ban_count ? a.ban_count[b] : 0;
-  const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
+  const int nb = a.banned ? a.n_banned : 0;
+  const int32_t* bl = a.banned ? a.banned + (int64_t)b * a.n_banned : nullptr;
+  // the proposal this row scores (none for the bonus row) and its logit
+  const int pi = is_target ? i : i - G1;
+  const int32_t xprop = pi < a.gamma ? a.draft_tokens[(int64_t)b * a.gamma + pi] : -1;
+  const bool xvalid = xprop >= 0 && xprop < V;
+  const float zx = (tid == 0 && xvalid) ? elem_value<Elem>(rowp[xprop]) : 0.0f;
+  const int32_t ban0 = tid < nb ? bl[tid] : -1;
+  if (tid == 0) sh.xban = 0u;
 
   RowStat out;
   out.m = -INFINITY;
@@ -592,12 +650,14 @@ void row_stats_kernel(RowStatsArgs a) {
   out.lse = -INFINITY;
   out.flags = 0u;
   out.path = 0u;
-  out.pad[0] = out.pad[1] = 0u;
+  out.px = 0.0;
 
   bool generic = (sizeof(Elem) == 4) || a.force_generic;
 
   if (!generic) {
-    for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = 0u;
+    // the first HT_SLOTS bins hold the ban hash set until the stream starts
+    const uint32_t fill = nb > 0 ? HT_EMPTY : 0u;
+    for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = k < HT_SLOTS ? fill : 0u;
     if (tid == 0) {
       sh.zero_cnt = 0u;
       sh.nonfinite = 0u;
@@ -607,8 +667,15 @@ void row_stats_kernel(RowStatsArgs a) {
     __syncthreads();
 
     const uint16_t* rp = (const uint16_t*)rowp;
-    // the banned logits are gathered now and subtracted after the stream
-    const uint32_t ban_bits = tid < nb ? (uint32_t)rp[bans[tid]] : 0xFF80u;
+    uint32_t own = 0u, ban_bits = 0u;
+    if (nb > 0) {
+      own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
+      // the banned logits are gathered now and subtracted after the stream
+      if (own & 1u) ban_bits = rp[ban0];
+      __syncthreads();
+      for (uint32_t k = tid; k < HT_SLOTS; k += RS_THREADS) sh.hist[k] = 0u;
+      __syncthreads();
+    }
     const uintptr_t addr = (uintptr_t)rp;
     int head = (int)(((16u - (addr & 15u)) & 15u) >> 1);
     if (head > V) head = V;
@@ -645,9 +712,11 @@ void row_stats_kernel(RowStatsArgs a) {
     }
     __syncthreads();
 
-    // remove the banned ids (sorted, unique, all in [0, V))
-    for (int j = tid; j < nb; j += RS_THREADS) {
-      const uint32_t bits = j == tid ? ban_bits : (uint32_t)rp[bans[j]];
+    // remove each distinct banned id once (its owner subtracts it)
+    int kb = 0;
+    for (int j = tid; j < nb; j += RS_THREADS, ++kb) {
+      if (!((own >> kb) & 1u)) continue;
+      const uint32_t bits = kb == 0 ? ban_bits : (uint32_t)rp[bl[j]];
       const uint32_t ae = bits & 0x7FFFu;
       const uint32_t t = ae - HB_BASE;
       if (t < HB_WIN)
@@ -678,31 +747,26 @@ void row_stats_kernel(RowStatsArgs a) {
 
   if (generic) {
     __syncthreads();
-    // bans move into LDS (reusing the histogram storage): a bitmap if it fits
-    GenericCtx g{nullptr, nullptr, nb};
+    // the ban set moves into the (now free) histogram storage
+    GenericCtx g{nullptr};
     if (nb > 0) {
-      if (V <= BM_MAX_BITS) {
-        const int words = (V + 31) >> 5;
-        for (int k = tid; k < words; k += RS_THREADS) sh.hist[k] = 0u;
-        __syncthreads();
-        for (int j = tid; j < nb; j += RS_THREADS) {
-          const int id = bans[j];
-          atomicOr(&sh.hist[id >> 5], 1u << (id & 31));
-        }
-        g.bm = sh.hist;
-      } else {
-        int32_t* lbans = (int32_t*)sh.hist;
-        for (int j = tid; j < nb; j += RS_THREADS) lbans[j] = bans[j];
-        g.bans = lbans;
-      }
+      for (uint32_t k = tid; k < HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
       __syncthreads();
+      (void)ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
+      __syncthreads();
+      g.tab = sh.hist;
     }
     out.flags &= ~FLAG_EMPTY;
     row_generic<Elem>(rowp, V, s, g, sh, out);
   }
 
   if (tid == 0) {
+    // probability of the row's proposal under the row's distribution
+    const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zx > -INFINITY &&
+                      zx < INFINITY && zx >= out.tau;
+    out.px = kept ? exp((double)zx / (double)s.temperature - out.lse) : 0.0;
     a.stats[row] = out;
+    if (i == 0 && a.tickets) a.tickets[b] = 0;
     if (is_target) {
       if (a.out_tlse) a.out_tlse[(int64_t)b * G1 + i] = (float)out.lse;
     } else {

@@ -15,25 +15,19 @@ constexpr uint32_t FLAG_RESIDUAL_ZERO = 16u;
 constexpr int WAVE = 64;
 
 // Statistics of one sampler-transformed logit row, produced by row_stats and
-// consumed by the acceptance and final-draw kernels. A token x of the row is
-// kept iff it is not banned, its logit z is finite and z >= tau.
+// consumed by the draw kernel. A token x of the row is kept iff it is not
+// banned, its logit z is finite and z >= tau.
 struct alignas(16) RowStat {
   float m;         // largest kept logit (-inf for an empty row)
   float tau;       // truncation threshold on the logit value (-inf: none)
   double lse;      // log sum_{kept} exp(z / T)   (-inf for an empty row)
   uint32_t flags;  // FLAG_NONFINITE | FLAG_EMPTY
   uint32_t path;   // 0 = count histogram, 1 = generic streaming path
-  uint32_t pad[2];
+  double px;       // probability of the row's proposal token (target row i < gamma:
+                   // p_i(x_i); draft row i: q_i(x_i)); 0 when it has none
 };
 
-// Per-request state handed from the acceptance kernel to the final draw.
-struct alignas(16) ReqState {
-  int32_t n;       // accepted proposals; the final token goes to slot n
-  uint32_t flags;  // flags gathered so far
-  double u_final;  // uniform of the final draw
-};
-
-// Partial sums of one vocabulary chunk for the final draw.
+// Partial sums of one vocabulary sub-chunk for the final draw.
 struct alignas(16) ChunkSums {
   double w;  // sum of max(0, p - q) (bonus draw: sum of p)
   double p;  // sum of p (fallback when the residual mass is zero)
@@ -262,32 +256,6 @@ __device__ __forceinline__ T block_excl_scan(T v, T* scratch, T* total) {
   }
   *total = all;
   return before + incl - v;
-}
-
-// Sorted, de-duplicated ban list of one request (ids in [0, V)).
-__device__ __forceinline__ bool in_sorted(const int32_t* list, int n, int32_t id) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int32_t v = list[mid];
-    if (v < id)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return lo < n && list[lo] == id;
-}
-// First index with list[i] >= id.
-__device__ __forceinline__ int lower_bound(const int32_t* list, int n, int32_t id) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] < id)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return lo;
 }
 
 }  // namespace sv

@@ -1,11 +1,11 @@
-// Ban-list preparation, acceptance walk and final draw of spec_verify_sample.
+// Acceptance walk and final draw of spec_verify_sample, in one kernel.
 //
 // Acceptance ("Speculative Decoding - Turn guesses into parallel work", section
 // "Exact sampling: account for every probability"; "Speculative Token
 // Decoupling ..." Equation 3.1): proposal i of a request is accepted iff
 // u_i * q_i(x_i) <= p_i(x_i), walking left to right and stopping at the first
-// rejection. p and q are recomputed in fp64 from the gathered logits and the
-// row statistics.
+// rejection. p_i(x_i) and q_i(x_i) come from the row statistics pass, which
+// evaluates them in fp64 next to each row's normaliser.
 //
 // Final draw ("Drafters and Speculative Decoding: Useful Tokens, Correct State",
 // section "Sampling needs a correction rule"; "Speculative Decoding"
@@ -13,153 +13,37 @@
 // drawn from norm(max(0, p_n - q_n)); if every proposal survived it is drawn
 // from p_gamma. The draw is an inverse CDF in ascending token order: the
 // smallest x whose running weight sum reaches u * S. Only the one (or two)
-// selected rows per request are read again. The vocabulary is cut into chunks:
-// one kernel sums each chunk's weights, a second one locates the chunk holding
-// u * S and scans just that chunk.
+// selected rows per request are read again.
+//
+// Work split: each request gets `nwg` workgroups, each owning `spw` consecutive
+// sub-chunks of DRAW_SUB tokens. Every workgroup repeats the (tiny) acceptance
+// walk to learn n, sums the draw weights of its sub-chunks and publishes them;
+// the last workgroup of the request to finish (an arrival counter) locates the
+// sub-chunk holding u * S, rescans it and writes the request's outputs.
 
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 
 namespace sv {
 
-// ------------------------------------------------------------------ ban lists
+constexpr int DR_THREADS = 256;
+constexpr int DR_NW = DR_THREADS / WAVE;
+constexpr int GRP = 8;          // logits per thread per sub-chunk
+constexpr int GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
+static_assert(DRAW_SUB == DR_THREADS * GRP, "one group of GRP logits per thread per sub-chunk");
 
-constexpr int BP_THREADS = 256;
-constexpr int BP_MAX = 2048;
-
-__global__ __launch_bounds__(BP_THREADS) void ban_prep_kernel(BanPrepArgs a) {
-  __shared__ int32_t s[BP_MAX];
-  __shared__ uint32_t scr[BP_THREADS / WAVE];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int np = 1;
-  while (np < a.n_banned) np <<= 1;
-  for (int j = tid; j < np; j += BP_THREADS) {
-    int32_t v = INT32_MAX;
-    if (j < a.n_banned) {
-      const int32_t id = a.banned[(int64_t)b * a.n_banned + j];
-      if (id >= 0 && id < a.V) v = id;
-    }
-    s[j] = v;
-  }
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int k = 2; k <= np; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < np; i += BP_THREADS) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = s[i], y = s[ixj];
-          const bool up = (i & k) == 0;
-          if (up ? (x > y) : (x < y)) {
-            s[i] = y;
-            s[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // keep the first of every run of equal valid ids, compacted in order
-  const int per = (np + BP_THREADS - 1) / BP_THREADS;
-  const int j0 = tid * per;
-  uint32_t keep = 0;
-  for (int j = j0; j < j0 + per && j < np; ++j)
-    keep += (s[j] != INT32_MAX && (j == 0 || s[j] != s[j - 1])) ? 1u : 0u;
-  uint32_t total;
-  uint32_t pos = block_excl_scan<BP_THREADS>(keep, scr, &total);
-  for (int j = j0; j < j0 + per && j < np; ++j) {
-    if (s[j] != INT32_MAX && (j == 0 || s[j] != s[j - 1]))
-      a.ban_sorted[(int64_t)b * a.n_banned + pos++] = s[j];
-  }
-  if (tid == 0) a.ban_count[b] = (int32_t)total;
-}
-
-int launch_ban_prep(const BanPrepArgs& a, int B, hipStream_t st) {
-  hipLaunchKernelGGL(ban_prep_kernel, dim3(B), dim3(BP_THREADS), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// ------------------------------------------------------------------ helpers
-
-__device__ __forceinline__ float load_logit(const void* base, int bf16, int64_t idx) {
-  if (bf16) return bf16_to_f32(((const uint16_t*)base)[idx]);
-  return ((const float*)base)[idx];
-}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool is_kept(float z, const RowStat& s, bool banned) {
   return !banned && !(s.flags & FLAG_EMPTY) && z > -INFINITY && z < INFINITY && z >= s.tau;
 }
-
-// ------------------------------------------------------------------ acceptance
-
-__global__ __launch_bounds__(WAVE) void accept_kernel(AcceptArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
-  const RowStat* st = a.stats + (int64_t)b * RPR;
-  const int nb = a.ban_count ? a.ban_count[b] : 0;
-  const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
-
-  uint32_t rf = 0;
-  for (int r = lane; r < RPR; r += WAVE) rf |= st[r].flags & (FLAG_NONFINITE | FLAG_EMPTY);
-#pragma unroll
-  for (int off = WAVE / 2; off > 0; off >>= 1) rf |= __shfl_xor(rf, off, WAVE);
-
-  int32_t x = -1;
-  bool acc = false, range = false, qzero = false;
-  if (lane < g) {
-    x = a.draft_tokens[(int64_t)b * g + lane];
-    range = x < 0 || x >= a.V;
-    if (!range) {
-      const float zt = load_logit(a.target, a.bf16, ((int64_t)b * G1 + lane) * a.V + x);
-      const float zd = load_logit(a.draft, a.bf16, ((int64_t)b * g + lane) * a.V + x);
-      const bool banned = nb > 0 && in_sorted(bans, nb, x);
-      const RowStat ts = st[lane], ds = st[G1 + lane];
-      const double p = is_kept(zt, ts, banned) ? exp((double)zt / (double)a.t_temp - ts.lse) : 0.0;
-      const double q = is_kept(zd, ds, banned) ? exp((double)zd / (double)a.d_temp - ds.lse) : 0.0;
-      const double u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
-                                  : philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)lane);
-      qzero = !(q > 0.0);
-      acc = !qzero && u * q <= p;
-    }
-  }
-  const uint64_t accm = __ballot(acc);
-  const uint64_t rangem = __ballot(range);
-  const uint64_t qzm = __ballot(qzero && !range);
-  int n = __ffsll((unsigned long long)~accm) - 1;
-  if (n > g) n = g;
-  uint32_t flags = rf;
-  if (rangem) flags |= FLAG_TOKEN_RANGE;
-  if (n < g && ((qzm >> n) & 1ull)) flags |= FLAG_Q_ZERO;
-  if (lane < n) a.out_tokens[(int64_t)b * G1 + lane] = x;
-  if (lane == 0) {
-    a.out_num_accepted[b] = n;
-    ReqState rs;
-    rs.n = n;
-    rs.flags = flags;
-    rs.u_final = a.uniforms ? a.uniforms[(int64_t)b * G1 + g]
-                            : philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)g);
-    a.req[b] = rs;
-  }
-}
-
-int launch_accept(const AcceptArgs& a, int B, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(WAVE), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// ------------------------------------------------------------------ final draw
-
-constexpr int DR_THREADS = 256;
-constexpr int GRP = 8;                                   // logits per group
-constexpr int GPT = DRAW_CHUNK / GRP / DR_THREADS;       // groups per thread
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct DrawRow {
   const void* trow;
   const void* drow;   // nullptr for the bonus draw
   RowStat ts, ds;
   double tinv, dinv;  // 1/T of both rows
+  float tcut;         // no target token below this is kept (+inf: empty row)
 };
 
 __device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n) {
@@ -170,6 +54,7 @@ __device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n) {
   r.trow = (const char*)a.target + ((int64_t)b * G1 + n) * V * es;
   r.ts = a.stats[(int64_t)b * RPR + n];
   r.tinv = 1.0 / (double)a.t_temp;
+  r.tcut = (r.ts.flags & FLAG_EMPTY) ? INFINITY : r.ts.tau;
   if (n < g) {
     r.drow = (const char*)a.draft + ((int64_t)b * g + n) * V * es;
     r.ds = a.stats[(int64_t)b * RPR + G1 + n];
@@ -219,143 +104,302 @@ __device__ __forceinline__ float group_val(const Group<Elem>& g, int j) {
   return __uint_as_float(g.w[j >> 2][j & 3]);
 }
 
-// p(x) and the draw weight of token x: max(0, p - q) at a rejection, p for the
-// bonus draw. fp64 throughout (exp of an fp64 argument), so the running sums
-// of the inverse CDF carry no fp32 error.
-__device__ __forceinline__ void pair_weight(const DrawRow& r, float zt, float zd, bool banned,
-                                            double& w, double& p) {
-  p = is_kept(zt, r.ts, banned) ? exp_neg((double)zt * r.tinv - r.ts.lse) : 0.0;
+// exp(a) in fp64 for a <= about 0, table-driven (P. T. P. Tang, "Table-driven
+// implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989): a = (256 k' + j) ln2 / 256 + r with
+// |r| <= ln2 / 512, so e^a = 2^k' * 2^(j/256) * e^r; 2^(j/256) comes from a
+// 256-entry LDS table and e^r - 1 from its degree-4 Taylor polynomial
+// (remainder below 4e-17 relative). Error a few ulp.
+__device__ __forceinline__ double exp_tab(double a, const double* tab) {
+  a = fmax(a, -1000.0);                                    // exp(-1000) is 0 in fp64
+  const double kf = rint(a * 0x1.71547652b82fep+8);        // 256 / ln2
+  double r = fma(-kf, 0x1.62e42fef80000p-9, a);            // head of ln2 / 256 (34 bits)
+  r = fma(-kf, 0x1.1cf79abc9e3b4p-44, r);                  // tail of ln2 / 256
+  double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+  q = fma(q, r, 0.5);
+  q = fma(q, r, 1.0);
+  q *= r;                                                  // e^r - 1
+  const int k = (int)kf;
+  const double t = tab[k & 255];
+  return ldexp(fma(t, q, t), k >> 8);
+}
+
+// The 2^(j/256) table of exp_tab, filled by the first 256 threads.
+__device__ __forceinline__ void exp_table_fill(double* tab) {
+  if (threadIdx.x < 256) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 256.0));
+}
+
+// Draw weight of one token whose target logit zt is kept: p(x), and
+// w(x) = max(0, p - q) at a rejection (w = p for the bonus draw).
+__device__ __forceinline__ void tok_weight(const DrawRow& r, float zt, float zd, const double* tab,
+                                           double& w, double& p) {
+  p = exp_tab(fma((double)zt, r.tinv, -r.ts.lse), tab);
+  w = p;
   if (r.drow) {
-    const double q = is_kept(zd, r.ds, banned) ? exp_neg((double)zd * r.dinv - r.ds.lse) : 0.0;
+    // zd belongs to a token that is not banned (its target logit is kept)
+    const double q = is_kept(zd, r.ds, false) ? exp_tab(fma((double)zd, r.dinv, -r.ds.lse), tab)
+                                              : 0.0;
     w = p > q ? p - q : 0.0;
-  } else {
-    w = p;
   }
 }
 
-// Marks the banned ids of [c0, c0 + len) in an LDS bitmap of len / 32 words.
-__device__ __forceinline__ void range_bans(uint32_t* bm, int len, const int32_t* bans, int nb,
-                                           int c0) {
+// Bit e set when token e of the group is kept in the target row; only those
+// tokens have p > 0, hence w > 0. `banned` holds one bit per token.
+template <typename Elem>
+__device__ __forceinline__ uint32_t kept_mask(const DrawRow& r, const Group<Elem>& tg,
+                                              uint32_t banned) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int e = 0; e < GRP; ++e)
+    m |= (is_kept(group_val<Elem>(tg, e), r.ts, (banned >> e) & 1u) ? 1u : 0u) << e;
+  return m;
+}
+
+// Per-token draw weights of a group (0 outside the kept mask).
+template <typename Elem>
+__device__ __forceinline__ void group_weights(const DrawRow& r, const Group<Elem>& tg,
+                                              const Group<Elem>& dg, uint32_t km,
+                                              const double* tab, double (&w)[GRP],
+                                              double (&p)[GRP]) {
+#pragma unroll
+  for (int e = 0; e < GRP; ++e) {
+    w[e] = 0.0;
+    p[e] = 0.0;
+    if ((km >> e) & 1u)
+      tok_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab, w[e], p[e]);
+  }
+}
+
+// Marks the banned ids that fall in [c0, c0 + len) in an LDS bitmap of len / 32
+// words. The list is raw: ids outside [0, V) are padding and duplicates set the
+// same bit. `first` is element threadIdx.x of the list, loaded by the caller.
+__device__ __forceinline__ void mark_bans(uint32_t* bm, int len, const int32_t* bl, int nb,
+                                          int32_t first, int c0, int V) {
   for (int k = threadIdx.x; k < len / 32; k += blockDim.x) bm[k] = 0u;
   __syncthreads();
-  if (nb > 0) {
-    const int lo = lower_bound(bans, nb, c0);
-    const int hi = lower_bound(bans, nb, c0 + len);
-    for (int j = lo + (int)threadIdx.x; j < hi; j += blockDim.x) {
-      const int o = bans[j] - c0;
+  for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+    const int32_t id = j == (int)threadIdx.x ? first : bl[j];
+    if (id >= c0 && id < V && id - c0 < len) {
+      const int o = id - c0;
       atomicOr(&bm[o >> 5], 1u << (o & 31));
     }
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ bool bm_test(const uint32_t* bm, int o) {
-  return (bm[o >> 5] >> (o & 31)) & 1u;
+// Ban bits of the eight tokens at offset o (a multiple of 8) of the bitmap.
+__device__ __forceinline__ uint32_t bm_group(const uint32_t* bm, int o) {
+  return (bm[o >> 5] >> (o & 31)) & 0xFFu;
 }
 
-// One workgroup per (request, DRAW_CHUNK tokens): weight sums per DRAW_SUB.
-// Group j of thread t covers tokens c0 + j*DRAW_SUB + 8t .. +8, so sub-chunk j
-// is exactly the j-th group of every thread and the loads are coalesced.
-template <typename Elem>
-__global__ __launch_bounds__(DR_THREADS) void residual_partial_kernel(DrawArgs a) {
-  static_assert(DRAW_SUB == DR_THREADS * GRP && GPT == SUB_PER_CHUNK, "draw tiling");
-  __shared__ uint32_t bm[DRAW_CHUNK / 32];
-  __shared__ double scr[2 * SUB_PER_CHUNK][DR_THREADS / WAVE];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
-  const ReqState rs = a.req[b];
-  const DrawRow r = draw_row(a, b, rs.n);
-  const int nb = a.ban_count ? a.ban_count[b] : 0;
-  const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
-  const int c0 = c * DRAW_CHUNK;
-  const bool vec = a.vec;
-  // every load of this thread in flight before any use
-  Group<Elem> tg[GPT], dg[GPT];
-#pragma unroll
-  for (int j = 0; j < GPT; ++j) {
-    const int x0 = c0 + j * DRAW_SUB + tid * GRP;
-    if (x0 < a.V) {
-      load_group<Elem>(r.trow, x0, a.V, vec, tg[j]);
-      if (r.drow) load_group<Elem>(r.drow, x0, a.V, vec, dg[j]);
-    }
+__device__ __forceinline__ double wave_total(double v) {
+  return lane63(wave_scan_dpp(v, 0.0, [](double x, double y) { return x + y; }));
+}
+
+// Outcome of the acceptance walk of one request, computed by every wave.
+struct Walk {
+  int n;           // accepted proposals; the final token goes to slot n
+  uint32_t flags;
+  double u_final;  // uniform of the final draw
+  int32_t x;       // proposal of this lane (lanes < gamma)
+};
+
+__device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
+  const RowStat* st = a.stats + (int64_t)b * RPR;
+  uint32_t rf = 0u;
+  double p = 0.0, q = 0.0, u = 0.0;
+  int32_t x = -1;
+  if (lane <= g) {
+    const RowStat t = st[lane];
+    rf |= t.flags;
+    p = t.px;
+    u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
+                   : philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)lane);
   }
-  range_bans(bm, DRAW_CHUNK, bans, nb, c0);
-  double sw[GPT], sp[GPT];
+  if (lane < g) {
+    const RowStat d = st[G1 + lane];
+    rf |= d.flags;
+    q = d.px;
+    x = a.draft_tokens[(int64_t)b * g + lane];
+  }
+  rf &= FLAG_NONFINITE | FLAG_EMPTY;
 #pragma unroll
-  for (int j = 0; j < GPT; ++j) {
-    sw[j] = 0.0;
-    sp[j] = 0.0;
-    const int x0 = c0 + j * DRAW_SUB + tid * GRP;
-    if (x0 < a.V) {
+  for (int off = WAVE / 2; off > 0; off >>= 1) rf |= __shfl_xor(rf, off, WAVE);
+  const bool range = lane < g && (x < 0 || x >= a.V);
+  const bool qzero = lane < g && !range && !(q > 0.0);
+  const bool acc = lane < g && !range && !qzero && u * q <= p;
+  const uint64_t accm = __ballot(acc);
+  const uint64_t rangem = __ballot(range);
+  const uint64_t qzm = __ballot(qzero);
+  Walk w;
+  w.n = __ffsll((unsigned long long)~accm) - 1;   // lane g never accepts: n <= g
+  w.flags = rf;
+  if (rangem) w.flags |= FLAG_TOKEN_RANGE;
+  if (w.n < g && ((qzm >> w.n) & 1ull)) w.flags |= FLAG_Q_ZERO;
+  const uint64_t ub = (uint64_t)__double_as_longlong(u);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ub, g);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ub >> 32), g);
+  w.u_final = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  w.x = x;
+  return w;
+}
+
+// A kept token of a wave's sub-chunk, queued for dense evaluation.
+struct alignas(16) KeptTok {
+  int32_t x;
+  float zt, zd;
+  int32_t pad;
+};
+
+struct DrawShared {
+  double etab[256];
+  KeptTok kt[DR_NW][WAVE];
+  uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
+  double w[DRAW_SPW_MAX];
+  double p[DRAW_SPW_MAX];
+  double scr[DR_NW];
+  int32_t last;
+  int32_t sel_sub, sel_x;
+  double sel_before;
+};
+
+template <typename Elem>
+__global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
+  __shared__ DrawShared sh;
+  const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
+  const int b = blockIdx.x / a.nwg, part = blockIdx.x % a.nwg;
+  const int g = a.gamma, G1 = g + 1;
+  const int sub0 = part * a.spw;
+  const int nsl = min(a.spw, a.nsub - sub0);
+  const int tok0 = sub0 * DRAW_SUB;
+  const int nb = a.banned ? a.n_banned : 0;
+  const int32_t* bl = a.banned ? a.banned + (int64_t)b * a.n_banned : nullptr;
+  const int32_t ban0 = tid < nb ? bl[tid] : -1;
+
+  exp_table_fill(sh.etab);
+  const Walk wk = accept_walk(a, b);
+  const DrawRow r = draw_row(a, b, wk.n);
+  mark_bans(sh.bm, nsl * DRAW_SUB, bl, nb, ban0, tok0, a.V);   // also publishes etab
+
+  // Weight sums of the workgroup's sub-chunks: wave wv owns sub-chunks wv,
+  // wv + DR_NW, ...; lane l reads groups l, l + 64, l + 128, l + 192 of a
+  // sub-chunk, so every load instruction covers 1 KiB of the row. Only tokens
+  // kept in the target row carry weight. A truncated target row keeps few
+  // tokens, spread thinly: their draft logits are gathered once the target
+  // groups are known, and the wave queues its kept tokens in LDS so that lane k
+  // evaluates the k-th one (one dense pass instead of divergent ones). A wave
+  // with more kept tokens than lanes evaluates them in place.
+  const bool sparse = r.ts.tau > -INFINITY;
+  for (int sl = wv; sl < nsl; sl += DR_NW) {
+    const int sbase = tok0 + sl * DRAW_SUB;
+    Group<Elem> tg[GPL], dg[GPL];
 #pragma unroll
-      for (int e = 0; e < GRP; ++e) {
-        double w, p;
-        pair_weight(r, group_val<Elem>(tg[j], e), r.drow ? group_val<Elem>(dg[j], e) : 0.0f,
-                    bm_test(bm, x0 - c0 + e), w, p);
-        sw[j] += w;
-        sp[j] += p;
+    for (int k = 0; k < GPL; ++k) {
+      const int x0 = sbase + (lane + k * WAVE) * GRP;
+      if (x0 < a.V) {
+        load_group<Elem>(r.trow, x0, a.V, a.vec, tg[k]);
+        if (r.drow && !sparse) load_group<Elem>(r.drow, x0, a.V, a.vec, dg[k]);
       }
     }
-  }
-  // per-sub-chunk block sums in a fixed order
-  const int wv = tid / WAVE, lane = tid & (WAVE - 1);
+    uint32_t km[GPL], cnt = 0u;
 #pragma unroll
-  for (int j = 0; j < GPT; ++j) {
-    const double a0 = wave_sum(sw[j]), a1 = wave_sum(sp[j]);
+    for (int k = 0; k < GPL; ++k) {
+      const int x0 = sbase + (lane + k * WAVE) * GRP;
+      km[k] = x0 < a.V ? kept_mask<Elem>(r, tg[k], bm_group(sh.bm, x0 - tok0)) : 0u;
+      cnt += (uint32_t)__popc(km[k]);
+    }
+    if (r.drow && sparse) {
+#pragma unroll
+      for (int k = 0; k < GPL; ++k)
+        if (km[k]) load_group<Elem>(r.drow, sbase + (lane + k * WAVE) * GRP, a.V, a.vec, dg[k]);
+    }
+    double sw = 0.0, sp = 0.0;
+    const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+    const uint32_t total = lane63(incl);
+    if (total <= (uint32_t)WAVE) {
+      if (total) {
+        uint32_t pos = incl - cnt;
+#pragma unroll
+        for (int k = 0; k < GPL; ++k) {
+          uint32_t mm = km[k];
+          while (mm) {
+            const int e = __ffs(mm) - 1;
+            mm &= mm - 1u;
+            KeptTok t;
+            t.x = sbase + (lane + k * WAVE) * GRP + e;
+            t.zt = group_val<Elem>(tg[k], e);
+            t.zd = r.drow ? group_val<Elem>(dg[k], e) : 0.0f;
+            t.pad = 0;
+            sh.kt[wv][pos++] = t;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if ((uint32_t)lane < total) {
+          const KeptTok t = sh.kt[wv][lane];
+          tok_weight(r, t.zt, t.zd, sh.etab, sw, sp);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < GPL; ++k) {
+        if (km[k]) {
+          double w[GRP], p[GRP];
+          group_weights<Elem>(r, tg[k], dg[k], km[k], sh.etab, w, p);
+#pragma unroll
+          for (int e = 0; e < GRP; ++e) {
+            sw += w[e];
+            sp += p[e];
+          }
+        }
+      }
+    }
+    sw = wave_total(sw);
+    sp = wave_total(sp);
     if (lane == 0) {
-      scr[2 * j][wv] = a0;
-      scr[2 * j + 1][wv] = a1;
+      sh.w[sl] = sw;
+      sh.p[sl] = sp;
     }
   }
   __syncthreads();
-  if (tid < GPT) {
-    const int sub = c * SUB_PER_CHUNK + tid;
-    if (sub < a.nsub) {
-      double w = 0.0, p = 0.0;
-#pragma unroll
-      for (int k = 0; k < DR_THREADS / WAVE; ++k) {
-        w += scr[2 * tid][k];
-        p += scr[2 * tid + 1][k];
-      }
-      ChunkSums cs;
-      cs.w = w;
-      cs.p = p;
-      a.sums[(int64_t)b * a.nsub + sub] = cs;
-    }
+  if (tid < nsl) {
+    // Publication without a release fence: the sums are agent-scope atomic
+    // stores, which the hardware writes through to the device-coherent level,
+    // and each writer waits for its stores to complete before the barrier, so
+    // they are visible device-wide before thread 0 bumps the arrival counter.
+    // The reader uses agent-scope atomic loads. (A release on the counter would
+    // also write back the whole L2, once per workgroup, for nothing.)
+    double* dst = &a.sums[(int64_t)b * a.nsub + sub0 + tid].w;
+    __hip_atomic_store(dst, sh.w[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, sh.p[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
   }
-}
+  // the last workgroup of the request to arrive performs the selection
+  __syncthreads();
+  if (tid == 0)
+    sh.last = __hip_atomic_fetch_add(&a.tickets[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              a.nwg - 1;
+  __syncthreads();
+  if (!sh.last) return;
 
-int launch_residual_partial(const DrawArgs& a, int B, hipStream_t st) {
-  if (a.bf16)
-    hipLaunchKernelGGL(residual_partial_kernel<uint16_t>, dim3(a.nchunk * B), dim3(DR_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(residual_partial_kernel<float>, dim3(a.nchunk * B), dim3(DR_THREADS), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// One workgroup per request: locate the sub-chunk holding u * S from the
-// partial sums, then rescan those DRAW_SUB tokens (8 per thread, in id order).
-template <typename Elem>
-__global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a) {
-  __shared__ uint32_t bm[DRAW_SUB / 32];
-  __shared__ double scr[DR_THREADS / WAVE];
-  __shared__ int32_t sel_sub, sel_x;
-  __shared__ double sel_before;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int g = a.gamma, G1 = g + 1;
-  const ReqState rs = a.req[b];
-  const int n = rs.n;
-  uint32_t flags = rs.flags;
-  const ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
-
-  // totals; fall back to p when the residual has no mass
+  const int n = wk.n;
+  uint32_t flags = wk.flags;
+  ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
+  auto ld = [](double* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   double tw = 0.0, tp = 0.0;
   for (int c = tid; c < a.nsub; c += DR_THREADS) {
-    tw += cs[c].w;
-    tp += cs[c].p;
+    tw += ld(&cs[c].w);
+    tp += ld(&cs[c].p);
   }
-  tw = block_sum<DR_THREADS>(tw, scr);
-  tp = block_sum<DR_THREADS>(tp, scr);
+  tw = block_sum<DR_THREADS>(tw, sh.scr);
+  tp = block_sum<DR_THREADS>(tp, sh.scr);
+  // fall back to p when the residual has no mass
   bool use_p = false;
   double S = tw;
   if (!(tw > 0.0) && n < g) {
@@ -367,80 +411,80 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
   if (!(S > 0.0)) {
     flags |= FLAG_EMPTY;
   } else {
-    const double t = rs.u_final * S;
+    const double t = wk.u_final * S;
     // sub-chunk holding t: per-thread contiguous runs, a block scan, and the
     // first thread whose run reaches t searches its run
     const int per = (a.nsub + DR_THREADS - 1) / DR_THREADS;
     const int k0 = tid * per;
     double loc = 0.0;
-    for (int c = k0; c < k0 + per && c < a.nsub; ++c) loc += use_p ? cs[c].p : cs[c].w;
+    for (int c = k0; c < k0 + per && c < a.nsub; ++c) loc += ld(use_p ? &cs[c].p : &cs[c].w);
     double tot;
-    const double before = block_excl_scan<DR_THREADS>(loc, scr, &tot);
+    const double before = block_excl_scan<DR_THREADS>(loc, sh.scr, &tot);
     const int cand = block_min<DR_THREADS>((loc > 0.0 && before + loc >= t) ? tid : DR_THREADS,
-                                           (int*)scr);
+                                           (int*)sh.scr);
     if (tid == 0) {
-      sel_sub = -1;
-      sel_before = 0.0;
+      sh.sel_sub = -1;
+      sh.sel_before = 0.0;
     }
     __syncthreads();
     if (tid == cand) {
       double run = before;
       for (int c = k0; c < k0 + per && c < a.nsub; ++c) {
-        const double v = use_p ? cs[c].p : cs[c].w;
+        const double v = ld(use_p ? &cs[c].p : &cs[c].w);
         if (v > 0.0) {
-          sel_sub = c;              // the last sub-chunk with weight unless one reaches t
-          sel_before = run;
+          sh.sel_sub = c;           // the last sub-chunk with weight unless one reaches t
+          sh.sel_before = run;
           if (run + v >= t) break;
         }
         run += v;
       }
     }
     __syncthreads();
-    if (sel_sub < 0 && tid == 0) {
+    if (sh.sel_sub < 0 && tid == 0) {
       // t above every prefix through rounding: the last sub-chunk with weight
       double run = 0.0;
       for (int c = 0; c < a.nsub; ++c) {
-        const double v = use_p ? cs[c].p : cs[c].w;
+        const double v = ld(use_p ? &cs[c].p : &cs[c].w);
         if (v > 0.0) {
-          sel_sub = c;
-          sel_before = run;
+          sh.sel_sub = c;
+          sh.sel_before = run;
         }
         run += v;
       }
     }
     __syncthreads();
-    const int s0 = sel_sub * DRAW_SUB;
-    const double tl = t - sel_before;
-    const DrawRow r = draw_row(a, b, n);
-    const int nb = a.ban_count ? a.ban_count[b] : 0;
-    const int32_t* bans = a.ban_sorted ? a.ban_sorted + (int64_t)b * a.ban_stride : nullptr;
+  }
+  if (S > 0.0 && sh.sel_sub < 0) flags |= FLAG_EMPTY;   // no sub-chunk with weight
+  if (S > 0.0 && sh.sel_sub >= 0) {
+    const int s0 = sh.sel_sub * DRAW_SUB;
+    const double tl = wk.u_final * S - sh.sel_before;
     const int x0 = s0 + tid * GRP;
     Group<Elem> tg, dg;
     if (x0 < a.V) {
       load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
       if (r.drow) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
     }
-    range_bans(bm, DRAW_SUB, bans, nb, s0);
-    double v[GRP];
+    mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
+    double v[GRP], pv[GRP];
+    if (x0 < a.V) {
+      group_weights<Elem>(r, tg, dg, kept_mask<Elem>(r, tg, bm_group(sh.bm, x0 - s0)), sh.etab, v, pv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < GRP; ++e) v[e] = pv[e] = 0.0;
+    }
     double lsum = 0.0;
 #pragma unroll
     for (int e = 0; e < GRP; ++e) {
-      v[e] = 0.0;
-      if (x0 + e < a.V) {
-        double w, p;
-        pair_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f,
-                    bm_test(bm, x0 - s0 + e), w, p);
-        v[e] = use_p ? p : w;
-      }
+      if (use_p) v[e] = pv[e];
       lsum += v[e];
     }
     double ctot;
-    const double cb = block_excl_scan<DR_THREADS>(lsum, scr, &ctot);
+    const double cb = block_excl_scan<DR_THREADS>(lsum, sh.scr, &ctot);
     const int xc = block_min<DR_THREADS>((lsum > 0.0 && cb + lsum >= tl) ? tid : DR_THREADS,
-                                         (int*)scr);
-    const int xl = block_max<DR_THREADS>(lsum > 0.0 ? tid : -1, (int*)scr);
+                                         (int*)sh.scr);
+    const int xl = block_max<DR_THREADS>(lsum > 0.0 ? tid : -1, (int*)sh.scr);
     const int who = xc < DR_THREADS ? xc : xl;   // a sub-chunk chosen here has weight
-    if (tid == 0) sel_x = -1;
+    if (tid == 0) sh.sel_x = -1;
     __syncthreads();
     if (tid == who) {
       double run = cb;
@@ -452,23 +496,25 @@ __global__ __launch_bounds__(DR_THREADS) void residual_select_kernel(DrawArgs a)
         }
         run += v[e];
       }
-      sel_x = pick;
+      sh.sel_x = pick;
     }
     __syncthreads();
-    token = sel_x;
+    token = sh.sel_x;
   }
+  int32_t* ot = a.out_tokens + (int64_t)b * G1;
+  if (tid < G1) ot[tid] = tid < n ? wk.x : (tid == n ? token : -1);
   if (tid == 0) {
-    a.out_tokens[(int64_t)b * G1 + n] = token;
-    for (int j = n + 1; j < G1; ++j) a.out_tokens[(int64_t)b * G1 + j] = -1;
+    a.out_num_accepted[b] = n;
     if (a.out_flags) a.out_flags[b] = flags;
   }
 }
 
-int launch_residual_select(const DrawArgs& a, int B, hipStream_t st) {
+int launch_draw(const DrawArgs& a, int B, hipStream_t st) {
+  const dim3 grid((unsigned)(a.nwg * B));
   if (a.bf16)
-    hipLaunchKernelGGL(residual_select_kernel<uint16_t>, dim3(B), dim3(DR_THREADS), 0, st, a);
+    hipLaunchKernelGGL(draw_kernel<uint16_t>, grid, dim3(DR_THREADS), 0, st, a);
   else
-    hipLaunchKernelGGL(residual_select_kernel<float>, dim3(B), dim3(DR_THREADS), 0, st, a);
+    hipLaunchKernelGGL(draw_kernel<float>, grid, dim3(DR_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

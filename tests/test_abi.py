@@ -52,7 +52,7 @@ def test_workspace_bytes(lib):
     ws = lib.spec_verify_workspace_bytes
     a = ws(128, 8, 151936, 64)
     assert a > 0 and a % 256 == 0
-    assert ws(128, 8, 151936, 0) < a
+    assert ws(128, 8, 151936, 0) == a    # ban lists are read in place
     assert ws(1, 4, 1000, 0) > 0
     for bad in [(0, 4, 10, 0), (1, 0, 10, 0), (1, 64, 10, 0), (1, 4, 0, 0), (1, 4, 10, -1),
                 (1, 4, 10, 2049), (2**30, 63, 10, 0)]:
