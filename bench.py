@@ -19,7 +19,6 @@ the float64 oracle on a bounded sample of the same workload on one host core.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -53,16 +52,6 @@ def workload_label(cfg):
             f"T={cfg.temperature} {t}")
 
 
-def source_digest():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "lossless_draft_verification_sample_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode())
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_record(kernel, workload):
     """Counter-measured HBM bytes per launch, if taken on the current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -71,6 +60,7 @@ def traffic_record(kernel, workload):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get(f"{kernel}/{workload}")
+    from lossless_draft_verification_sample_amd.rocprof_summary import source_digest
     if not ent or ent.get("source_digest") != source_digest():
         return None
     return ent.get("bytes_per_launch")
