@@ -51,9 +51,9 @@ namespace sv {
 #define SV_RS_THREADS 512
 #endif
 #ifndef SV_RS_UNROLL
-#define SV_RS_UNROLL 4
+#define SV_RS_UNROLL 8
 #endif
-// One workgroup per row; each thread keeps four 16-byte loads in flight.
+// One workgroup per row; each thread keeps eight 16-byte loads in flight.
 constexpr int RS_THREADS = SV_RS_THREADS;
 constexpr int RS_UNROLL = SV_RS_UNROLL;
 

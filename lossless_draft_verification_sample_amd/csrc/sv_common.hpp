@@ -258,4 +258,57 @@ __device__ __forceinline__ T block_excl_scan(T v, T* scratch, T* total) {
   return before + incl - v;
 }
 
+// Exclusive prefix sums over the block, in thread order, of two values at
+// once, with both totals. `scr` holds 2 * NT / WAVE doubles.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(double x, double y, double* scr, double& px,
+                                                 double& py, double& tx, double& ty) {
+  constexpr int NW = NT / WAVE;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  const auto add = [](double u, double v) { return u + v; };
+  const double ix = wave_scan_dpp(x, 0.0, add), iy = wave_scan_dpp(y, 0.0, add);
+  __syncthreads();
+  if (lane == WAVE - 1) {
+    scr[w] = ix;
+    scr[NW + w] = iy;
+  }
+  __syncthreads();
+  double bx = 0.0, by = 0.0, ax = 0.0, ay = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if (i < w) {
+      bx += scr[i];
+      by += scr[NW + i];
+    }
+    ax += scr[i];
+    ay += scr[NW + i];
+  }
+  px = bx + ix - x;
+  py = by + iy - y;
+  tx = ax;
+  ty = ay;
+}
+
+// Lowest thread index whose `f` holds (NT if none) and highest whose `l` holds
+// (-1 if none), for the whole block. `scr` holds 2 * NT / WAVE ints.
+template <int NT>
+__device__ __forceinline__ void block_first_last(bool f, bool l, int* scr, int& first, int& last) {
+  constexpr int NW = NT / WAVE;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  const uint64_t bf = __ballot(f), bl = __ballot(l);
+  __syncthreads();
+  if (lane == 0) {
+    scr[w] = bf ? w * WAVE + __ffsll((unsigned long long)bf) - 1 : NT;
+    scr[NW + w] = bl ? w * WAVE + 63 - __clzll((long long)bl) : -1;
+  }
+  __syncthreads();
+  first = NT;
+  last = -1;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    first = scr[i] < first ? scr[i] : first;
+    last = scr[NW + i] > last ? scr[NW + i] : last;
+  }
+}
+
 }  // namespace sv

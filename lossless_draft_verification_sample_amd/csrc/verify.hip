@@ -155,18 +155,35 @@ __device__ __forceinline__ uint32_t kept_mask(const DrawRow& r, const Group<Elem
   return m;
 }
 
-// Per-token draw weights of a group (0 outside the kept mask).
+// Sums of w and p over the kept tokens of a group.
 template <typename Elem>
-__device__ __forceinline__ void group_weights(const DrawRow& r, const Group<Elem>& tg,
-                                              const Group<Elem>& dg, uint32_t km,
-                                              const double* tab, double (&w)[GRP],
-                                              double (&p)[GRP]) {
+__device__ __forceinline__ void group_sums(const DrawRow& r, const Group<Elem>& tg,
+                                           const Group<Elem>& dg, uint32_t km, const double* tab,
+                                           double& sw, double& sp) {
 #pragma unroll
   for (int e = 0; e < GRP; ++e) {
-    w[e] = 0.0;
-    p[e] = 0.0;
-    if ((km >> e) & 1u)
-      tok_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab, w[e], p[e]);
+    if ((km >> e) & 1u) {
+      double w, p;
+      tok_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab, w, p);
+      sw += w;
+      sp += p;
+    }
+  }
+}
+
+// Per-token draw weights of a group: w, or p when `use_p` (0 outside the mask).
+template <typename Elem>
+__device__ __forceinline__ void group_values(const DrawRow& r, const Group<Elem>& tg,
+                                             const Group<Elem>& dg, uint32_t km, const double* tab,
+                                             bool use_p, double (&v)[GRP]) {
+#pragma unroll
+  for (int e = 0; e < GRP; ++e) {
+    v[e] = 0.0;
+    if ((km >> e) & 1u) {
+      double w, p;
+      tok_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab, w, p);
+      v[e] = use_p ? p : w;
+    }
   }
 }
 
@@ -259,7 +276,8 @@ struct DrawShared {
   uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
   double w[DRAW_SPW_MAX];
   double p[DRAW_SPW_MAX];
-  double scr[DR_NW];
+  double scr[2 * DR_NW];
+  int32_t iscr[2 * DR_NW];
   int32_t last;
   int32_t sel_sub, sel_x;
   double sel_before;
@@ -281,7 +299,10 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   exp_table_fill(sh.etab);
   const Walk wk = accept_walk(a, b);
   const DrawRow r = draw_row(a, b, wk.n);
-  mark_bans(sh.bm, nsl * DRAW_SUB, bl, nb, ban0, tok0, a.V);   // also publishes etab
+  if (nb > 0)
+    mark_bans(sh.bm, nsl * DRAW_SUB, bl, nb, ban0, tok0, a.V);   // also publishes etab
+  else
+    __syncthreads();                                               // publishes etab
 
   // Weight sums of the workgroup's sub-chunks: wave wv owns sub-chunks wv,
   // wv + DR_NW, ...; lane l reads groups l, l + 64, l + 128, l + 192 of a
@@ -292,41 +313,31 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   // evaluates the k-th one (one dense pass instead of divergent ones). A wave
   // with more kept tokens than lanes evaluates them in place.
   const bool sparse = r.ts.tau > -INFINITY;
-  for (int sl = wv; sl < nsl; sl += DR_NW) {
-    const int sbase = tok0 + sl * DRAW_SUB;
-    Group<Elem> tg[GPL], dg[GPL];
+  // the kept tokens of the wave's groups of one sub-chunk, and their number
+  auto sub_mask = [&](int sbase, const Group<Elem>(&tg)[GPL], uint32_t(&km)[GPL]) {
+    uint32_t cnt = 0u;
 #pragma unroll
     for (int k = 0; k < GPL; ++k) {
       const int x0 = sbase + (lane + k * WAVE) * GRP;
-      if (x0 < a.V) {
-        load_group<Elem>(r.trow, x0, a.V, a.vec, tg[k]);
-        if (r.drow && !sparse) load_group<Elem>(r.drow, x0, a.V, a.vec, dg[k]);
-      }
-    }
-    uint32_t km[GPL], cnt = 0u;
-#pragma unroll
-    for (int k = 0; k < GPL; ++k) {
-      const int x0 = sbase + (lane + k * WAVE) * GRP;
-      km[k] = x0 < a.V ? kept_mask<Elem>(r, tg[k], bm_group(sh.bm, x0 - tok0)) : 0u;
+      km[k] = x0 < a.V ? kept_mask<Elem>(r, tg[k], nb > 0 ? bm_group(sh.bm, x0 - tok0) : 0u) : 0u;
       cnt += (uint32_t)__popc(km[k]);
     }
-    if (r.drow && sparse) {
-#pragma unroll
-      for (int k = 0; k < GPL; ++k)
-        if (km[k]) load_group<Elem>(r.drow, sbase + (lane + k * WAVE) * GRP, a.V, a.vec, dg[k]);
-    }
-    double sw = 0.0, sp = 0.0;
+    return cnt;
+  };
+  // sums of those kept tokens, added to sw and sp
+  auto sub_sums = [&](int sbase, const Group<Elem>(&tg)[GPL], const Group<Elem>(&dg)[GPL],
+                      const uint32_t(&km)[GPL], uint32_t cnt, double& sw, double& sp) {
     const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
     const uint32_t total = lane63(incl);
+    if (total == 0u) return;
     if (total <= (uint32_t)WAVE) {
-      if (total) {
-        uint32_t pos = incl - cnt;
+      uint32_t pos = incl - cnt;
 #pragma unroll
-        for (int k = 0; k < GPL; ++k) {
-          uint32_t mm = km[k];
-          while (mm) {
-            const int e = __ffs(mm) - 1;
-            mm &= mm - 1u;
+      for (int k = 0; k < GPL; ++k) {
+        if (!km[k]) continue;
+#pragma unroll
+        for (int e = 0; e < GRP; ++e) {   // static token index: the group stays in registers
+          if ((km[k] >> e) & 1u) {
             KeptTok t;
             t.x = sbase + (lane + k * WAVE) * GRP + e;
             t.zt = group_val<Elem>(tg[k], e);
@@ -335,37 +346,57 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
             sh.kt[wv][pos++] = t;
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if ((uint32_t)lane < total) {
-          const KeptTok t = sh.kt[wv][lane];
-          tok_weight(r, t.zt, t.zd, sh.etab, sw, sp);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if ((uint32_t)lane < total) {
+        const KeptTok t = sh.kt[wv][lane];
+        double w, p;
+        tok_weight(r, t.zt, t.zd, sh.etab, w, p);
+        sw += w;
+        sp += p;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     } else {
 #pragma unroll
-      for (int k = 0; k < GPL; ++k) {
-        if (km[k]) {
-          double w[GRP], p[GRP];
-          group_weights<Elem>(r, tg[k], dg[k], km[k], sh.etab, w, p);
-#pragma unroll
-          for (int e = 0; e < GRP; ++e) {
-            sw += w[e];
-            sp += p[e];
-          }
-        }
-      }
+      for (int k = 0; k < GPL; ++k)
+        if (km[k]) group_sums<Elem>(r, tg[k], dg[k], km[k], sh.etab, sw, sp);
     }
+  };
+  auto load_sub = [&](int sbase, Group<Elem>(&g)[GPL], const void* row) {
+#pragma unroll
+    for (int k = 0; k < GPL; ++k) {
+      const int x0 = sbase + (lane + k * WAVE) * GRP;
+      if (x0 < a.V) load_group<Elem>(row, x0, a.V, a.vec, g[k]);
+    }
+  };
+  auto publish = [&](int sl, double sw, double sp) {
     sw = wave_total(sw);
     sp = wave_total(sp);
     if (lane == 0) {
       sh.w[sl] = sw;
       sh.p[sl] = sp;
     }
+  };
+  for (int sl = wv; sl < nsl; sl += DR_NW) {
+    const int sbase = tok0 + sl * DRAW_SUB;
+    Group<Elem> tg[GPL], dg[GPL];
+    load_sub(sbase, tg, r.trow);
+    if (r.drow && !sparse) load_sub(sbase, dg, r.drow);
+    uint32_t km[GPL];
+    const uint32_t cnt = sub_mask(sbase, tg, km);
+    if (r.drow && sparse) {
+      // truncated target: draft groups only where a target token is kept
+#pragma unroll
+      for (int k = 0; k < GPL; ++k)
+        if (km[k]) load_group<Elem>(r.drow, sbase + (lane + k * WAVE) * GRP, a.V, a.vec, dg[k]);
+    }
+    double sw = 0.0, sp = 0.0;
+    sub_sums(sbase, tg, dg, km, cnt, sw, sp);
+    publish(sl, sw, sp);
   }
   __syncthreads();
   if (tid < nsl) {
@@ -392,13 +423,17 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   uint32_t flags = wk.flags;
   ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
   auto ld = [](double* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  double tw = 0.0, tp = 0.0;
-  for (int c = tid; c < a.nsub; c += DR_THREADS) {
-    tw += ld(&cs[c].w);
-    tp += ld(&cs[c].p);
+  // every thread sums a contiguous run of sub-chunks (w and p), read once;
+  // one block scan gives the prefixes before each run and both totals
+  const int per = (a.nsub + DR_THREADS - 1) / DR_THREADS;
+  const int k0 = tid * per, k1 = min(k0 + per, a.nsub);
+  double lw = 0.0, lp = 0.0;
+  for (int c = k0; c < k1; ++c) {
+    lw += ld(&cs[c].w);
+    lp += ld(&cs[c].p);
   }
-  tw = block_sum<DR_THREADS>(tw, sh.scr);
-  tp = block_sum<DR_THREADS>(tp, sh.scr);
+  double bw, bp, tw, tp;
+  block_excl_scan2<DR_THREADS>(lw, lp, sh.scr, bw, bp, tw, tp);
   // fall back to p when the residual has no mass
   bool use_p = false;
   double S = tw;
@@ -412,46 +447,30 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
     flags |= FLAG_EMPTY;
   } else {
     const double t = wk.u_final * S;
-    // sub-chunk holding t: per-thread contiguous runs, a block scan, and the
-    // first thread whose run reaches t searches its run
-    const int per = (a.nsub + DR_THREADS - 1) / DR_THREADS;
-    const int k0 = tid * per;
-    double loc = 0.0;
-    for (int c = k0; c < k0 + per && c < a.nsub; ++c) loc += ld(use_p ? &cs[c].p : &cs[c].w);
-    double tot;
-    const double before = block_excl_scan<DR_THREADS>(loc, sh.scr, &tot);
-    const int cand = block_min<DR_THREADS>((loc > 0.0 && before + loc >= t) ? tid : DR_THREADS,
-                                           (int*)sh.scr);
-    if (tid == 0) {
-      sh.sel_sub = -1;
-      sh.sel_before = 0.0;
-    }
-    __syncthreads();
-    if (tid == cand) {
+    // the sub-chunk holding t: the first thread whose run reaches t searches its
+    // run; when rounding leaves t above every prefix, the last sub-chunk with
+    // weight is taken
+    const double loc = use_p ? lp : lw, before = use_p ? bp : bw;
+    int cand, lastw;
+    block_first_last<DR_THREADS>(loc > 0.0 && before + loc >= t, loc > 0.0, sh.iscr, cand, lastw);
+    const int who = cand < DR_THREADS ? cand : lastw;
+    if (tid == who) {
       double run = before;
-      for (int c = k0; c < k0 + per && c < a.nsub; ++c) {
+      int sel = -1;
+      double selb = 0.0;
+      for (int c = k0; c < k1; ++c) {
         const double v = ld(use_p ? &cs[c].p : &cs[c].w);
         if (v > 0.0) {
-          sh.sel_sub = c;           // the last sub-chunk with weight unless one reaches t
-          sh.sel_before = run;
+          sel = c;                  // the last sub-chunk with weight unless one reaches t
+          selb = run;
           if (run + v >= t) break;
         }
         run += v;
       }
+      sh.sel_sub = sel;
+      sh.sel_before = selb;
     }
-    __syncthreads();
-    if (sh.sel_sub < 0 && tid == 0) {
-      // t above every prefix through rounding: the last sub-chunk with weight
-      double run = 0.0;
-      for (int c = 0; c < a.nsub; ++c) {
-        const double v = ld(use_p ? &cs[c].p : &cs[c].w);
-        if (v > 0.0) {
-          sh.sel_sub = c;
-          sh.sel_before = run;
-        }
-        run += v;
-      }
-    }
+    if (who < 0 && tid == 0) sh.sel_sub = -1;
     __syncthreads();
   }
   if (S > 0.0 && sh.sel_sub < 0) flags |= FLAG_EMPTY;   // no sub-chunk with weight
@@ -464,29 +483,19 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
       load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
       if (r.drow) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
     }
-    mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
-    double v[GRP], pv[GRP];
-    if (x0 < a.V) {
-      group_weights<Elem>(r, tg, dg, kept_mask<Elem>(r, tg, bm_group(sh.bm, x0 - s0)), sh.etab, v, pv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < GRP; ++e) v[e] = pv[e] = 0.0;
-    }
+    if (nb > 0) mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
+    double v[GRP];
+    const uint32_t km = x0 < a.V ? kept_mask<Elem>(r, tg, nb > 0 ? bm_group(sh.bm, x0 - s0) : 0u) : 0u;
+    group_values<Elem>(r, tg, dg, km, sh.etab, use_p, v);
     double lsum = 0.0;
 #pragma unroll
-    for (int e = 0; e < GRP; ++e) {
-      if (use_p) v[e] = pv[e];
-      lsum += v[e];
-    }
-    double ctot;
-    const double cb = block_excl_scan<DR_THREADS>(lsum, sh.scr, &ctot);
-    const int xc = block_min<DR_THREADS>((lsum > 0.0 && cb + lsum >= tl) ? tid : DR_THREADS,
-                                         (int*)sh.scr);
-    const int xl = block_max<DR_THREADS>(lsum > 0.0 ? tid : -1, (int*)sh.scr);
-    const int who = xc < DR_THREADS ? xc : xl;   // a sub-chunk chosen here has weight
-    if (tid == 0) sh.sel_x = -1;
-    __syncthreads();
-    if (tid == who) {
+    for (int e = 0; e < GRP; ++e) lsum += v[e];
+    double cb, dummy, ctot, dtot;
+    block_excl_scan2<DR_THREADS>(lsum, 0.0, sh.scr, cb, dummy, ctot, dtot);
+    int xc, xl;
+    block_first_last<DR_THREADS>(lsum > 0.0 && cb + lsum >= tl, lsum > 0.0, sh.iscr, xc, xl);
+    const int whot = xc < DR_THREADS ? xc : xl;   // a sub-chunk chosen here has weight
+    if (tid == whot) {
       double run = cb;
       int pick = -1;
       for (int e = 0; e < GRP; ++e) {
@@ -498,6 +507,7 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
       }
       sh.sel_x = pick;
     }
+    if (whot < 0 && tid == 0) sh.sel_x = -1;
     __syncthreads();
     token = sh.sel_x;
   }
