@@ -51,7 +51,7 @@ def short_name(name):
     return n
 
 
-def stats(run_dir, out_path, command):
+def stats(run_dir, out_path, command, tail=200):
     path = _one(os.path.join(run_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     lines = [
@@ -71,6 +71,20 @@ def stats(run_dir, out_path, command):
             f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
             f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
             f"{float(r['Percentage']):.1f}% |")
+    # steady state: the last `tail` dispatches of each kernel (the GPU's first
+    # ~150 calls run at lower clocks)
+    trace = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if trace:
+        per = {}
+        for r in csv.DictReader(open(trace[0])):
+            per.setdefault(short_name(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", f"Steady state, last {tail} dispatches of each kernel (from the kernel trace):", "",
+                  "| kernel | dispatches | average (us) | median (us) |", "|---|---:|---:|---:|"]
+        for name, v in per.items():
+            d = [x[1] for x in sorted(v)][-tail:]
+            lines.append(f"| {name} | {len(d)} | {statistics.mean(d) / 1e3:.1f} | "
+                         f"{statistics.median(d) / 1e3:.1f} |")
     lines += ["", f"Kernel sources digest: `{source_digest()}`", ""]
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
