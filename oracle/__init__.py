@@ -15,11 +15,22 @@ Parity status of each function (what pins it to something other than itself):
                      Monte Carlo; chi-square of emitted tokens against p.
   verify_greedy      pinned: brute-force loop over small rows.
   first_token_law    pinned: the worked example's printed numbers.
+  diagnostics        per-position overlap 1 - TV, accepted-prefix histogram,
+                     conditional acceptance, accepted-length law; each pin is
+                     listed in oracle/diagnostics.py.
 Parity unpinned (fixed by convention only, not by anything the pages print):
 the uniform layout, the tie rules of top-k, top-p and greedy, and the actual
 numbers of the alpha = 0.8 example (only its invariants are printed).
 """
 
+from . import diagnostics  # noqa: F401
+from .diagnostics import (  # noqa: F401
+    accepted_prefix_histogram,
+    conditional_acceptance,
+    overlap,
+    position_overlaps,
+    prefix_length_law,
+)
 from .philox import philox4x64_10, uniform, uniforms, word_to_uniform  # noqa: F401
 from .verifier import (  # noqa: F401
     BOUNDARY_EPS,
