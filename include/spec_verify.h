@@ -118,6 +118,23 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
  *   out_target_lse   [B][gamma+1] float log-normaliser of each tempered target
  *                    row over its kept set (-inf if empty), or NULL.
  *   out_draft_lse    [B][gamma] float, same for the draft rows, or NULL.
+ *   out_overlap      [B][gamma] double, or NULL (then not computed): the overlap
+ *                    sum_x min(p_i(x), q_i(x)) = 1 - TV(p_i, q_i) of target row
+ *                    i and draft row i after every sampler transform; with x_i
+ *                    drawn from q_i it is the probability that proposal i is
+ *                    accepted once the walk reaches it ("Drafters and
+ *                    Speculative Decoding", sections "Confidence and
+ *                    verification admission" and "Accepted length is not
+ *                    speed"). 0 when either row is empty; unspecified for a
+ *                    request flagged SV_FLAG_NONFINITE. Computing it reads the
+ *                    rows 0..gamma-1 once more (only the kept groups of the
+ *                    other row when one of the two is truncated).
+ *   out_accept_hist  [gamma+1] uint32, or NULL: out_accept_hist[n] = number of
+ *                    requests of this call with n accepted proposals (an
+ *                    accepted-prefix histogram, same page, section "Read the
+ *                    benchmark contract"). Overwritten by each call. Requests
+ *                    that reached position i number sum_{n >= i} hist[n], and
+ *                    sum_{n > i} hist[n] of them accepted it.
  *   workspace        device scratch of at least spec_verify_workspace_bytes(...)
  *                    bytes, 256-byte aligned.
  * Limits: 1 <= B, 1 <= gamma <= 63, 1 <= V < 2^31, B*(2*gamma+1) < 2^31,
@@ -128,6 +145,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
                        sv_sampler target, sv_sampler draft, uint64_t seed, uint64_t offset,
                        const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
                        uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
+                       double* out_overlap, uint32_t* out_accept_hist,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Greedy verification ("Drafters and Speculative Decoding", section "Greedy
@@ -137,11 +155,14 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
  * appended. Needs no workspace: out_tokens doubles as scratch.
  *   target_logits [B][gamma+1][V], draft_tokens [B][gamma];
  *   out_tokens [B][gamma+1] (n matches, argmax, then -1), out_num_accepted [B],
- *   out_flags [B] or NULL (SV_FLAG_TOKEN_RANGE, SV_FLAG_NONFINITE).
+ *   out_flags [B] or NULL (SV_FLAG_TOKEN_RANGE, SV_FLAG_NONFINITE),
+ *   out_accept_hist [gamma+1] or NULL: accepted-prefix histogram of the call,
+ *   as for spec_verify_sample.
  * NaN logits are ignored by the argmax and flagged. */
 int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,
                        int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
-                       int32_t* out_num_accepted, uint32_t* out_flags, void* stream);
+                       int32_t* out_num_accepted, uint32_t* out_flags,
+                       uint32_t* out_accept_hist, void* stream);
 
 /* Static description of a status code. */
 const char* spec_verify_strerror(int status);
@@ -156,7 +177,8 @@ const char* spec_verify_strerror(int status);
 #define SV_K_DRAW 1
 #define SV_K_GREEDY_ARGMAX 2
 #define SV_K_GREEDY_SCAN 3
-#define SV_NUM_KERNELS 4
+#define SV_K_OVERLAP 4
+#define SV_NUM_KERNELS 5
 int spec_verify_profile_start(int32_t max_launches_per_kernel);
 int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 

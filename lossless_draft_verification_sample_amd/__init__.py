@@ -28,8 +28,10 @@ from ._lib import (  # noqa: F401
     SvSampler,
 )
 
-SampleOut = namedtuple("SampleOut", "tokens num_accepted flags target_lse draft_lse")
-GreedyOut = namedtuple("GreedyOut", "tokens num_accepted flags")
+SampleOut = namedtuple("SampleOut",
+                       "tokens num_accepted flags target_lse draft_lse overlap accept_hist",
+                       defaults=(None, None))
+GreedyOut = namedtuple("GreedyOut", "tokens num_accepted flags accept_hist", defaults=(None,))
 
 
 class SpecVerifyError(RuntimeError):
@@ -64,6 +66,13 @@ def _dev_ptr(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _checked(t, name, dtype, shape):
+    """Device pointer of an optional output whose shape the library assumes."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return _dev_ptr(t, name, dtype)
+
+
 def _sampler(s):
     if isinstance(s, SvSampler):
         return s
@@ -91,14 +100,19 @@ def spec_verify_workspace_bytes(B, gamma, V, n_banned=0):
 
 def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler=(1.0, 0, 1.0),
                        draft_sampler=(1.0, 0, 1.0), banned_ids=None, seed=0, offset=0,
-                       uniforms=None, want_lse=True, workspace=None, out=None, stream=None):
+                       uniforms=None, want_lse=True, want_overlap=False, want_hist=False,
+                       workspace=None, out=None, stream=None):
     """Speculative-sampling verification of a batch (see include/spec_verify.h).
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (bf16 or fp32),
     draft_tokens [B, gamma] int32, banned_ids [B, n] int32 or None,
     uniforms [B, gamma+1] float64 or None (then Philox(seed, offset)).
     Samplers are (temperature, top_k, top_p) tuples, dicts or SvSampler.
-    Returns SampleOut(tokens, num_accepted, flags, target_lse, draft_lse).
+    want_overlap adds the per-position overlaps [B, gamma] (float64; one more
+    read of the rows), want_hist the accepted-prefix histogram [gamma+1]
+    (int32 storage of the library's uint32 counts).
+    Returns SampleOut(tokens, num_accepted, flags, target_lse, draft_lse,
+    overlap, accept_hist).
     """
     torch = _torch()
     lib = _lib.load()
@@ -124,6 +138,8 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
             torch.empty((B,), dtype=torch.int32, device=dev),
             torch.empty((B, G1), dtype=torch.float32, device=dev) if want_lse else None,
             torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_lse else None,
+            torch.empty((B, gamma), dtype=torch.float64, device=dev) if want_overlap else None,
+            torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None,
         )
     need = lib.spec_verify_workspace_bytes(B, gamma, V, n_banned)
     if workspace is None:
@@ -139,6 +155,8 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
         _dev_ptr(out.flags, "out_flags", torch.int32),
         _dev_ptr(out.target_lse, "out_target_lse", torch.float32),
         _dev_ptr(out.draft_lse, "out_draft_lse", torch.float32),
+        _checked(out.overlap, "out_overlap", torch.float64, (B, gamma)),
+        _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)),
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_handle(stream))
     if rc != SV_OK:
@@ -146,8 +164,9 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
     return out
 
 
-def spec_verify_greedy(target_logits, draft_tokens, out=None, stream=None):
-    """Greedy verification (see include/spec_verify.h). Returns GreedyOut."""
+def spec_verify_greedy(target_logits, draft_tokens, want_hist=False, out=None, stream=None):
+    """Greedy verification (see include/spec_verify.h). Returns
+    GreedyOut(tokens, num_accepted, flags, accept_hist)."""
     torch = _torch()
     lib = _lib.load()
     B, G1, V = target_logits.shape
@@ -159,13 +178,15 @@ def spec_verify_greedy(target_logits, draft_tokens, out=None, stream=None):
     if out is None:
         out = GreedyOut(torch.empty((B, G1), dtype=torch.int32, device=dev),
                         torch.empty((B,), dtype=torch.int32, device=dev),
-                        torch.empty((B,), dtype=torch.int32, device=dev))
+                        torch.empty((B,), dtype=torch.int32, device=dev),
+                        torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None)
     rc = lib.spec_verify_greedy(
         _dev_ptr(target_logits, "target_logits"), dt,
         _dev_ptr(draft_tokens, "draft_tokens", torch.int32), B, gamma, V,
         _dev_ptr(out.tokens, "out_tokens", torch.int32),
         _dev_ptr(out.num_accepted, "out_num_accepted", torch.int32),
-        _dev_ptr(out.flags, "out_flags", torch.int32), _stream_handle(stream))
+        _dev_ptr(out.flags, "out_flags", torch.int32),
+        _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)), _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_greedy")
     return out

@@ -32,8 +32,9 @@ SV_K_ROW_STATS = 0
 SV_K_DRAW = 1
 SV_K_GREEDY_ARGMAX = 2
 SV_K_GREEDY_SCAN = 3
-SV_NUM_KERNELS = 4
-KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan"]
+SV_K_OVERLAP = 4
+SV_NUM_KERNELS = 5
+KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap"]
 
 
 class SvSampler(ctypes.Structure):
@@ -50,8 +51,9 @@ SIGNATURES = {
     "spec_verify_workspace_bytes": (_c.c_size_t, [_i32, _i32, _i32, _i32]),
     "spec_verify_sample": (_c.c_int, [
         _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
-        _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]),
-    "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+        _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]),
+    "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                      _vp]),
     "spec_verify_strerror": (_c.c_char_p, [_c.c_int]),
     "spec_verify_profile_start": (_c.c_int, [_i32]),
     "spec_verify_profile_stop": (_c.c_int, [_vp, _vp]),

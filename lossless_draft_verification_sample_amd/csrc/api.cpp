@@ -19,8 +19,9 @@ constexpr size_t WS_ALIGN = 256;
 size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
-  size_t stats, sums, tickets, total;
+  size_t stats, sums, tickets, ov_partial, ov_tickets, total;
   int nsub, spw, nwg;
+  int ov_spp, ov_parts;
 };
 
 bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
@@ -37,9 +38,21 @@ bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
   if (spw > sv::DRAW_SPW_MAX) spw = sv::DRAW_SPW_MAX;
   nwg = (nsub + spw - 1) / spw;
   if ((int64_t)B * nwg >= INT32_MAX) return false;
+  // overlap workgroups: about OV_TARGET_WGS in total, each over at most
+  // OV_SPW_MAX sub-chunks of one (request, position) pair
+  const int64_t pairs = (int64_t)B * gamma;
+  int64_t parts = (sv::OV_TARGET_WGS + pairs - 1) / pairs;
+  const int64_t min_parts = (nsub + sv::OV_SPW_MAX - 1) / sv::OV_SPW_MAX;
+  if (parts < min_parts) parts = min_parts;
+  if (parts > nsub) parts = nsub;
+  const int64_t spp = (nsub + parts - 1) / parts;
+  parts = (nsub + spp - 1) / spp;
+  if (pairs * parts >= INT32_MAX) return false;
   L->nsub = (int)nsub;
   L->spw = (int)spw;
   L->nwg = (int)nwg;
+  L->ov_spp = (int)spp;
+  L->ov_parts = (int)parts;
   size_t off = 0;
   L->stats = off;
   off = align_up(off + (size_t)rows * sizeof(sv::RowStat));
@@ -47,6 +60,10 @@ bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
   off = align_up(off + (size_t)B * (size_t)nsub * sizeof(sv::ChunkSums));
   L->tickets = off;
   off = align_up(off + (size_t)B * sizeof(int32_t));
+  L->ov_partial = off;
+  off = align_up(off + (size_t)pairs * (size_t)parts * sizeof(double));
+  L->ov_tickets = off;
+  off = align_up(off + (size_t)pairs * sizeof(int32_t));
   L->total = off;
   return true;
 }
@@ -122,6 +139,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
                        sv_sampler target, sv_sampler draft, uint64_t seed, uint64_t offset,
                        const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
                        uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
+                       double* out_overlap, uint32_t* out_accept_hist,
                        void* workspace, size_t workspace_bytes, void* stream) {
   if (!target_logits || !draft_logits || !draft_tokens || !out_tokens || !out_num_accepted)
     return SV_EINVAL;
@@ -141,6 +159,8 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
   sv::RowStat* stats = (sv::RowStat*)(ws + L.stats);
   sv::ChunkSums* sums = (sv::ChunkSums*)(ws + L.sums);
   int32_t* tickets = (int32_t*)(ws + L.tickets);
+  double* ov_partial = (double*)(ws + L.ov_partial);
+  int32_t* ov_tickets = (int32_t*)(ws + L.ov_tickets);
   const int bf16 = dtype == SV_BF16;
   const int rows = B * (2 * gamma + 1);
   const int32_t* bans = n_banned ? banned_ids : nullptr;
@@ -158,6 +178,8 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.n_banned = n_banned;
     a.stats = stats;
     a.tickets = tickets;
+    a.ov_tickets = out_overlap ? ov_tickets : nullptr;
+    a.accept_hist = out_accept_hist;
     a.out_tlse = out_target_lse;
     a.out_dlse = out_draft_lse;
     a.force_generic = 0;
@@ -190,15 +212,39 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.out_tokens = out_tokens;
     a.out_num_accepted = out_num_accepted;
     a.out_flags = out_flags;
+    a.accept_hist = out_accept_hist;
     ProfScope p(SV_K_DRAW, st);
     if (sv::launch_draw(a, B, st)) return SV_EHIP;
+  }
+  if (out_overlap) {
+    sv::OverlapArgs a{};
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.vec = ((uintptr_t)target_logits % 16 == 0) && ((uintptr_t)draft_logits % 16 == 0) &&
+            ((size_t)V * es) % 16 == 0;
+    a.gamma = gamma;
+    a.V = V;
+    a.nsub = L.nsub;
+    a.spp = L.ov_spp;
+    a.parts = L.ov_parts;
+    a.t_temp = target.temperature;
+    a.d_temp = draft.temperature;
+    a.banned = bans;
+    a.n_banned = n_banned;
+    a.stats = stats;
+    a.partial = ov_partial;
+    a.tickets = ov_tickets;
+    a.out_overlap = out_overlap;
+    ProfScope p(SV_K_OVERLAP, st);
+    if (sv::launch_overlap(a, bf16, B * gamma, st)) return SV_EHIP;
   }
   return SV_OK;
 }
 
 int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,
                        int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
-                       int32_t* out_num_accepted, uint32_t* out_flags, void* stream) {
+                       int32_t* out_num_accepted, uint32_t* out_flags,
+                       uint32_t* out_accept_hist, void* stream) {
   if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
   if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return SV_EINVAL;
@@ -207,7 +253,7 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
   if ((int64_t)B * (gamma + 1) >= INT32_MAX) return SV_ESIZE;
   hipStream_t st = (hipStream_t)stream;
   sv::GreedyArgs a{target_logits, dtype == SV_BF16, gamma, V, B, draft_tokens,
-                   out_tokens, out_num_accepted, out_flags};
+                   out_tokens, out_num_accepted, out_flags, out_accept_hist};
   {
     ProfScope p(SV_K_GREEDY_ARGMAX, st);
     if (sv::launch_greedy_argmax(a, st)) return SV_EHIP;

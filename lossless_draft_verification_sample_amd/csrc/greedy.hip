@@ -147,6 +147,7 @@ __global__ __launch_bounds__(GA_THREADS) void greedy_argmax_kernel(GreedyArgs a)
   }
   if (blk.i == INT32_MAX) blk.i = 0;   // only NaN: unspecified, flagged
   if (tid == 0) a.out_tokens[row] = blk.i | (int32_t)(nonfinite << 31);
+  if (row == 0 && a.accept_hist && tid <= a.gamma) a.accept_hist[tid] = 0u;
 }
 
 int launch_greedy_argmax(const GreedyArgs& a, hipStream_t st) {
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(WAVE) void greedy_scan_kernel(GreedyArgs a) {
   }
   a.out_num_accepted[b] = n;
   if (a.out_flags) a.out_flags[b] = flags;
+  if (a.accept_hist) atomicAdd(&a.accept_hist[n], 1u);
 }
 
 int launch_greedy_scan(const GreedyArgs& a, hipStream_t st) {

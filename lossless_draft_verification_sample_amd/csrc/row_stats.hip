@@ -767,6 +767,9 @@ void row_stats_kernel(RowStatsArgs a) {
     out.px = kept ? exp((double)zx / (double)s.temperature - out.lse) : 0.0;
     a.stats[row] = out;
     if (i == 0 && a.tickets) a.tickets[b] = 0;
+    if (i < a.gamma && a.ov_tickets) a.ov_tickets[(int64_t)b * a.gamma + i] = 0;
+    if (row == 0 && a.accept_hist)
+      for (int k = 0; k <= a.gamma; ++k) a.accept_hist[k] = 0u;
     if (is_target) {
       if (a.out_tlse) a.out_tlse[(int64_t)b * G1 + i] = (float)out.lse;
     } else {

@@ -15,6 +15,11 @@ constexpr int DRAW_SUB = 2048;
 constexpr int DRAW_SPW_MAX = 16;
 constexpr int DRAW_TARGET_WGS = 1024;   // about four draw workgroups per CU
 
+// Per-position overlap: every (request, position) pair is split into `parts`
+// workgroups of at most OV_SPW_MAX sub-chunks, about OV_TARGET_WGS in total.
+constexpr int OV_SPW_MAX = 64;
+constexpr int OV_TARGET_WGS = 2048;
+
 struct RowStatsArgs {
   const void* target;
   const void* draft;
@@ -25,6 +30,8 @@ struct RowStatsArgs {
   int n_banned;
   RowStat* stats;               // [B][2*gamma+1]: target rows 0..gamma, then draft rows
   int32_t* tickets;             // [B] draw-kernel arrival counters, zeroed here
+  int32_t* ov_tickets;          // [B][gamma] overlap arrival counters, zeroed here, or nullptr
+  uint32_t* accept_hist;        // [gamma+1] zeroed here, or nullptr
   float* out_tlse;
   float* out_dlse;
   int force_generic;
@@ -49,6 +56,22 @@ struct DrawArgs {
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   uint32_t* out_flags;
+  uint32_t* accept_hist;      // [gamma+1], zero on entry, or nullptr
+};
+
+struct OverlapArgs {
+  const void* target;
+  const void* draft;
+  int vec;                    // rows 16-byte aligned and V*size a multiple of 16
+  int gamma, V, nsub;
+  int spp, parts;             // sub-chunks per workgroup, workgroups per pair
+  float t_temp, d_temp;
+  const int32_t* banned;      // raw ban lists or nullptr
+  int n_banned;
+  const RowStat* stats;
+  double* partial;            // [B*gamma][parts] when parts > 1
+  int32_t* tickets;           // [B*gamma], zero on entry, when parts > 1
+  double* out_overlap;        // [B][gamma]
 };
 
 struct GreedyArgs {
@@ -59,10 +82,12 @@ struct GreedyArgs {
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   uint32_t* out_flags;
+  uint32_t* accept_hist;        // [gamma+1] or nullptr
 };
 
 int launch_row_stats(const RowStatsArgs& a, int dtype_bf16, int rows, hipStream_t s);
 int launch_draw(const DrawArgs& a, int B, hipStream_t s);
+int launch_overlap(const OverlapArgs& a, int bf16, int pairs, hipStream_t s);
 int launch_greedy_argmax(const GreedyArgs& a, hipStream_t s);
 int launch_greedy_scan(const GreedyArgs& a, hipStream_t s);
 

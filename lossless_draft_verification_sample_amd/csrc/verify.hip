@@ -21,22 +21,15 @@
 // the last workgroup of the request to finish (an arrival counter) locates the
 // sub-chunk holding u * S, rescans it and writes the request's outputs.
 
-#include "sv_common.hpp"
 #include "sv_launch.hpp"
+#include "sv_rowio.hpp"
 
 namespace sv {
 
 constexpr int DR_THREADS = 256;
 constexpr int DR_NW = DR_THREADS / WAVE;
-constexpr int GRP = 8;          // logits per thread per sub-chunk
 constexpr int GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
 static_assert(DRAW_SUB == DR_THREADS * GRP, "one group of GRP logits per thread per sub-chunk");
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bool is_kept(float z, const RowStat& s, bool banned) {
-  return !banned && !(s.flags & FLAG_EMPTY) && z > -INFINITY && z < INFINITY && z >= s.tau;
-}
 
 struct DrawRow {
   const void* trow;
@@ -63,70 +56,6 @@ __device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n) {
     r.drow = nullptr;
   }
   return r;
-}
-
-// Eight consecutive logits starting at x0, as raw bits (-inf beyond the row).
-template <typename Elem>
-struct Group {
-  u32x4 w[sizeof(Elem) == 2 ? 1 : 2];
-};
-
-template <typename Elem>
-__device__ __forceinline__ void load_group(const void* row, int x0, int V, bool vec, Group<Elem>& g) {
-  const Elem* e = (const Elem*)row;
-  if constexpr (sizeof(Elem) == 2) {
-    if (vec) {
-      g.w[0] = *(const u32x4*)(e + x0);   // V % 8 == 0 on this path
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = x0 + 2 * j < V ? (uint32_t)e[x0 + 2 * j] : 0xFF80u;
-        const uint32_t hi = x0 + 2 * j + 1 < V ? (uint32_t)e[x0 + 2 * j + 1] : 0xFF80u;
-        g.w[0][j] = lo | (hi << 16);
-      }
-    }
-  } else {
-    if (vec) {
-      const u32x4* p = (const u32x4*)(e + x0);
-      g.w[0] = p[0];                       // V % 4 == 0 on this path
-      g.w[1] = x0 + 4 < V ? p[1] : (u32x4)(0xFF800000u);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        g.w[j >> 2][j & 3] = x0 + j < V ? __float_as_uint(e[x0 + j]) : 0xFF800000u;
-    }
-  }
-}
-
-template <typename Elem>
-__device__ __forceinline__ float group_val(const Group<Elem>& g, int j) {
-  if constexpr (sizeof(Elem) == 2) return bf16_to_f32((g.w[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-  return __uint_as_float(g.w[j >> 2][j & 3]);
-}
-
-// exp(a) in fp64 for a <= about 0, table-driven (P. T. P. Tang, "Table-driven
-// implementation of the exponential function in IEEE floating-point
-// arithmetic", ACM TOMS 15(2), 1989): a = (256 k' + j) ln2 / 256 + r with
-// |r| <= ln2 / 512, so e^a = 2^k' * 2^(j/256) * e^r; 2^(j/256) comes from a
-// 256-entry LDS table and e^r - 1 from its degree-4 Taylor polynomial
-// (remainder below 4e-17 relative). Error a few ulp.
-__device__ __forceinline__ double exp_tab(double a, const double* tab) {
-  a = fmax(a, -1000.0);                                    // exp(-1000) is 0 in fp64
-  const double kf = rint(a * 0x1.71547652b82fep+8);        // 256 / ln2
-  double r = fma(-kf, 0x1.62e42fef80000p-9, a);            // head of ln2 / 256 (34 bits)
-  r = fma(-kf, 0x1.1cf79abc9e3b4p-44, r);                  // tail of ln2 / 256
-  double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-  q = fma(q, r, 0.5);
-  q = fma(q, r, 1.0);
-  q *= r;                                                  // e^r - 1
-  const int k = (int)kf;
-  const double t = tab[k & 255];
-  return ldexp(fma(t, q, t), k >> 8);
-}
-
-// The 2^(j/256) table of exp_tab, filled by the first 256 threads.
-__device__ __forceinline__ void exp_table_fill(double* tab) {
-  if (threadIdx.x < 256) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 256.0));
 }
 
 // Draw weight of one token whose target logit zt is kept: p(x), and
@@ -187,32 +116,6 @@ __device__ __forceinline__ void group_values(const DrawRow& r, const Group<Elem>
   }
 }
 
-// Marks the banned ids that fall in [c0, c0 + len) in an LDS bitmap of len / 32
-// words. The list is raw: ids outside [0, V) are padding and duplicates set the
-// same bit. `first` is element threadIdx.x of the list, loaded by the caller.
-__device__ __forceinline__ void mark_bans(uint32_t* bm, int len, const int32_t* bl, int nb,
-                                          int32_t first, int c0, int V) {
-  for (int k = threadIdx.x; k < len / 32; k += blockDim.x) bm[k] = 0u;
-  __syncthreads();
-  for (int j = threadIdx.x; j < nb; j += blockDim.x) {
-    const int32_t id = j == (int)threadIdx.x ? first : bl[j];
-    if (id >= c0 && id < V && id - c0 < len) {
-      const int o = id - c0;
-      atomicOr(&bm[o >> 5], 1u << (o & 31));
-    }
-  }
-  __syncthreads();
-}
-
-// Ban bits of the eight tokens at offset o (a multiple of 8) of the bitmap.
-__device__ __forceinline__ uint32_t bm_group(const uint32_t* bm, int o) {
-  return (bm[o >> 5] >> (o & 31)) & 0xFFu;
-}
-
-__device__ __forceinline__ double wave_total(double v) {
-  return lane63(wave_scan_dpp(v, 0.0, [](double x, double y) { return x + y; }));
-}
-
 // Outcome of the acceptance walk of one request, computed by every wave.
 struct Walk {
   int n;           // accepted proposals; the final token goes to slot n
@@ -262,13 +165,6 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b) {
   w.x = x;
   return w;
 }
-
-// A kept token of a wave's sub-chunk, queued for dense evaluation.
-struct alignas(16) KeptTok {
-  int32_t x;
-  float zt, zd;
-  int32_t pad;
-};
 
 struct DrawShared {
   double etab[256];
@@ -516,6 +412,7 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   if (tid == 0) {
     a.out_num_accepted[b] = n;
     if (a.out_flags) a.out_flags[b] = flags;
+    if (a.accept_hist) atomicAdd(&a.accept_hist[n], 1u);
   }
 }
 

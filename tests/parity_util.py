@@ -51,7 +51,7 @@ def stored_proposals(name):
 
 
 def run_gpu_sample(wl, xs, tsamp=None, dsamp=None, banned=None, uniforms=None, seed=None,
-                   offset=None, target=None, draft=None):
+                   offset=None, target=None, draft=None, diagnostics=False):
     import torch
     import lossless_draft_verification_sample_amd as sv
     cfg = wl.cfg
@@ -65,15 +65,20 @@ def run_gpu_sample(wl, xs, tsamp=None, dsamp=None, banned=None, uniforms=None, s
         banned_ids=None if ban is None else torch.from_numpy(np.ascontiguousarray(ban, dtype=np.int32)).to(dev),
         seed=cfg.philox_seed if seed is None else seed,
         offset=cfg.philox_offset if offset is None else offset,
-        uniforms=None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms, dtype=np.float64)).to(dev))
+        uniforms=None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms, dtype=np.float64)).to(dev),
+        want_overlap=diagnostics, want_hist=diagnostics)
     torch.cuda.synchronize()
-    return {
+    res = {
         "tokens": out.tokens.cpu().numpy(),
         "num_accepted": out.num_accepted.cpu().numpy(),
         "flags": out.flags.cpu().numpy().astype(np.uint32),
         "target_lse": out.target_lse.cpu().numpy().astype(np.float64),
         "draft_lse": out.draft_lse.cpu().numpy().astype(np.float64),
     }
+    if diagnostics:
+        res["overlap"] = out.overlap.cpu().numpy()
+        res["accept_hist"] = out.accept_hist.cpu().numpy().astype(np.int64)
+    return res
 
 
 def run_oracle_sample(wl, xs, u, reqs, tsamp=None, dsamp=None, banned=None):

@@ -67,13 +67,14 @@ def _sample(lib, **kw):
     a = dict(target=FAKE, draft=FAKE, dtype=1, tokens=FAKE, banned=None, n_banned=0, B=2,
              gamma=3, V=100, ts=SvSampler(1.0, 0, 1.0), ds=SvSampler(1.0, 0, 1.0), seed=0,
              offset=0, uniforms=None, out_tokens=FAKE, out_n=FAKE, out_flags=None,
-             out_tl=None, out_dl=None, ws=None, ws_bytes=0, stream=None)
+             out_tl=None, out_dl=None, out_ov=None, out_hist=None, ws=None, ws_bytes=0,
+             stream=None)
     a.update(kw)
     return lib.spec_verify_sample(
         a["target"], a["draft"], a["dtype"], a["tokens"], a["banned"], a["n_banned"], a["B"],
         a["gamma"], a["V"], a["ts"], a["ds"], a["seed"], a["offset"], a["uniforms"],
-        a["out_tokens"], a["out_n"], a["out_flags"], a["out_tl"], a["out_dl"], a["ws"],
-        a["ws_bytes"], a["stream"])
+        a["out_tokens"], a["out_n"], a["out_flags"], a["out_tl"], a["out_dl"], a["out_ov"],
+        a["out_hist"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_sample_argument_errors(lib):
@@ -105,16 +106,16 @@ def test_sample_argument_errors(lib):
 def test_greedy_argument_errors(lib):
     from lossless_draft_verification_sample_amd import _lib as L
     g = lib.spec_verify_greedy
-    assert g(None, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, None, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 3, 10, None, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 3, 10, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 5, FAKE, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EDTYPE
-    assert g(FAKE, 1, FAKE, 0, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 0, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 3, 0, FAKE, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE + 1, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2**30, 3, 10, FAKE, FAKE, None, None) == L.SV_ESIZE
+    assert g(None, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, None, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 3, 10, None, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 3, 10, FAKE, None, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 5, FAKE, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EDTYPE
+    assert g(FAKE, 1, FAKE, 0, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 0, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2, 3, 0, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE + 1, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, 2**30, 3, 10, FAKE, FAKE, None, None, None) == L.SV_ESIZE
 
 
 def test_profile_stop_without_start(lib):

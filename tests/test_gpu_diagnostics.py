@@ -1,0 +1,176 @@
+"""Parity of the per-position diagnostics of spec_verify_sample and
+spec_verify_greedy with the oracle: the overlap sum_x min(p_i, q_i) of every
+(request, position) pair, and the accepted-prefix histogram.
+
+Overlap tolerance: 1e-9 absolute. Both sides work in fp64 on the same kept
+sets; they differ only by the rounding of each row's lse (fp64 sums of at most
+V terms, a few 1e-16 relative per term), of 1/T against a division (at most
+|z/T| * 2^-52 per exponent), of the exp (a few ulp) and of the summation order
+(at most V * 2^-53 ~ 2e-11 for V ~ 1.5e5). Pairs whose top-p cut sits within
+1e-10 of its edge in either row are left out, as for the token decisions.
+The histogram is integer work: bit-exact."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+OVERLAP_TOL = 1e-9
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import lossless_draft_verification_sample_amd._lib as L
+    L.load()
+
+
+def _check_overlap(wl, got, reqs, tsamp, dsamp, banned=None, where=""):
+    ban = wl.banned if banned is None else banned
+    reqs = list(reqs)
+    alpha, margin = oracle.position_overlaps(
+        wl.target[reqs].astype(np.float64), wl.draft[reqs].astype(np.float64),
+        pu.oracle_sampler(tsamp), pu.oracle_sampler(dsamp), None if ban is None else ban[reqs])
+    g = got["overlap"][reqs]
+    ok = margin > pu.EXACT_BAND
+    err = np.abs(g - alpha)[ok]
+    assert err.size == 0 or err.max() <= OVERLAP_TOL, (where, err.max(), np.argwhere(
+        np.abs(g - alpha) > OVERLAP_TOL))
+    assert int((~ok).sum()) <= max(1, alpha.size // 100), where
+    return alpha
+
+
+def _check_hist(got, gamma, where=""):
+    h = got["accept_hist"]
+    assert h.shape == (gamma + 1,)
+    assert np.array_equal(h, np.bincount(got["num_accepted"], minlength=gamma + 1)), where
+
+
+CASES = [
+    # name, overrides, target sampler, draft sampler (None = the config's)
+    ("c1", {}, None, None),                                              # fp32, dense rows
+    ("c2", dict(B=3), None, None),                                       # top-k 50 in both
+    ("c3a", dict(B=2, V=20011), None, None),                             # dense, odd V
+    ("c5", dict(B=3, V=30011), None, None),                              # top-p + bans, odd V
+    ("c3a", dict(B=2, V=40000), (1.0, 0, 1.0), (0.9, 40, 1.0)),          # only the draft truncated
+    ("c5", dict(B=2, V=12000, dtype="f32"), None, None),                 # fp32, top-p + bans
+    ("c5", dict(B=2, gamma=3, V=300007), (0.8, 0, 0.95), (1.0, 0, 1.0)),  # many parts per pair
+]
+
+
+@pytest.mark.parametrize("name,over,tsamp,dsamp", CASES)
+def test_overlap_and_histogram_small(name, over, tsamp, dsamp):
+    wl = pu.make(name, **over)
+    cfg = wl.cfg
+    tsamp = tsamp or pu.sampler_of(cfg)
+    dsamp = dsamp or pu.sampler_of(cfg)
+    xs = pu.oracle_proposals(wl, draft_sampler=dsamp)
+    where = f"{name} {over}"
+    got = pu.run_gpu_sample(wl, xs, tsamp=tsamp, dsamp=dsamp, diagnostics=True)
+    _check_overlap(wl, got, range(cfg.B), tsamp, dsamp, where=where)
+    _check_hist(got, cfg.gamma, where)
+    # the diagnostics leave every other output as it was
+    plain = pu.run_gpu_sample(wl, xs, tsamp=tsamp, dsamp=dsamp)
+    for k in ("tokens", "num_accepted", "flags", "target_lse", "draft_lse"):
+        assert np.array_equal(plain[k], got[k]), (where, k)
+
+
+@pytest.mark.parametrize("name", ["c3a", "c5"])
+def test_overlap_full_size_sampled_requests(name):
+    wl = pu.make(name)
+    cfg = wl.cfg
+    xs = pu.stored_proposals(name)
+    got = pu.run_gpu_sample(wl, xs, diagnostics=True)
+    reqs = [0, cfg.B // 2, cfg.B - 1]
+    _check_overlap(wl, got, reqs, pu.sampler_of(cfg), pu.sampler_of(cfg), where=name)
+    a = got["overlap"]
+    assert a.shape == (cfg.B, cfg.gamma)
+    assert np.all((a >= 0.0) & (a <= 1.0 + 1e-12))
+    _check_hist(got, cfg.gamma, name)
+    assert got["accept_hist"].sum() == cfg.B
+    # the accepted lengths the oracle reaches on the same requests
+    u = pu.philox_uniforms(cfg.philox_seed, cfg.philox_offset, cfg.B, cfg.gamma)
+    ref = pu.run_oracle_sample(wl, xs, u, reqs)
+    for k, b in enumerate(reqs):
+        if not ref.margin[k] <= pu.EXACT_BAND:
+            assert got["num_accepted"][b] == ref.num_accepted[k]
+
+
+def test_overlap_one_part_per_pair():
+    # many pairs and short rows: one workgroup per pair, no partial sums
+    wl = pu.make("c5", B=300, gamma=8, V=5000, n_banned=16, seed=81)
+    cfg = wl.cfg
+    s = pu.sampler_of(cfg)
+    xs = pu.oracle_proposals(wl, reqs=[0, 150, 299])
+    got = pu.run_gpu_sample(wl, xs, diagnostics=True)
+    _check_overlap(wl, got, [0, 150, 299], s, s, where="one part")
+    _check_hist(got, cfg.gamma, "one part")
+
+
+def test_overlap_of_empty_rows_and_identical_rows():
+    from lossless_draft_verification_sample_amd import synth
+    V, gamma, B = 2000, 3, 3                       # V within the 2048-entry ban limit
+    wl = pu.make("c3a", B=B, gamma=gamma, V=V, boost="none", seed=82)
+    banned = np.full((B, V), -1, dtype=np.int32)
+    banned[0] = np.arange(V)                       # request 0: every row empty
+    t = wl.target.copy()
+    t[1, 1, :] = -np.inf                           # request 1: target row 1 empty
+    wl.target = t
+    wl.target_bits = synth.f32_to_bf16_bits(t)
+    d = wl.draft.copy()
+    d[2] = wl.target[2, :gamma]                    # request 2: p == q
+    wl.draft = d
+    wl.draft_bits = synth.f32_to_bf16_bits(d)
+    s = (0.9, 0, 0.95)
+    xs = pu.oracle_proposals(wl, draft_sampler=s, reqs=[1, 2])
+    got = pu.run_gpu_sample(wl, xs, tsamp=s, dsamp=s, banned=banned, diagnostics=True)
+    _check_overlap(wl, got, range(B), s, s, banned=banned, where="empty/identical")
+    assert np.all(got["overlap"][0] == 0.0)
+    assert got["overlap"][1, 1] == 0.0
+    assert np.all(np.abs(got["overlap"][2] - 1.0) < 1e-12)
+    _check_hist(got, gamma, "empty/identical")
+
+
+def test_histogram_is_overwritten_by_each_call():
+    import torch
+    import lossless_draft_verification_sample_amd as sv
+    wl = pu.make("c2", B=8, V=4000, seed=83)
+    cfg = wl.cfg
+    dev = pu.torch_dev()
+    xs = pu.oracle_proposals(wl)
+    t = pu.logits_tensor(wl.target, wl.target_bits, cfg.dtype, dev)
+    d = pu.logits_tensor(wl.draft, wl.draft_bits, cfg.dtype, dev)
+    xt = torch.from_numpy(xs).to(dev)
+    s = pu.sampler_of(cfg)
+    out = sv.spec_verify_sample(t, d, xt, s, s, want_hist=True)
+    hist = out.accept_hist
+    hist.fill_(12345)
+    for off in range(3):
+        out = sv.spec_verify_sample(t, d, xt, s, s, offset=off, want_hist=True, out=out)
+        torch.cuda.synchronize()
+        n = out.num_accepted.cpu().numpy()
+        assert np.array_equal(out.accept_hist.cpu().numpy(),
+                              np.bincount(n, minlength=cfg.gamma + 1)), off
+    assert out.accept_hist.data_ptr() == hist.data_ptr()
+
+
+def test_greedy_histogram():
+    import torch
+    import lossless_draft_verification_sample_amd as sv
+    wl = pu.make("c4", B=40, V=9000)
+    cfg = wl.cfg
+    dev = pu.torch_dev()
+    t = pu.logits_tensor(wl.target, wl.target_bits, cfg.dtype, dev)
+    am = np.argmax(wl.target, axis=2)
+    xs = np.where(wl.match_coin < cfg.match_prob, am[:, :cfg.gamma], wl.random_tokens).astype(np.int32)
+    out = sv.spec_verify_greedy(t, torch.from_numpy(xs).to(dev), want_hist=True)
+    torch.cuda.synchronize()
+    n = out.num_accepted.cpu().numpy()
+    ref = oracle.verify_greedy(wl.target.astype(np.float64), xs)
+    assert np.array_equal(n, ref.num_accepted)
+    assert np.array_equal(out.accept_hist.cpu().numpy(),
+                          oracle.accepted_prefix_histogram(ref.num_accepted, cfg.gamma))
