@@ -16,6 +16,11 @@ Prints one JSON line. `value` is verified logit rows per second
 divided by its average duration, measured with HIP events recorded by the
 library around each of its launches on the launch stream. `cpu_baseline` times
 the float64 oracle on a bounded sample of the same workload on one host core.
+
+With --diagnostics every step also asks for the per-position overlaps and the
+accepted-prefix histogram; the line then carries a `diagnostics` object that
+rates the overlap kernel the same way (algorithmic bytes: the row of each pair
+that is read in full, both rows when neither is truncated).
 """
 
 import argparse
@@ -107,6 +112,8 @@ def main():
     ap.add_argument("--config", default="c5")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="also compute per-position overlaps and the accepted-prefix histogram")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -154,11 +161,17 @@ def main():
                          dtype=torch.uint8, device=dev)
         out = sv.SampleOut(torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev),
                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
-                           torch.empty((cfg.B,), dtype=torch.int32, device=dev), None, None)
+                           torch.empty((cfg.B,), dtype=torch.int32, device=dev), None, None,
+                           torch.empty((cfg.B, cfg.gamma), dtype=torch.float64, device=dev)
+                           if args.diagnostics else None,
+                           torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev)
+                           if args.diagnostics else None)
     else:
         out = sv.GreedyOut(torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev),
                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
-                           torch.empty((cfg.B,), dtype=torch.int32, device=dev))
+                           torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+                           torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev)
+                           if args.diagnostics else None)
 
     def step(k):
         c = k % COPIES
@@ -229,6 +242,23 @@ def main():
         "mean_emitted_per_request": float(n_acc.mean() + 1),
         "flags_nonzero": int((flags != 0).sum()),
     }
+    if args.diagnostics:
+        res["config"]["diagnostics"] = True
+        diag = {"accept_hist": out.accept_hist.cpu().numpy().tolist()}
+        if cfg.mode == "sample":
+            ov_ms, ov_n = prof["overlap"]
+            ov_avg = ov_ms / max(ov_n, 1)
+            truncated = cfg.top_k > 0 or cfg.top_p < 1.0
+            ov_bytes = cfg.B * cfg.gamma * cfg.V * s * (1 if truncated else 2)
+            ov_gbps = ov_bytes / (ov_avg / 1e3) / 1e9
+            diag.update({
+                "mean_overlap": float(out.overlap.mean().item()),
+                "roofline": {"kernel": "overlap", "bound": "hbm", "achieved": ov_gbps,
+                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": ov_gbps / HBM_PEAK_GBPS, "avg_kernel_ms": ov_avg,
+                             "launches": ov_n, "algorithmic_bytes": ov_bytes,
+                             "traffic": traffic_record("overlap", cfg.name)}})
+        res["diagnostics"] = diag
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2**20 // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)

@@ -15,11 +15,15 @@
 // s_d - lse_d)): one fp64 exp per token kept in both rows.
 //
 // Work split: each (request, position) pair gets `parts` workgroups over
-// consecutive sub-chunks of DRAW_SUB tokens; a wave owns whole sub-chunks. A
-// truncated row keeps few tokens: it is read in full and the other row only in
-// the groups where it keeps something. Sums are fixed-order (lanes, waves,
-// parts), so the result does not depend on scheduling; with several parts the
-// last workgroup of a pair to arrive adds the partial sums in part order.
+// consecutive sub-chunks of DRAW_SUB tokens; a wave owns whole sub-chunks and
+// issues the loads of its next sub-chunk before it works on the current one. A
+// truncated row keeps few tokens: it is streamed in full, its kept tokens are
+// queued in LDS, and the other row is read only at the queued positions, in one
+// batch of independent loads when the queue fills or the wave's sub-chunks end
+// (so no load waits on another inside the stream). Sums are fixed-order (queue
+// order, lanes, waves, parts), so the result does not depend on scheduling;
+// with several parts the last workgroup of a pair to arrive adds the partial
+// sums in part order.
 
 #include "sv_launch.hpp"
 #include "sv_rowio.hpp"
@@ -30,12 +34,195 @@ constexpr int OV_THREADS = 256;
 constexpr int OV_NW = OV_THREADS / WAVE;
 constexpr int OV_GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
 
+constexpr int OV_QCAP = 8 * WAVE;   // queued kept tokens per wave: one batch of 8 loads per lane
+
+// A token kept in the leading row, waiting for the other row's logit.
+struct alignas(8) QueuedTok {
+  int32_t x;
+  float z;   // the leading row's logit
+};
+
 struct OverlapShared {
   double etab[256];
-  KeptTok kt[OV_NW][WAVE];
+  QueuedTok q[OV_NW][OV_QCAP];
   uint32_t bm[OV_SPW_MAX * DRAW_SUB / 32];
   double w[OV_NW];
 };
+
+template <typename Elem>
+__device__ __forceinline__ float load_logit(const void* row, int x) {
+  if constexpr (sizeof(Elem) == 2) return bf16_to_f32(((const uint16_t*)row)[x]);
+  return ((const float*)row)[x];
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// What the streaming loop needs to know about one (request, position) pair.
+struct OvPair {
+  const void* trow;
+  const void* drow;
+  RowStat ts, ds;
+  double tinv, dinv;  // 1/T of both rows
+  int V, tok0, nsl, nb;
+  bool vec;
+};
+
+// The wave's sum of min(p, q) over its sub-chunks wv, wv + OV_NW, ... .
+// LEAD 0: the target row is truncated and leads: it is read in full and the
+// draft row only where the target keeps a token; LEAD 1: the reverse; LEAD 2:
+// neither is truncated and both rows are read in full.
+template <typename Elem, int LEAD>
+__device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, int wv, int lane) {
+  constexpr bool FULL_T = LEAD != 1, FULL_D = LEAD != 0;
+  auto term = [&](float zt, float zd) {
+    const double lt = fma((double)zt, r.tinv, -r.ts.lse);
+    const double ld = fma((double)zd, r.dinv, -r.ds.lse);
+    return exp_tab(fmin(lt, ld), sh.etab);
+  };
+  const void* lrow = LEAD == 1 ? r.drow : r.trow;   // leading row
+  const void* orow = LEAD == 1 ? r.trow : r.drow;   // the other row
+  const RowStat& ls = LEAD == 1 ? r.ds : r.ts;
+  const RowStat& os = LEAD == 1 ? r.ts : r.ds;
+  double acc = 0.0;
+  // the other row's logits at the n queued tokens: lane l takes entries l,
+  // l + 64, ...; all loads are issued before any is used
+  auto flush = [&](int n) {
+    wave_sync_lds();
+    float zl[OV_QCAP / WAVE], zo[OV_QCAP / WAVE];
+#pragma unroll
+    for (int u = 0; u < OV_QCAP / WAVE; ++u) {
+      const int j = u * WAVE + lane;
+      zo[u] = -INFINITY;
+      zl[u] = -INFINITY;
+      if (j < n) {
+        const QueuedTok t = sh.q[wv][j];
+        zl[u] = t.z;
+        zo[u] = load_logit<Elem>(orow, t.x);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < OV_QCAP / WAVE; ++u) {
+      if (u * WAVE + lane < n && is_kept(zo[u], os, false))
+        acc += LEAD == 1 ? term(zo[u], zl[u]) : term(zl[u], zo[u]);
+    }
+    wave_sync_lds();
+  };
+
+  Group<Elem> tn[OV_GPL], dn[OV_GPL];   // the next sub-chunk, in flight
+  auto issue = [&](int sl) {
+    const int sbase = r.tok0 + sl * DRAW_SUB;
+#pragma unroll
+    for (int k = 0; k < OV_GPL; ++k) {
+      const int x0 = sbase + (lane + k * WAVE) * GRP;
+      if (x0 < r.V) {
+        if constexpr (FULL_T) load_group<Elem>(r.trow, x0, r.V, r.vec, tn[k]);
+        if constexpr (FULL_D) load_group<Elem>(r.drow, x0, r.V, r.vec, dn[k]);
+      }
+    }
+  };
+  int qlen = 0;   // wave-uniform
+  if (wv < r.nsl) issue(wv);
+  for (int sl = wv; sl < r.nsl; sl += OV_NW) {
+    const int sbase = r.tok0 + sl * DRAW_SUB;
+    Group<Elem> tg[OV_GPL], dg[OV_GPL];
+#pragma unroll
+    for (int k = 0; k < OV_GPL; ++k) {
+      if constexpr (FULL_T) tg[k] = tn[k];
+      if constexpr (FULL_D) dg[k] = dn[k];
+    }
+    if (sl + OV_NW < r.nsl) issue(sl + OV_NW);
+    // kept in the leading row (in both rows when neither leads); bans apply to
+    // both rows alike, so they are tested once
+    uint32_t km[OV_GPL];
+#pragma unroll
+    for (int k = 0; k < OV_GPL; ++k) {
+      const int x0 = sbase + (lane + k * WAVE) * GRP;
+      uint32_t m = 0u;
+      if (x0 < r.V) {
+        const uint32_t ban = r.nb > 0 ? bm_group(sh.bm, x0 - r.tok0) : 0u;
+#pragma unroll
+        for (int e = 0; e < GRP; ++e) {
+          const bool bn = (ban >> e) & 1u;
+          bool kept;
+          if constexpr (LEAD == 0)
+            kept = is_kept(group_val<Elem>(tg[k], e), r.ts, bn);
+          else if constexpr (LEAD == 1)
+            kept = is_kept(group_val<Elem>(dg[k], e), r.ds, bn);
+          else
+            kept = is_kept(group_val<Elem>(tg[k], e), r.ts, bn) &&
+                   is_kept(group_val<Elem>(dg[k], e), r.ds, false);
+          m |= (kept ? 1u : 0u) << e;
+        }
+      }
+      km[k] = m;
+    }
+    if constexpr (LEAD == 2) {
+#pragma unroll
+      for (int k = 0; k < OV_GPL; ++k) {
+        if (!km[k]) continue;
+#pragma unroll
+        for (int e = 0; e < GRP; ++e)
+          if ((km[k] >> e) & 1u) acc += term(group_val<Elem>(tg[k], e), group_val<Elem>(dg[k], e));
+      }
+    } else {
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int k = 0; k < OV_GPL; ++k) cnt += (uint32_t)__popc(km[k]);
+      const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+      const int total = (int)lane63(incl);
+      if (total == 0) continue;
+      if (qlen + total > OV_QCAP) {
+        flush(qlen);
+        qlen = 0;
+      }
+      if (total <= OV_QCAP) {
+        // queue the kept tokens in ascending token order of the wave's groups
+        int pos = qlen + (int)(incl - cnt);
+#pragma unroll
+        for (int k = 0; k < OV_GPL; ++k) {
+          if (!km[k]) continue;
+          const Group<Elem>& lg = LEAD == 1 ? dg[k] : tg[k];
+#pragma unroll
+          for (int e = 0; e < GRP; ++e) {
+            if ((km[k] >> e) & 1u) {
+              QueuedTok t;
+              t.x = sbase + (lane + k * WAVE) * GRP + e;
+              t.z = group_val<Elem>(lg, e);
+              sh.q[wv][pos++] = t;
+            }
+          }
+        }
+        qlen += total;
+      } else {
+        // a sub-chunk that keeps more tokens than the queue holds: read the
+        // other row's groups where needed and evaluate in place
+#pragma unroll
+        for (int k = 0; k < OV_GPL; ++k) {
+          if (!km[k]) continue;
+          const int x0 = sbase + (lane + k * WAVE) * GRP;
+          Group<Elem> og;
+          load_group<Elem>(orow, x0, r.V, r.vec, og);
+          const Group<Elem>& lg = LEAD == 1 ? dg[k] : tg[k];
+#pragma unroll
+          for (int e = 0; e < GRP; ++e) {
+            const float zo = group_val<Elem>(og, e), zl = group_val<Elem>(lg, e);
+            if (((km[k] >> e) & 1u) && is_kept(zo, os, false))
+              acc += LEAD == 1 ? term(zo, zl) : term(zl, zo);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (LEAD != 2) {
+    if (qlen > 0) flush(qlen);
+  }
+  (void)ls;
+  return acc;
+}
 
 template <typename Elem>
 __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
@@ -44,139 +231,37 @@ __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
   const int pair = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
   const int b = pair / g, i = pair % g;
-  const int V = a.V;
-  const RowStat ts = a.stats[(int64_t)b * RPR + i];
-  const RowStat ds = a.stats[(int64_t)b * RPR + G1 + i];
-  const Elem* trow = (const Elem*)a.target + ((int64_t)b * G1 + i) * V;
-  const Elem* drow = (const Elem*)a.draft + ((int64_t)b * g + i) * V;
-  const double tinv = 1.0 / (double)a.t_temp, dinv = 1.0 / (double)a.d_temp;
+  OvPair r;
+  r.V = a.V;
+  r.vec = a.vec != 0;
+  r.ts = a.stats[(int64_t)b * RPR + i];
+  r.ds = a.stats[(int64_t)b * RPR + G1 + i];
+  r.trow = (const Elem*)a.target + ((int64_t)b * G1 + i) * a.V;
+  r.drow = (const Elem*)a.draft + ((int64_t)b * g + i) * a.V;
+  r.tinv = 1.0 / (double)a.t_temp;
+  r.dinv = 1.0 / (double)a.d_temp;
   const int sub0 = part * a.spp;
-  const int nsl = min(a.spp, a.nsub - sub0);
-  const int tok0 = sub0 * DRAW_SUB;
+  r.tok0 = sub0 * DRAW_SUB;
   // an empty row has p (or q) = 0 everywhere: the overlap is 0
-  const bool empty = ((ts.flags | ds.flags) & FLAG_EMPTY) != 0u;
-  const int nb = (a.banned && !empty) ? a.n_banned : 0;
-  const int32_t* bl = nb ? a.banned + (int64_t)b * a.n_banned : nullptr;
-  const int32_t ban0 = tid < nb ? bl[tid] : -1;
+  const bool empty = ((r.ts.flags | r.ds.flags) & FLAG_EMPTY) != 0u;
+  r.nsl = empty ? 0 : min(a.spp, a.nsub - sub0);
+  r.nb = (a.banned && !empty) ? a.n_banned : 0;
+  const int32_t* bl = r.nb ? a.banned + (int64_t)b * a.n_banned : nullptr;
+  const int32_t ban0 = tid < r.nb ? bl[tid] : -1;
 
   exp_table_fill(sh.etab);
-  if (nb > 0)
-    mark_bans(sh.bm, nsl * DRAW_SUB, bl, nb, ban0, tok0, V);   // also publishes etab
+  if (r.nb > 0)
+    mark_bans(sh.bm, r.nsl * DRAW_SUB, bl, r.nb, ban0, r.tok0, r.V);   // also publishes etab
   else
-    __syncthreads();                                            // publishes etab
+    __syncthreads();                                                  // publishes etab
 
-  // 0: the target row is truncated and leads; 1: the draft row leads; 2: both dense
-  const int lead = ts.tau > -INFINITY ? 0 : (ds.tau > -INFINITY ? 1 : 2);
-  auto term = [&](float zt, float zd) {
-    const double lt = fma((double)zt, tinv, -ts.lse);
-    const double ld = fma((double)zd, dinv, -ds.lse);
-    return exp_tab(fmin(lt, ld), sh.etab);
-  };
-
-  double acc = 0.0;
-  const int nsl_used = empty ? 0 : nsl;
-  for (int sl = wv; sl < nsl_used; sl += OV_NW) {
-    const int sbase = tok0 + sl * DRAW_SUB;
-    Group<Elem> tg[OV_GPL], dg[OV_GPL];
-    uint32_t km[OV_GPL];
-#pragma unroll
-    for (int k = 0; k < OV_GPL; ++k) {
-      const int x0 = sbase + (lane + k * WAVE) * GRP;
-      if (x0 < V) {
-        if (lead != 1) load_group<Elem>(trow, x0, V, a.vec, tg[k]);
-        if (lead != 0) load_group<Elem>(drow, x0, V, a.vec, dg[k]);
-      }
-    }
-    // kept in the leading row (both rows when dense); bans apply to both rows
-    // alike, so they are tested once
-#pragma unroll
-    for (int k = 0; k < OV_GPL; ++k) {
-      const int x0 = sbase + (lane + k * WAVE) * GRP;
-      uint32_t m = 0u;
-      if (x0 < V) {
-        const uint32_t ban = nb > 0 ? bm_group(sh.bm, x0 - tok0) : 0u;
-#pragma unroll
-        for (int e = 0; e < GRP; ++e) {
-          const bool bn = (ban >> e) & 1u;
-          bool kept;
-          if (lead == 0)
-            kept = is_kept(group_val<Elem>(tg[k], e), ts, bn);
-          else if (lead == 1)
-            kept = is_kept(group_val<Elem>(dg[k], e), ds, bn);
-          else
-            kept = is_kept(group_val<Elem>(tg[k], e), ts, bn) &&
-                   is_kept(group_val<Elem>(dg[k], e), ds, false);
-          m |= (kept ? 1u : 0u) << e;
-        }
-      }
-      km[k] = m;
-    }
-    // the other row, only where the leading row keeps a token
-    if (lead != 2) {
-#pragma unroll
-      for (int k = 0; k < OV_GPL; ++k) {
-        if (!km[k]) continue;
-        const int x0 = sbase + (lane + k * WAVE) * GRP;
-        uint32_t m = 0u;
-        if (lead == 0) {
-          load_group<Elem>(drow, x0, V, a.vec, dg[k]);
-#pragma unroll
-          for (int e = 0; e < GRP; ++e)
-            m |= (is_kept(group_val<Elem>(dg[k], e), ds, false) ? 1u : 0u) << e;
-        } else {
-          load_group<Elem>(trow, x0, V, a.vec, tg[k]);
-#pragma unroll
-          for (int e = 0; e < GRP; ++e)
-            m |= (is_kept(group_val<Elem>(tg[k], e), ts, false) ? 1u : 0u) << e;
-        }
-        km[k] &= m;
-      }
-    }
-    uint32_t cnt = 0u;
-#pragma unroll
-    for (int k = 0; k < OV_GPL; ++k) cnt += (uint32_t)__popc(km[k]);
-    const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
-    const uint32_t total = lane63(incl);
-    if (total == 0u) continue;
-    if (total <= (uint32_t)WAVE) {
-      // few tokens kept in both rows: queue them so that lane k evaluates the
-      // k-th one
-      uint32_t pos = incl - cnt;
-#pragma unroll
-      for (int k = 0; k < OV_GPL; ++k) {
-        if (!km[k]) continue;
-#pragma unroll
-        for (int e = 0; e < GRP; ++e) {
-          if ((km[k] >> e) & 1u) {
-            KeptTok t;
-            t.x = sbase + (lane + k * WAVE) * GRP + e;
-            t.zt = group_val<Elem>(tg[k], e);
-            t.zd = group_val<Elem>(dg[k], e);
-            t.pad = 0;
-            sh.kt[wv][pos++] = t;
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if ((uint32_t)lane < total) {
-        const KeptTok t = sh.kt[wv][lane];
-        acc += term(t.zt, t.zd);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else {
-#pragma unroll
-      for (int k = 0; k < OV_GPL; ++k) {
-        if (!km[k]) continue;
-#pragma unroll
-        for (int e = 0; e < GRP; ++e)
-          if ((km[k] >> e) & 1u) acc += term(group_val<Elem>(tg[k], e), group_val<Elem>(dg[k], e));
-      }
-    }
-  }
+  double acc;
+  if (r.ts.tau > -INFINITY)
+    acc = ov_stream<Elem, 0>(r, sh, wv, lane);
+  else if (r.ds.tau > -INFINITY)
+    acc = ov_stream<Elem, 1>(r, sh, wv, lane);
+  else
+    acc = ov_stream<Elem, 2>(r, sh, wv, lane);
   acc = wave_total(acc);
   if (lane == 0) sh.w[wv] = acc;
   __syncthreads();

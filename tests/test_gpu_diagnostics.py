@@ -59,6 +59,11 @@ CASES = [
     ("c3a", dict(B=2, V=40000), (1.0, 0, 1.0), (0.9, 40, 1.0)),          # only the draft truncated
     ("c5", dict(B=2, V=12000, dtype="f32"), None, None),                 # fp32, top-p + bans
     ("c5", dict(B=2, gamma=3, V=300007), (0.8, 0, 0.95), (1.0, 0, 1.0)),  # many parts per pair
+    # a truncated row keeping ~12% of its tokens: the per-wave queue of kept
+    # tokens fills and is drained in the middle of the stream
+    ("c3a", dict(B=2, V=40000), (1.0, 5000, 1.0), (1.0, 0, 1.0)),
+    # keeping ~75%: sub-chunks hold more kept tokens than the queue, evaluated in place
+    ("c3a", dict(B=2, V=40000), (1.0, 0, 1.0), (1.0, 30000, 1.0)),
 ]
 
 
