@@ -34,7 +34,7 @@ constexpr int OV_THREADS = 256;
 constexpr int OV_NW = OV_THREADS / WAVE;
 constexpr int OV_GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
 
-constexpr int OV_QCAP = 8 * WAVE;   // queued kept tokens per wave: one batch of 8 loads per lane
+constexpr int OV_QCAP = 4 * WAVE;   // queued kept tokens per wave: one batch of 4 loads per lane
 
 // A token kept in the leading row, waiting for the other row's logit.
 struct alignas(8) QueuedTok {

@@ -17,7 +17,7 @@ constexpr int DRAW_TARGET_WGS = 1024;   // about four draw workgroups per CU
 
 // Per-position overlap: every (request, position) pair is split into `parts`
 // workgroups of at most OV_SPW_MAX sub-chunks, about OV_TARGET_WGS in total.
-constexpr int OV_SPW_MAX = 64;
+constexpr int OV_SPW_MAX = 32;
 constexpr int OV_TARGET_WGS = 2048;
 
 struct RowStatsArgs {
