@@ -36,12 +36,6 @@ constexpr int OV_GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave o
 
 constexpr int OV_QCAP = 4 * WAVE;   // queued kept tokens per wave: one batch of 4 loads per lane
 
-// A token kept in the leading row, waiting for the other row's logit.
-struct alignas(8) QueuedTok {
-  int32_t x;
-  float z;   // the leading row's logit
-};
-
 struct OverlapShared {
   double etab[256];
   QueuedTok q[OV_NW][OV_QCAP];
@@ -49,17 +43,7 @@ struct OverlapShared {
   double w[OV_NW];
 };
 
-template <typename Elem>
-__device__ __forceinline__ float load_logit(const void* row, int x) {
-  if constexpr (sizeof(Elem) == 2) return bf16_to_f32(((const uint16_t*)row)[x]);
-  return ((const float*)row)[x];
-}
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // What the streaming loop needs to know about one (request, position) pair.
 struct OvPair {

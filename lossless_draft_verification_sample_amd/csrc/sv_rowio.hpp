@@ -115,4 +115,25 @@ struct alignas(16) KeptTok {
   int32_t pad;
 };
 
+// A token kept in a leading row, queued in LDS until the other row's logit at
+// the same position is read.
+struct alignas(8) QueuedTok {
+  int32_t x;
+  float z;   // the leading row's logit
+};
+
+// One logit of a row as float (a single-element read).
+template <typename Elem>
+__device__ __forceinline__ float load_logit(const void* row, int x) {
+  if constexpr (sizeof(Elem) == 2) return bf16_to_f32(((const uint16_t*)row)[x]);
+  return ((const float*)row)[x];
+}
+
+// Orders a wave's LDS writes before its later LDS reads (and the reverse).
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace sv

@@ -21,6 +21,8 @@
 // the last workgroup of the request to finish (an arrival counter) locates the
 // sub-chunk holding u * S, rescans it and writes the request's outputs.
 
+#include <type_traits>
+
 #include "sv_launch.hpp"
 #include "sv_rowio.hpp"
 
@@ -166,9 +168,14 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b) {
   return w;
 }
 
+constexpr int DR_QCAP = 4 * WAVE;   // queued kept tokens per wave: one batch of 4 reads per lane
+
 struct DrawShared {
   double etab[256];
-  KeptTok kt[DR_NW][WAVE];
+  union {
+    KeptTok kt[DR_NW][WAVE];          // bonus draws and untruncated targets
+    QueuedTok q[DR_NW][DR_QCAP];      // rejections at a truncated target
+  };
   uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
   double w[DRAW_SPW_MAX];
   double p[DRAW_SPW_MAX];
@@ -202,13 +209,19 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
 
   // Weight sums of the workgroup's sub-chunks: wave wv owns sub-chunks wv,
   // wv + DR_NW, ...; lane l reads groups l, l + 64, l + 128, l + 192 of a
-  // sub-chunk, so every load instruction covers 1 KiB of the row. Only tokens
-  // kept in the target row carry weight. A truncated target row keeps few
-  // tokens, spread thinly: their draft logits are gathered once the target
-  // groups are known, and the wave queues its kept tokens in LDS so that lane k
-  // evaluates the k-th one (one dense pass instead of divergent ones). A wave
-  // with more kept tokens than lanes evaluates them in place.
+  // sub-chunk, so every load instruction covers 1 KiB of the row, and the wave
+  // issues the loads of its next sub-chunk before it works on the current one.
+  // Only tokens kept in the target row carry weight.
+  // - At a rejection with a truncated target row (few kept tokens, spread
+  //   thinly) the draft logits are needed only at the kept tokens: the wave
+  //   queues them in LDS in token order and reads the draft row at the queued
+  //   positions in one batch of independent loads, when the queue would
+  //   overflow or its sub-chunks end; the sums then go to their sub-chunks.
+  // - Otherwise (the bonus draw, or an untruncated target whose draft row is
+  //   streamed alongside) the weights come from registers: through a per-wave
+  //   compaction when at most 64 tokens are kept, in place when more are.
   const bool sparse = r.ts.tau > -INFINITY;
+  const bool queued = sparse && r.drow;
   // the kept tokens of the wave's groups of one sub-chunk, and their number
   auto sub_mask = [&](int sbase, const Group<Elem>(&tg)[GPL], uint32_t(&km)[GPL]) {
     uint32_t cnt = 0u;
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
     }
     return cnt;
   };
-  // sums of those kept tokens, added to sw and sp
+  // sums of those kept tokens from registers, added to sw and sp
   auto sub_sums = [&](int sbase, const Group<Elem>(&tg)[GPL], const Group<Elem>(&dg)[GPL],
                       const uint32_t(&km)[GPL], uint32_t cnt, double& sw, double& sp) {
     const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
@@ -243,9 +256,7 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync_lds();
       if ((uint32_t)lane < total) {
         const KeptTok t = sh.kt[wv][lane];
         double w, p;
@@ -253,20 +264,11 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
         sw += w;
         sp += p;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync_lds();
     } else {
 #pragma unroll
       for (int k = 0; k < GPL; ++k)
         if (km[k]) group_sums<Elem>(r, tg[k], dg[k], km[k], sh.etab, sw, sp);
-    }
-  };
-  auto load_sub = [&](int sbase, Group<Elem>(&g)[GPL], const void* row) {
-#pragma unroll
-    for (int k = 0; k < GPL; ++k) {
-      const int x0 = sbase + (lane + k * WAVE) * GRP;
-      if (x0 < a.V) load_group<Elem>(row, x0, a.V, a.vec, g[k]);
     }
   };
   auto publish = [&](int sl, double sw, double sp) {
@@ -277,23 +279,128 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
       sh.p[sl] = sp;
     }
   };
-  for (int sl = wv; sl < nsl; sl += DR_NW) {
-    const int sbase = tok0 + sl * DRAW_SUB;
-    Group<Elem> tg[GPL], dg[GPL];
-    load_sub(sbase, tg, r.trow);
-    if (r.drow && !sparse) load_sub(sbase, dg, r.drow);
-    uint32_t km[GPL];
-    const uint32_t cnt = sub_mask(sbase, tg, km);
-    if (r.drow && sparse) {
-      // truncated target: draft groups only where a target token is kept
+  // The wave's sub-chunks, specialised by how the draft row is read: 0 =
+  // queued reads at a truncated target, 1 = none (bonus draw), 2 = streamed.
+  auto run = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    Group<Elem> tn[GPL], dn[GPL];   // the wave's next sub-chunk, in flight
+    auto issue = [&](int sl) {
+      const int sbase = tok0 + sl * DRAW_SUB;
 #pragma unroll
-      for (int k = 0; k < GPL; ++k)
-        if (km[k]) load_group<Elem>(r.drow, sbase + (lane + k * WAVE) * GRP, a.V, a.vec, dg[k]);
+      for (int k = 0; k < GPL; ++k) {
+        const int x0 = sbase + (lane + k * WAVE) * GRP;
+        if (x0 < a.V) {
+          load_group<Elem>(r.trow, x0, a.V, a.vec, tn[k]);
+          if constexpr (MODE == 2) load_group<Elem>(r.drow, x0, a.V, a.vec, dn[k]);
+        }
+      }
+    };
+    // queued tokens and the wave's sub-chunks they belong to (pend_lo ..
+    // pend_hi, step DR_NW; wave-uniform)
+    int qlen = 0, pend_lo = 0, pend_hi = -1;
+    auto flush = [&]() {
+      constexpr int QU = DR_QCAP / WAVE;
+      wave_sync_lds();
+      int qx[QU];
+      float qt[QU], qd[QU];
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int j = u * WAVE + lane;
+        qx[u] = -1;
+        qt[u] = 0.0f;
+        qd[u] = 0.0f;
+        if (j < qlen) {
+          const QueuedTok t = sh.q[wv][j];
+          qx[u] = t.x;
+          qt[u] = t.z;
+          qd[u] = load_logit<Elem>(r.drow, t.x);
+        }
+      }
+      double qw[QU], qp[QU];
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        qw[u] = 0.0;
+        qp[u] = 0.0;
+        if (qx[u] >= 0) tok_weight(r, qt[u], qd[u], sh.etab, qw[u], qp[u]);
+      }
+      for (int sl = pend_lo; sl <= pend_hi; sl += DR_NW) {
+        const int lo = tok0 + sl * DRAW_SUB;
+        double sw = 0.0, sp = 0.0;
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          if (qx[u] >= lo && qx[u] < lo + DRAW_SUB) {
+            sw += qw[u];
+            sp += qp[u];
+          }
+        }
+        publish(sl, sw, sp);
+      }
+      wave_sync_lds();
+      qlen = 0;
+      pend_hi = -1;
+    };
+    if (wv < nsl) issue(wv);
+    for (int sl = wv; sl < nsl; sl += DR_NW) {
+      const int sbase = tok0 + sl * DRAW_SUB;
+      Group<Elem> tg[GPL], dg[GPL];
+#pragma unroll
+      for (int k = 0; k < GPL; ++k) {
+        tg[k] = tn[k];
+        if constexpr (MODE == 2) dg[k] = dn[k];
+      }
+      if (sl + DR_NW < nsl) issue(sl + DR_NW);
+      uint32_t km[GPL];
+      const uint32_t cnt = sub_mask(sbase, tg, km);
+      if constexpr (MODE != 0) {
+        double sw = 0.0, sp = 0.0;
+        sub_sums(sbase, tg, dg, km, cnt, sw, sp);
+        publish(sl, sw, sp);
+      } else {
+        const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+        const int total = (int)lane63(incl);
+        if (pend_hi >= 0 && qlen + total > DR_QCAP) flush();
+        if (total > DR_QCAP) {
+          // more kept tokens than the queue holds: draft groups where needed,
+          // evaluated in place
+#pragma unroll
+          for (int k = 0; k < GPL; ++k)
+            if (km[k]) load_group<Elem>(r.drow, sbase + (lane + k * WAVE) * GRP, a.V, a.vec, dg[k]);
+          double sw = 0.0, sp = 0.0;
+#pragma unroll
+          for (int k = 0; k < GPL; ++k)
+            if (km[k]) group_sums<Elem>(r, tg[k], dg[k], km[k], sh.etab, sw, sp);
+          publish(sl, sw, sp);
+          continue;
+        }
+        int pos = qlen + (int)(incl - cnt);
+#pragma unroll
+        for (int k = 0; k < GPL; ++k) {
+          if (!km[k]) continue;
+#pragma unroll
+          for (int e = 0; e < GRP; ++e) {
+            if ((km[k] >> e) & 1u) {
+              QueuedTok t;
+              t.x = sbase + (lane + k * WAVE) * GRP + e;
+              t.z = group_val<Elem>(tg[k], e);
+              sh.q[wv][pos++] = t;
+            }
+          }
+        }
+        qlen += total;
+        if (pend_hi < 0) pend_lo = sl;
+        pend_hi = sl;
+      }
     }
-    double sw = 0.0, sp = 0.0;
-    sub_sums(sbase, tg, dg, km, cnt, sw, sp);
-    publish(sl, sw, sp);
-  }
+    if constexpr (MODE == 0) {
+      if (pend_hi >= 0) flush();
+    }
+  };
+  if (queued)
+    run(std::integral_constant<int, 0>{});
+  else if (!r.drow)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 2>{});
   __syncthreads();
   if (tid < nsl) {
     // Publication without a release fence: the sums are agent-scope atomic

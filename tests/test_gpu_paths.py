@@ -124,3 +124,17 @@ def test_many_requests_small_rows():
     samp = (0.7, 50, 1.0)
     xs = pu.oracle_proposals(wl, draft_sampler=samp)
     _check(wl, xs, samp, seed=3, where="B=600")
+
+
+@pytest.mark.parametrize("k", [5000, 30000])
+def test_dense_truncated_targets_at_a_rejection(k):
+    # a truncated target keeping ~12% (k = 5000) or ~75% (k = 30000) of V: the
+    # draw's per-wave queue of kept tokens is drained mid-stream, or a
+    # sub-chunk keeps more tokens than the queue holds and is evaluated in place
+    V, B, gamma = 40000, 6, 3
+    wl = pu.make("c3a", B=B, gamma=gamma, V=V, boost="none", target_sd=1.0, draft_sd=1.0,
+                 seed=78 + k % 7)
+    samp = (1.0, k, 1.0)
+    xs = pu.oracle_proposals(wl, draft_sampler=samp)
+    got, ref = _check(wl, xs, samp, seed=9, where=f"top-k {k}")
+    assert np.any(got["num_accepted"] < gamma)      # rejections take the queued path
