@@ -15,6 +15,9 @@ Parity status of each function (what pins it to something other than itself):
                      Monte Carlo; chi-square of emitted tokens against p.
   verify_greedy      pinned: brute-force loop over small rows.
   first_token_law    pinned: the worked example's printed numbers.
+  commit_chain       pinned: the running example of "Committing state after
+                     rejection" (tests/golden/commit_example.json) and the
+                     row-partition invariants.
   diagnostics        per-position overlap 1 - TV, accepted-prefix histogram,
                      conditional acceptance, accepted-length law; each pin is
                      listed in oracle/diagnostics.py.
@@ -23,7 +26,8 @@ the uniform layout, the tie rules of top-k, top-p and greedy, and the actual
 numbers of the alpha = 0.8 example (only its invariants are printed).
 """
 
-from . import diagnostics  # noqa: F401
+from . import commit, diagnostics  # noqa: F401
+from .commit import commit_chain  # noqa: F401
 from .diagnostics import (  # noqa: F401
     accepted_prefix_histogram,
     conditional_acceptance,
