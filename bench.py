@@ -21,6 +21,10 @@ With --diagnostics every step also asks for the per-position overlaps and the
 accepted-prefix histogram; the line then carries a `diagnostics` object that
 rates the overlap kernel the same way (algorithmic bytes: the row of each pair
 that is read in full, both rows when neither is truncated).
+
+With --commit every step is followed by spec_verify_commit (chain KV-commit
+metadata from the step's outputs, with synthetic KV lengths and slots); the
+line then carries a `commit` object with that kernel's time and bytes.
 """
 
 import argparse
@@ -114,6 +118,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--diagnostics", action="store_true",
                     help="also compute per-position overlaps and the accepted-prefix histogram")
+    ap.add_argument("--commit", action="store_true",
+                    help="follow every step with the chain KV-commit metadata kernel")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -173,6 +179,16 @@ def main():
                            torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev)
                            if args.diagnostics else None)
 
+    if args.commit:
+        G1 = cfg.gamma + 1
+        kv_len = torch.arange(cfg.B, dtype=torch.int32, device=dev) * 4096
+        slots = (torch.arange(cfg.B * G1, dtype=torch.int32, device=dev).reshape(cfg.B, G1)
+                 + 1_000_000)
+        cout = sv.CommitOut(torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
+                            torch.empty((cfg.B, cfg.gamma), dtype=torch.int32, device=dev))
+
     def step(k):
         c = k % COPIES
         if cfg.mode == "sample":
@@ -181,6 +197,8 @@ def main():
                                   workspace=ws, out=out)
         else:
             sv.spec_verify_greedy(copies[c], toks, out=out)
+        if args.commit:
+            sv.spec_verify_commit(out.tokens, out.num_accepted, kv_len, slots, out=cout)
 
     for k in range(args.warmup):
         step(k)
@@ -259,6 +277,18 @@ def main():
                              "launches": ov_n, "algorithmic_bytes": ov_bytes,
                              "traffic": traffic_record("overlap", cfg.name)}})
         res["diagnostics"] = diag
+    if args.commit:
+        res["config"]["commit"] = True
+        cm_ms, cm_n = prof["commit"]
+        cm_avg = cm_ms / max(cm_n, 1)
+        G1 = cfg.gamma + 1
+        # tokens, slots, accepted counts and KV lengths in; lengths, anchors,
+        # free counts and free slots out
+        cm_bytes = 4 * (2 * cfg.B * G1 + 2 * cfg.B + 3 * cfg.B + cfg.B * cfg.gamma)
+        res["commit"] = {"kernel": "commit", "avg_kernel_ms": cm_avg, "launches": cm_n,
+                         "bytes_per_launch": cm_bytes,
+                         "achieved_gbps": cm_bytes / (cm_avg / 1e3) / 1e9,
+                         "bound": "launch latency (one wave per request)"}
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2**20 // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)

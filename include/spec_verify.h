@@ -164,6 +164,34 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
                        int32_t* out_num_accepted, uint32_t* out_flags,
                        uint32_t* out_accept_hist, void* stream);
 
+/* Chain KV-commit metadata of one verification round ("Drafters and
+ * Speculative Decoding: Useful Tokens, Correct State", sections "Committed
+ * tokens versus cached states" and "Committing state after rejection"), from
+ * the outputs of spec_verify_sample or spec_verify_greedy, on the same stream.
+ * Convention: before the round request b has kv_len[b] = K materialised target
+ * KV rows, and its last committed token (the anchor) is pending: it has no row
+ * yet. The verification pass ran the gamma+1 inputs (anchor, x_0, ...,
+ * x_{gamma-1}) at positions K .. K+gamma and wrote their rows; slots[b][j] is
+ * the physical KV slot of position K + j. After the round:
+ *   new_kv_len[b] = K + 1 + n   the anchor's row and the n accepted rows are
+ *                               committed history (logical length = new_kv_len + 1);
+ *   anchor[b] = out_tokens[b][n]  the correction or bonus token, pending until
+ *                               the next pass computes its row (-1 if the
+ *                               verifier emitted none, see SV_FLAG_EMPTY);
+ *   n_free[b] = gamma - n       rows of the rejected proposals x_n .. x_{gamma-1};
+ *   free_slots[b][0 .. gamma-n-1] = slots[b][n+1 .. gamma], then -1.
+ * Pointers: out_tokens [B][gamma+1], out_num_accepted [B], kv_len [B] (inputs,
+ * device); new_kv_len [B], anchor [B] (required outputs); n_free [B] or NULL;
+ * free_slots [B][gamma] or NULL, which needs slots [B][gamma+1]. A request
+ * whose accepted count lies outside [0, gamma] is left unchanged (new_kv_len =
+ * kv_len, anchor -1, nothing freed). The caller keeps kv_len + gamma + 1 within
+ * int32. Returns SV_EINVAL for a missing required pointer, free_slots without
+ * slots, B < 1 or gamma outside [1, 63]; SV_ESIZE if B*(gamma+1) overflows. */
+int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepted,
+                       const int32_t* kv_len, const int32_t* slots, int32_t B, int32_t gamma,
+                       int32_t* new_kv_len, int32_t* anchor, int32_t* n_free,
+                       int32_t* free_slots, void* stream);
+
 /* Static description of a status code. */
 const char* spec_verify_strerror(int status);
 
@@ -178,7 +206,8 @@ const char* spec_verify_strerror(int status);
 #define SV_K_GREEDY_ARGMAX 2
 #define SV_K_GREEDY_SCAN 3
 #define SV_K_OVERLAP 4
-#define SV_NUM_KERNELS 5
+#define SV_K_COMMIT 5
+#define SV_NUM_KERNELS 6
 int spec_verify_profile_start(int32_t max_launches_per_kernel);
 int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 

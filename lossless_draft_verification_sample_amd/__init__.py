@@ -32,6 +32,7 @@ SampleOut = namedtuple("SampleOut",
                        "tokens num_accepted flags target_lse draft_lse overlap accept_hist",
                        defaults=(None, None))
 GreedyOut = namedtuple("GreedyOut", "tokens num_accepted flags accept_hist", defaults=(None,))
+CommitOut = namedtuple("CommitOut", "new_kv_len anchor n_free free_slots")
 
 
 class SpecVerifyError(RuntimeError):
@@ -189,6 +190,41 @@ def spec_verify_greedy(target_logits, draft_tokens, want_hist=False, out=None, s
         _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)), _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_greedy")
+    return out
+
+
+def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, out=None, stream=None):
+    """Chain KV-commit metadata of a verification round (see include/spec_verify.h).
+
+    tokens [B, gamma+1] and num_accepted [B] from spec_verify_sample or
+    spec_verify_greedy, kv_len [B] int32, slots [B, gamma+1] int32 or None.
+    Returns CommitOut(new_kv_len, anchor, n_free, free_slots); free_slots is
+    None when slots is None.
+    """
+    torch = _torch()
+    lib = _lib.load()
+    B, G1 = tokens.shape
+    gamma = G1 - 1
+    if tuple(num_accepted.shape) != (B,) or tuple(kv_len.shape) != (B,):
+        raise ValueError("num_accepted and kv_len must be [B]")
+    if slots is not None and tuple(slots.shape) != (B, G1):
+        raise ValueError("slots must be [B, gamma+1]")
+    dev = tokens.device
+    if out is None:
+        out = CommitOut(torch.empty((B,), dtype=torch.int32, device=dev),
+                        torch.empty((B,), dtype=torch.int32, device=dev),
+                        torch.empty((B,), dtype=torch.int32, device=dev),
+                        torch.empty((B, gamma), dtype=torch.int32, device=dev)
+                        if slots is not None else None)
+    rc = lib.spec_verify_commit(
+        _dev_ptr(tokens, "tokens", torch.int32), _dev_ptr(num_accepted, "num_accepted", torch.int32),
+        _dev_ptr(kv_len, "kv_len", torch.int32), _dev_ptr(slots, "slots", torch.int32), B, gamma,
+        _checked(out.new_kv_len, "new_kv_len", torch.int32, (B,)),
+        _checked(out.anchor, "anchor", torch.int32, (B,)),
+        _checked(out.n_free, "n_free", torch.int32, (B,)),
+        _checked(out.free_slots, "free_slots", torch.int32, (B, gamma)), _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_commit")
     return out
 
 

@@ -33,8 +33,9 @@ SV_K_DRAW = 1
 SV_K_GREEDY_ARGMAX = 2
 SV_K_GREEDY_SCAN = 3
 SV_K_OVERLAP = 4
-SV_NUM_KERNELS = 5
-KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap"]
+SV_K_COMMIT = 5
+SV_NUM_KERNELS = 6
+KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap", "commit"]
 
 
 class SvSampler(ctypes.Structure):
@@ -54,6 +55,7 @@ SIGNATURES = {
         _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]),
     "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                       _vp]),
+    "spec_verify_commit": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_strerror": (_c.c_char_p, [_c.c_int]),
     "spec_verify_profile_start": (_c.c_int, [_i32]),
     "spec_verify_profile_stop": (_c.c_int, [_vp, _vp]),

@@ -13,7 +13,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libspecverify.so"
-SOURCES = ["row_stats.hip", "verify.hip", "overlap.hip", "greedy.hip", "api.cpp"]
+SOURCES = ["row_stats.hip", "verify.hip", "overlap.hip", "greedy.hip", "commit.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -265,6 +265,22 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
   return SV_OK;
 }
 
+int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepted,
+                       const int32_t* kv_len, const int32_t* slots, int32_t B, int32_t gamma,
+                       int32_t* new_kv_len, int32_t* anchor, int32_t* n_free,
+                       int32_t* free_slots, void* stream) {
+  if (!out_tokens || !out_num_accepted || !kv_len || !new_kv_len || !anchor) return SV_EINVAL;
+  if (free_slots && !slots) return SV_EINVAL;
+  if (B < 1 || gamma < 1 || gamma > 63) return SV_EINVAL;
+  if ((int64_t)B * (gamma + 1) >= INT32_MAX) return SV_ESIZE;
+  hipStream_t st = (hipStream_t)stream;
+  sv::CommitArgs a{out_tokens, out_num_accepted, kv_len, slots, B, gamma,
+                   new_kv_len, anchor, n_free, free_slots};
+  ProfScope p(SV_K_COMMIT, st);
+  if (sv::launch_commit(a, st)) return SV_EHIP;
+  return SV_OK;
+}
+
 int spec_verify_profile_start(int32_t max_launches_per_kernel) {
   if (g_prof.on || max_launches_per_kernel < 1) return SV_EINVAL;
   for (int k = 0; k < SV_NUM_KERNELS; ++k) {

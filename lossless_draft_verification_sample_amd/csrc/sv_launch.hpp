@@ -85,10 +85,23 @@ struct GreedyArgs {
   uint32_t* accept_hist;        // [gamma+1] or nullptr
 };
 
+struct CommitArgs {
+  const int32_t* tokens;        // [B][gamma+1] verifier output
+  const int32_t* num_accepted;  // [B]
+  const int32_t* kv_len;        // [B] materialised rows before the round
+  const int32_t* slots;         // [B][gamma+1] or nullptr (only with free_slots)
+  int B, gamma;
+  int32_t* new_kv_len;          // [B]
+  int32_t* anchor;              // [B]
+  int32_t* n_free;              // [B] or nullptr
+  int32_t* free_slots;          // [B][gamma] or nullptr
+};
+
 int launch_row_stats(const RowStatsArgs& a, int dtype_bf16, int rows, hipStream_t s);
 int launch_draw(const DrawArgs& a, int B, hipStream_t s);
 int launch_overlap(const OverlapArgs& a, int bf16, int pairs, hipStream_t s);
 int launch_greedy_argmax(const GreedyArgs& a, hipStream_t s);
 int launch_greedy_scan(const GreedyArgs& a, hipStream_t s);
+int launch_commit(const CommitArgs& a, hipStream_t s);
 
 }  // namespace sv
