@@ -13,7 +13,10 @@ Parity status of each function (what pins it to something other than itself):
                      0.75/0.25/0, final law = p); alpha = 0.8 invariants;
                      closed form (1 - a^(g+1)) / (1 - a) and the survival form by
                      Monte Carlo; chi-square of emitted tokens against p.
-  verify_greedy      pinned: brute-force loop over small rows.
+  verify_greedy      pinned: brute-force loop over small rows (bans included).
+  verify_batch       pinned: each request equals the same request verified
+                     alone by verify_sample / verify_greedy on its own rows;
+                     a request with g_b proposals equals a gamma = g_b batch.
   first_token_law    pinned: the worked example's printed numbers.
   commit_chain       pinned: the running example of "Committing state after
                      rejection" (tests/golden/commit_example.json) and the
@@ -38,6 +41,7 @@ from .diagnostics import (  # noqa: F401
 from .philox import philox4x64_10, uniform, uniforms, word_to_uniform  # noqa: F401
 from .verifier import (  # noqa: F401
     BOUNDARY_EPS,
+    FLAG_BAD_PARAM,
     FLAG_EMPTY,
     FLAG_NONFINITE,
     FLAG_Q_ZERO,
@@ -49,9 +53,11 @@ from .verifier import (  # noqa: F401
     Sampler,
     accept,
     first_token_law,
+    greedy_argmax,
     residual_weights,
     row_distribution,
     sample_categorical,
+    verify_batch,
     verify_block,
     verify_greedy,
     verify_sample,

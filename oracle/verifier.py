@@ -44,6 +44,7 @@ FLAG_Q_ZERO = 2           # an examined proposal has q(x) = 0
 FLAG_NONFINITE = 4        # NaN or +inf in one of the request's rows
 FLAG_EMPTY = 8            # a row of the request has no admissible token
 FLAG_RESIDUAL_ZERO = 16   # residual mass was 0 at a rejection; drew from p instead
+FLAG_BAD_PARAM = 32       # a per-request draft length or sampler setting is out of range
 
 BOUNDARY_EPS = 1e-6       # a uniform this close to a decision edge is a boundary case
 
@@ -308,6 +309,26 @@ def verify_block(p_rows, q_rows, xs, u):
     return tokens, n, f, margin, acc_prob
 
 
+def greedy_argmax(z, banned_ids=()):
+    """Argmax of one target row for greedy verification ([DRAFT] "Greedy
+    verification"; [ATLAS] "Greedy, sampling and the real sampler": bans are
+    part of the real sampler). Admissible tokens are those not banned whose
+    logit is not NaN; the result is the lowest admissible id holding the
+    largest admissible logit (-inf included, so a row of -inf still has an
+    argmax), or -1 when nothing is admissible.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    adm = ~np.isnan(z)
+    for tok in banned_ids:
+        tok = int(tok)
+        if 0 <= tok < z.size:
+            adm[tok] = False
+    if not adm.any():
+        return -1
+    m = z[adm].max()
+    return int(np.flatnonzero(adm & (z == m))[0])
+
+
 @dataclass
 class GreedyResult:
     tokens: np.ndarray
@@ -316,12 +337,13 @@ class GreedyResult:
     argmax: np.ndarray            # [B, gamma+1] per-row argmax
 
 
-def verify_greedy(target, draft_tokens):
+def verify_greedy(target, draft_tokens, banned=None):
     """Greedy verification ([DRAFT] "Greedy verification"; [ATLAS] "Greedy,
     sampling and the real sampler"): keep proposals while they equal the target
     argmax of their row, emit the argmax at the first mismatch, or the bonus
-    argmax of row gamma when all match. np.argmax returns the first maximum,
-    i.e. the lowest token id on exact ties.
+    argmax of row gamma when all match. The argmax is greedy_argmax: lowest
+    token id on exact ties, banned ids (banned[b], -1 = padding) and NaN
+    excluded.
     """
     target = np.asarray(target, dtype=np.float64)
     draft_tokens = np.asarray(draft_tokens)
@@ -333,11 +355,12 @@ def verify_greedy(target, draft_tokens):
     am = np.zeros((B, G1), dtype=np.int32)
     for b in range(B):
         f = 0
+        bans = () if banned is None else [t for t in np.asarray(banned[b]).tolist() if t >= 0]
         for i in range(G1):
             row = target[b, i]
             if np.any(np.isnan(row) | (row == np.inf)):
                 f |= FLAG_NONFINITE
-            am[b, i] = int(np.argmax(row))
+            am[b, i] = greedy_argmax(row, bans)
         xs = [int(x) for x in draft_tokens[b]]
         if any(x < 0 or x >= V for x in xs):
             f |= FLAG_TOKEN_RANGE
@@ -348,9 +371,96 @@ def verify_greedy(target, draft_tokens):
                 break
             tokens[b, i] = xs[i]
         tokens[b, n] = am[b, n]
+        if am[b, n] < 0:
+            f |= FLAG_EMPTY
         num_acc[b] = n
         flags[b] = f
     return GreedyResult(tokens, num_acc, flags, am)
+
+
+def sampler_valid(s, allow_greedy):
+    """Range check of one sampler setting (temperature 0 only where a greedy
+    request is allowed)."""
+    T, k, P = _f32(s.temperature), int(s.top_k), _f32(s.top_p)
+    if not math.isfinite(T) or T < 0.0 or (T == 0.0 and not allow_greedy):
+        return False
+    return k >= 0 and 0.0 < P <= 1.0
+
+
+def verify_batch(target, draft, draft_tokens, uniforms, target_samplers, draft_samplers,
+                 banned=None, banned_draft=None, gammas=None):
+    """A mixed batch: per-request draft lengths, samplers and draft bans.
+
+    target [B, gamma+1, V], draft [B, gamma, V], draft_tokens [B, gamma] and
+    uniforms [B, gamma+1] as in verify_sample; target_samplers / draft_samplers
+    are lists of B Samplers; banned [B, n] bans the target rows (and the draft
+    rows unless banned_draft [B, m] is given, which then bans the draft rows);
+    gammas [B] gives each request's number of proposals g_b <= gamma (None: all
+    gamma). Request b uses target rows 0..g_b, draft rows 0..g_b-1, proposals
+    0..g_b-1, acceptance uniforms u[b, 0..g_b-1] and the final-draw uniform
+    u[b, gamma]. A target temperature of 0 makes the request greedy (its draft
+    rows and uniforms are unused): the walk of verify_greedy with
+    greedy_argmax. A draft length or sampler setting out of range gives flag
+    FLAG_BAD_PARAM, no accepted proposal and no token. lse of rows a request
+    does not use (and of every row of a greedy request) is NaN.
+
+    [ATLAS] "Implementation roadmap and tests" (continuous batching with
+    per-request metadata); [ATLAS] "Greedy, sampling and the real sampler".
+    """
+    target = np.asarray(target, dtype=np.float64)
+    draft = np.asarray(draft, dtype=np.float64)
+    draft_tokens = np.asarray(draft_tokens)
+    uniforms = np.asarray(uniforms, dtype=np.float64)
+    B, G1, V = target.shape
+    gamma = G1 - 1
+    tokens = np.full((B, G1), -1, dtype=np.int32)
+    num_acc = np.zeros(B, dtype=np.int32)
+    flags = np.zeros(B, dtype=np.uint32)
+    tlse = np.full((B, G1), np.nan)
+    dlse = np.full((B, gamma), np.nan)
+    boundary = np.zeros(B, dtype=bool)
+    acc_prob = np.full((B, gamma), np.nan)
+    margin = np.full(B, math.inf)
+    for b in range(B):
+        gb = gamma if gammas is None else int(gammas[b])
+        ts, ds = target_samplers[b], draft_samplers[b]
+        greedy = _f32(ts.temperature) == 0.0
+        if not (0 <= gb <= gamma) or not sampler_valid(ts, True) or (
+                not greedy and not sampler_valid(ds, False)):
+            flags[b] = FLAG_BAD_PARAM
+            continue
+        tb = () if banned is None else [t for t in np.asarray(banned[b]).tolist() if t >= 0]
+        db = tb if banned_draft is None else [t for t in np.asarray(banned_draft[b]).tolist()
+                                              if t >= 0]
+        xs = [int(x) for x in draft_tokens[b, :gb]]
+        if greedy:
+            r = verify_greedy(target[b:b + 1, :gb + 1], np.array([xs], dtype=np.int64).reshape(1, gb),
+                              None if banned is None else [tb])
+            tokens[b, :gb + 1] = r.tokens[0]
+            num_acc[b] = r.num_accepted[0]
+            flags[b] = r.flags[0]
+            continue
+        pt = [row_distribution(target[b, i], ts, tb) for i in range(gb + 1)]
+        qd = [row_distribution(draft[b, i], ds, db) for i in range(gb)]
+        f = 0
+        mg = math.inf
+        for d in pt + qd:
+            if d.nonfinite:
+                f |= FLAG_NONFINITE
+            if d.empty:
+                f |= FLAG_EMPTY
+            mg = min(mg, d.topp_margin)
+        tlse[b, :gb + 1] = [d.lse for d in pt]
+        dlse[b, :gb] = [d.lse for d in qd]
+        u = np.concatenate([uniforms[b, :gb], uniforms[b, gamma:gamma + 1]])
+        out, n, fb, bmg, ap = verify_block([d.p for d in pt], [d.p for d in qd], xs, u)
+        tokens[b, :gb + 1] = out
+        num_acc[b] = n
+        flags[b] = f | fb
+        margin[b] = min(mg, bmg)
+        boundary[b] = margin[b] <= BOUNDARY_EPS
+        acc_prob[b, :gb] = ap
+    return SampleResult(tokens, num_acc, flags, tlse, dlse, boundary, acc_prob, margin)
 
 
 def first_token_law(p, q):
