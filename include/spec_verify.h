@@ -154,12 +154,20 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
  * emits that row's argmax, and if all gamma match the argmax of row gamma is
  * appended. Needs no workspace: out_tokens doubles as scratch.
  *   target_logits [B][gamma+1][V], draft_tokens [B][gamma];
+ *   banned_ids [B][n_banned] ids that are never an argmax (the sampler's bans
+ *   are part of greedy decoding too: "Speculative Decoding - Turn guesses into
+ *   parallel work", section "Greedy, sampling and the real sampler"); same list
+ *   rules as for spec_verify_sample; NULL only when n_banned == 0;
  *   out_tokens [B][gamma+1] (n matches, argmax, then -1), out_num_accepted [B],
- *   out_flags [B] or NULL (SV_FLAG_TOKEN_RANGE, SV_FLAG_NONFINITE),
+ *   out_flags [B] or NULL (SV_FLAG_TOKEN_RANGE, SV_FLAG_NONFINITE, and
+ *   SV_FLAG_EMPTY when the emitted token's row has no admissible id: that token
+ *   is then -1),
  *   out_accept_hist [gamma+1] or NULL: accepted-prefix histogram of the call,
  *   as for spec_verify_sample.
- * NaN logits are ignored by the argmax and flagged. */
+ * NaN logits are not candidates and are flagged; a row whose admissible
+ * logits are all -inf has the lowest such id as its argmax. */
 int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,
+                       const int32_t* banned_ids, int32_t n_banned,
                        int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
                        int32_t* out_num_accepted, uint32_t* out_flags,
                        uint32_t* out_accept_hist, void* stream);

@@ -165,15 +165,19 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
     return out
 
 
-def spec_verify_greedy(target_logits, draft_tokens, want_hist=False, out=None, stream=None):
-    """Greedy verification (see include/spec_verify.h). Returns
-    GreedyOut(tokens, num_accepted, flags, accept_hist)."""
+def spec_verify_greedy(target_logits, draft_tokens, banned_ids=None, want_hist=False, out=None,
+                       stream=None):
+    """Greedy verification (see include/spec_verify.h); banned_ids [B, n] int32
+    or None. Returns GreedyOut(tokens, num_accepted, flags, accept_hist)."""
     torch = _torch()
     lib = _lib.load()
     B, G1, V = target_logits.shape
     gamma = G1 - 1
     if tuple(draft_tokens.shape) != (B, gamma):
         raise ValueError("draft_tokens must be [B, gamma]")
+    n_banned = 0 if banned_ids is None else int(banned_ids.shape[1])
+    if banned_ids is not None and tuple(banned_ids.shape) != (B, n_banned):
+        raise ValueError("banned_ids must be [B, n_banned]")
     dt = _dtype_code(target_logits)
     dev = target_logits.device
     if out is None:
@@ -183,7 +187,8 @@ def spec_verify_greedy(target_logits, draft_tokens, want_hist=False, out=None, s
                         torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None)
     rc = lib.spec_verify_greedy(
         _dev_ptr(target_logits, "target_logits"), dt,
-        _dev_ptr(draft_tokens, "draft_tokens", torch.int32), B, gamma, V,
+        _dev_ptr(draft_tokens, "draft_tokens", torch.int32),
+        _dev_ptr(banned_ids, "banned_ids", torch.int32), n_banned, B, gamma, V,
         _dev_ptr(out.tokens, "out_tokens", torch.int32),
         _dev_ptr(out.num_accepted, "out_num_accepted", torch.int32),
         _dev_ptr(out.flags, "out_flags", torch.int32),

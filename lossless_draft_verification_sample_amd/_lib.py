@@ -53,8 +53,8 @@ SIGNATURES = {
     "spec_verify_sample": (_c.c_int, [
         _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
         _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]),
-    "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                                      _vp]),
+    "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                      _vp, _vp, _vp]),
     "spec_verify_commit": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_strerror": (_c.c_char_p, [_c.c_int]),
     "spec_verify_profile_start": (_c.c_int, [_i32]),

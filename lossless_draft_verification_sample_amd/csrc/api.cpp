@@ -242,17 +242,20 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
 }
 
 int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,
+                       const int32_t* banned_ids, int32_t n_banned,
                        int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
                        int32_t* out_num_accepted, uint32_t* out_flags,
                        uint32_t* out_accept_hist, void* stream) {
   if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
   if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return SV_EINVAL;
+  if (n_banned < 0 || n_banned > SV_MAX_BANNED || (n_banned > 0 && !banned_ids)) return SV_EINVAL;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if ((uintptr_t)target_logits % es) return SV_EINVAL;
   if ((int64_t)B * (gamma + 1) >= INT32_MAX) return SV_ESIZE;
   hipStream_t st = (hipStream_t)stream;
   sv::GreedyArgs a{target_logits, dtype == SV_BF16, gamma, V, B, draft_tokens,
+                   n_banned ? banned_ids : nullptr, n_banned,
                    out_tokens, out_num_accepted, out_flags, out_accept_hist};
   {
     ProfScope p(SV_K_GREEDY_ARGMAX, st);

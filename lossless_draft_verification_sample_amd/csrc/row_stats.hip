@@ -42,6 +42,7 @@
 // i < gamma: p_i(x_i); draft row i: q_i(x_i)), which is all the acceptance walk
 // needs from the row.
 
+#include "sv_bans.hpp"
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 
@@ -66,9 +67,6 @@ constexpr uint32_t HB_BINS = HB_NEG + HB_WIN + 1u;
 constexpr int HB_RANKS = 2 * HB_WIN + 1;      // value-ordered ranks: +window, zero, -window
 constexpr uint32_t TINY_MAX = 64;             // tiny values tracked exactly per row
 
-// LDS hash set of a request's banned ids (linear probing, at most half full).
-constexpr uint32_t HT_SLOTS = 4096;
-constexpr uint32_t HT_EMPTY = 0xFFFFFFFFu;
 static_assert(HT_SLOTS >= 2 * 2048 && HT_SLOTS <= HB_BINS, "ban hash set size");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -147,49 +145,6 @@ __device__ __forceinline__ void hb_count_one(uint32_t bits, RowShared& sh) {
     atomicAdd(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
   else
     hb_classify_slow(bits, sh);
-}
-
-// ------------------------------------------------------------------ banned ids
-
-__device__ __forceinline__ uint32_t ht_slot(int32_t id) {
-  return ((uint32_t)id * 0x9E3779B1u) >> 20;   // multiplicative hash, 12 bits
-}
-
-// Inserts the valid ids of a raw ban list into the LDS hash set `tab` (all
-// slots HT_EMPTY beforehand). Bit k of the result is set when this thread's
-// k-th id (list index threadIdx.x + k * RS_THREADS) was the copy that entered
-// the set, so every distinct id has exactly one owner. `first` is list element
-// threadIdx.x, loaded by the caller. Sets *xban when the list holds `x`.
-__device__ __forceinline__ uint32_t ht_build(uint32_t* tab, const int32_t* bl, int nb, int V,
-                                             int32_t first, int32_t x, uint32_t* xban) {
-  uint32_t own = 0u;
-  int k = 0;
-  for (int j = threadIdx.x; j < nb; j += RS_THREADS, ++k) {
-    const int32_t id = j == (int)threadIdx.x ? first : bl[j];
-    if (id < 0 || id >= V) continue;
-    if (id == x) *xban = 1u;
-    uint32_t slot = ht_slot(id);
-    while (true) {
-      const uint32_t old = atomicCAS(&tab[slot], HT_EMPTY, (uint32_t)id);
-      if (old == HT_EMPTY) {
-        own |= 1u << k;
-        break;
-      }
-      if (old == (uint32_t)id) break;
-      slot = (slot + 1u) & (HT_SLOTS - 1u);
-    }
-  }
-  return own;
-}
-
-__device__ __forceinline__ bool ht_has(const uint32_t* tab, int32_t id) {
-  uint32_t slot = ht_slot(id);
-  while (true) {
-    const uint32_t v = tab[slot];
-    if (v == (uint32_t)id) return true;
-    if (v == HT_EMPTY) return false;
-    slot = (slot + 1u) & (HT_SLOTS - 1u);
-  }
 }
 
 // ------------------------------------------------------------------ generic path

@@ -79,6 +79,8 @@ struct GreedyArgs {
   int bf16;
   int gamma, V, B;
   const int32_t* draft_tokens;
+  const int32_t* banned;        // [B][n_banned] raw ban lists, or nullptr
+  int n_banned;
   int32_t* out_tokens;
   int32_t* out_num_accepted;
   uint32_t* out_flags;

@@ -131,11 +131,13 @@ def compare_sample(got, ref, reqs, lse_tol=1e-5, check_flags=True, where=""):
     return int(bnd.sum())
 
 
-def run_gpu_greedy(target_t, xs):
+def run_gpu_greedy(target_t, xs, banned=None):
     import torch
     import lossless_draft_verification_sample_amd as sv
     dev = target_t.device
-    out = sv.spec_verify_greedy(target_t, torch.from_numpy(np.ascontiguousarray(xs, dtype=np.int32)).to(dev))
+    out = sv.spec_verify_greedy(
+        target_t, torch.from_numpy(np.ascontiguousarray(xs, dtype=np.int32)).to(dev),
+        banned_ids=None if banned is None else torch.from_numpy(np.ascontiguousarray(banned, dtype=np.int32)).to(dev))
     torch.cuda.synchronize()
     return (out.tokens.cpu().numpy(), out.num_accepted.cpu().numpy(),
             out.flags.cpu().numpy().astype(np.uint32))

@@ -106,16 +106,18 @@ def test_sample_argument_errors(lib):
 def test_greedy_argument_errors(lib):
     from lossless_draft_verification_sample_amd import _lib as L
     g = lib.spec_verify_greedy
-    assert g(None, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, None, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 3, 10, None, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 3, 10, FAKE, None, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 5, FAKE, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EDTYPE
-    assert g(FAKE, 1, FAKE, 0, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 0, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2, 3, 0, FAKE, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE + 1, 1, FAKE, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
-    assert g(FAKE, 1, FAKE, 2**30, 3, 10, FAKE, FAKE, None, None, None) == L.SV_ESIZE
+    assert g(None, 1, FAKE, None, 0, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, None, None, 0, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, None, 0, 2, 3, 10, None, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, None, 0, 2, 3, 10, FAKE, None, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 5, FAKE, None, 0, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EDTYPE
+    assert g(FAKE, 1, FAKE, None, 0, 0, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, None, 0, 2, 0, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, None, 0, 2, 3, 0, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE + 1, 1, FAKE, None, 0, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, None, 0, 2**30, 3, 10, FAKE, FAKE, None, None, None) == L.SV_ESIZE
+    assert g(FAKE, 1, FAKE, None, 3, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
+    assert g(FAKE, 1, FAKE, FAKE, 2049, 2, 3, 10, FAKE, FAKE, None, None, None) == L.SV_EINVAL
 
 
 def test_commit_argument_errors(lib):

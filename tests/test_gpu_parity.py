@@ -122,6 +122,40 @@ def test_greedy_shapes_and_ties(dtype, V):
     assert np.array_equal(fl, ref.flags)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_greedy_with_bans(dtype):
+    import torch
+    from lossless_draft_verification_sample_amd import synth
+    rng = np.random.default_rng(41)
+    B, gamma, V = 6, 3, 2001                         # a full ban list fits the 2048 limit
+    vals = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0, 2.0, 4.0], np.float32), size=(B, gamma + 1, V))
+    vals[1, 0, :] = -np.inf                          # -inf row: lowest admissible id
+    vals[4, :, :V // 2] = -np.inf
+    ref0 = oracle.verify_greedy(vals.astype(np.float64), np.zeros((B, gamma), np.int32))
+    banned = rng.integers(-2, V + 2, (B, 40)).astype(np.int32)
+    banned[0, :4] = ref0.argmax[0, :4]               # ban the unbanned argmax of each row
+    banned[1, :3] = [0, 1, 2]                        # the first -inf ids
+    banned[2] = -1
+    banned[3, 0] = ref0.argmax[3, 0]
+    banned5 = np.arange(V, dtype=np.int32)           # request 5: every id banned
+    full = np.full((B, V), -1, np.int32)
+    full[:, :40] = banned
+    full[5] = banned5
+    bits = synth.f32_to_bf16_bits(vals)
+    t = pu.logits_tensor(vals, bits, dtype, torch.device("cuda:0"))
+    refb = oracle.verify_greedy(vals.astype(np.float64), np.zeros((B, gamma), np.int32), full)
+    xs = np.where(rng.random((B, gamma)) < 0.7, refb.argmax[:, :gamma],
+                  rng.integers(0, V, (B, gamma))).astype(np.int32)
+    ref = oracle.verify_greedy(vals.astype(np.float64), xs, full)
+    tok, n, fl = pu.run_gpu_greedy(t, xs, full)
+    assert np.array_equal(tok, ref.tokens)
+    assert np.array_equal(n, ref.num_accepted)
+    assert np.array_equal(fl, ref.flags)
+    assert fl[5] & oracle.FLAG_EMPTY and tok[5, n[5]] == -1
+    for b in range(5):
+        assert tok[b, n[b]] not in set(full[b].tolist())
+
+
 def test_greedy_nonfinite_flag():
     import torch
     B, gamma, V = 3, 2, 300
