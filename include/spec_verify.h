@@ -82,8 +82,41 @@ typedef struct {
 #define SV_FLAG_NONFINITE 4u      /* NaN or +inf in one of the request's rows */
 #define SV_FLAG_EMPTY 8u          /* a row has no admissible token; see out_tokens */
 #define SV_FLAG_RESIDUAL_ZERO 16u /* residual mass was 0 at a rejection; drawn from p */
+#define SV_FLAG_BAD_PARAM 32u     /* a per-request setting of sv_requests is out of range */
 
 #define SV_MAX_BANNED 2048 /* largest n_banned accepted */
+
+/* Per-request settings of a mixed batch ("Speculative Decoding - Turn guesses
+ * into parallel work", section "Implementation roadmap and tests": continuous
+ * batching keeps per-request metadata on the GPU). Every array is DEVICE
+ * memory of B entries (banned_draft: B rows of n_banned_draft); a NULL array
+ * keeps the call-wide value. Passed to spec_verify_sample by host pointer.
+ *   gamma         proposals of each request, 0 <= gamma[b] <= gamma: request b
+ *                 uses target rows 0..gamma[b], draft rows and draft tokens
+ *                 0..gamma[b]-1, acceptance uniforms (slots) 0..gamma[b]-1 and
+ *                 the final-draw uniform of slot gamma; its out_tokens row has
+ *                 at most gamma[b]+1 tokens.
+ *   target        target sampler of each request. Temperature 0 makes the
+ *                 request greedy: proposals are kept while they equal the
+ *                 argmax of their target row (banned_ids applied, NaN excluded,
+ *                 lowest id on ties), as in spec_verify_greedy; its draft rows
+ *                 and uniforms are not read.
+ *   draft         draft sampler of each request (ignored for greedy requests).
+ *   banned_draft  [B][n_banned_draft] bans of the draft rows; banned_ids then
+ *                 applies to the target rows only (same list rules).
+ * A request whose gamma[b] or sampler fields are out of range (the ranges of
+ * sv_sampler; temperature 0 only as a target) is not verified: flag
+ * SV_FLAG_BAD_PARAM, no accepted proposal, out_tokens row all -1. Rows a
+ * request does not use report NaN in out_target_lse / out_draft_lse, and so
+ * do the rows of greedy requests; out_overlap is NaN at positions a request
+ * does not have and for greedy requests. */
+typedef struct {
+  const int32_t* gamma;
+  const sv_sampler* target;
+  const sv_sampler* draft;
+  const int32_t* banned_draft;
+  int32_t n_banned_draft;
+} sv_requests;
 
 /* Workspace bytes needed by spec_verify_sample for these sizes (0 on bad sizes;
  * n_banned is validated but does not change the size). The workspace needs no
@@ -102,6 +135,8 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
  *                  row of the request; -1 or any id outside [0, V) is padding;
  *                  duplicates are allowed. NULL only when n_banned == 0.
  *   target, draft  sampler settings for p and q respectively.
+ *   requests       per-request settings of a mixed batch (sv_requests above),
+ *                  or NULL for a batch that shares gamma, samplers and bans.
  *   seed, offset   select the uniforms when `uniforms` is NULL: for request b
  *                  and slot j (j < gamma: acceptance of proposal j; j == gamma:
  *                  the single final draw) u = ((r >> 11) + 1) * 2^-53 with r the
@@ -142,7 +177,8 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
 int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype dtype,
                        const int32_t* draft_tokens, const int32_t* banned_ids,
                        int32_t n_banned, int32_t B, int32_t gamma, int32_t V,
-                       sv_sampler target, sv_sampler draft, uint64_t seed, uint64_t offset,
+                       sv_sampler target, sv_sampler draft, const sv_requests* requests,
+                       uint64_t seed, uint64_t offset,
                        const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
                        uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
                        double* out_overlap, uint32_t* out_accept_hist,
@@ -176,6 +212,8 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
  * Speculative Decoding: Useful Tokens, Correct State", sections "Committed
  * tokens versus cached states" and "Committing state after rejection"), from
  * the outputs of spec_verify_sample or spec_verify_greedy, on the same stream.
+ * gamma_b [B] (device) gives each request's number of proposals as in
+ * sv_requests (NULL: all gamma); below, gamma stands for gamma_b[b].
  * Convention: before the round request b has kv_len[b] = K materialised target
  * KV rows, and its last committed token (the anchor) is pending: it has no row
  * yet. The verification pass ran the gamma+1 inputs (anchor, x_0, ...,
@@ -191,12 +229,14 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
  * Pointers: out_tokens [B][gamma+1], out_num_accepted [B], kv_len [B] (inputs,
  * device); new_kv_len [B], anchor [B] (required outputs); n_free [B] or NULL;
  * free_slots [B][gamma] or NULL, which needs slots [B][gamma+1]. A request
- * whose accepted count lies outside [0, gamma] is left unchanged (new_kv_len =
+ * whose accepted count lies outside [0, gamma_b[b]], or whose gamma_b[b] lies
+ * outside [0, gamma], is left unchanged (new_kv_len =
  * kv_len, anchor -1, nothing freed). The caller keeps kv_len + gamma + 1 within
  * int32. Returns SV_EINVAL for a missing required pointer, free_slots without
  * slots, B < 1 or gamma outside [1, 63]; SV_ESIZE if B*(gamma+1) overflows. */
 int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepted,
-                       const int32_t* kv_len, const int32_t* slots, int32_t B, int32_t gamma,
+                       const int32_t* kv_len, const int32_t* slots, const int32_t* gamma_b,
+                       int32_t B, int32_t gamma,
                        int32_t* new_kv_len, int32_t* anchor, int32_t* n_free,
                        int32_t* free_slots, void* stream);
 
@@ -215,7 +255,8 @@ const char* spec_verify_strerror(int status);
 #define SV_K_GREEDY_SCAN 3
 #define SV_K_OVERLAP 4
 #define SV_K_COMMIT 5
-#define SV_NUM_KERNELS 6
+#define SV_K_GREEDY_ROWS 6
+#define SV_NUM_KERNELS 7
 int spec_verify_profile_start(int32_t max_launches_per_kernel);
 int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     SV_ESIZE,
     SV_EWORKSPACE,
     SV_F32,
+    SV_FLAG_BAD_PARAM,
     SV_FLAG_EMPTY,
     SV_FLAG_NONFINITE,
     SV_FLAG_Q_ZERO,
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     SV_FLAG_TOKEN_RANGE,
     SV_MAX_BANNED,
     SV_OK,
+    SvRequests,
     SvSampler,
 )
 
@@ -33,6 +35,10 @@ SampleOut = namedtuple("SampleOut",
                        defaults=(None, None))
 GreedyOut = namedtuple("GreedyOut", "tokens num_accepted flags accept_hist", defaults=(None,))
 CommitOut = namedtuple("CommitOut", "new_kv_len anchor n_free free_slots")
+# Per-request settings of a mixed batch (see sv_requests in include/spec_verify.h):
+# gamma [B] int32, target / draft [B, 12] uint8 sv_sampler records (sampler_array),
+# banned_draft [B, m] int32; None keeps the call-wide value.
+Requests = namedtuple("Requests", "gamma target draft banned_draft", defaults=(None,) * 4)
 
 
 class SpecVerifyError(RuntimeError):
@@ -84,6 +90,41 @@ def _sampler(s):
     return SvSampler(float(t), int(k), float(p))
 
 
+def sampler_array(samplers, device):
+    """[B] sv_sampler records (float temperature, int32 top_k, float top_p) on
+    `device`, as a [B, 12] uint8 tensor, from (temperature, top_k, top_p)
+    tuples, dicts or SvSampler."""
+    import numpy as np
+    torch = _torch()
+    rec = np.zeros(len(samplers), dtype=[("t", "<f4"), ("k", "<i4"), ("p", "<f4")])
+    for j, smp in enumerate(samplers):
+        c = _sampler(smp)
+        rec[j] = (c.temperature, c.top_k, c.top_p)
+    return torch.from_numpy(rec.view(np.uint8).reshape(len(samplers), 12).copy()).to(device)
+
+
+def _requests(req, B):
+    """ctypes sv_requests for a Requests tuple (or None)."""
+    import ctypes
+    if req is None:
+        return None
+    torch = _torch()
+    for name, t in (("target", req.target), ("draft", req.draft)):
+        if t is not None and (tuple(t.shape) != (B, 12) or t.dtype != torch.uint8):
+            raise ValueError(f"requests.{name} must be a [B, 12] uint8 tensor (sampler_array)")
+    if req.gamma is not None and tuple(req.gamma.shape) != (B,):
+        raise ValueError("requests.gamma must be [B]")
+    nbd = 0
+    if req.banned_draft is not None:
+        nbd = int(req.banned_draft.shape[1])
+        if tuple(req.banned_draft.shape) != (B, nbd):
+            raise ValueError("requests.banned_draft must be [B, n]")
+    r = SvRequests(_dev_ptr(req.gamma, "requests.gamma", torch.int32),
+                   _dev_ptr(req.target, "requests.target"), _dev_ptr(req.draft, "requests.draft"),
+                   _dev_ptr(req.banned_draft, "requests.banned_draft", torch.int32), nbd)
+    return ctypes.byref(r), r
+
+
 def _stream_handle(stream):
     torch = _torch()
     if stream is None:
@@ -102,7 +143,7 @@ def spec_verify_workspace_bytes(B, gamma, V, n_banned=0):
 def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler=(1.0, 0, 1.0),
                        draft_sampler=(1.0, 0, 1.0), banned_ids=None, seed=0, offset=0,
                        uniforms=None, want_lse=True, want_overlap=False, want_hist=False,
-                       workspace=None, out=None, stream=None):
+                       requests=None, workspace=None, out=None, stream=None):
     """Speculative-sampling verification of a batch (see include/spec_verify.h).
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (bf16 or fp32),
@@ -111,7 +152,8 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
     Samplers are (temperature, top_k, top_p) tuples, dicts or SvSampler.
     want_overlap adds the per-position overlaps [B, gamma] (float64; one more
     read of the rows), want_hist the accepted-prefix histogram [gamma+1]
-    (int32 storage of the library's uint32 counts).
+    (int32 storage of the library's uint32 counts). requests: a Requests tuple
+    of per-request settings (mixed batch) or None.
     Returns SampleOut(tokens, num_accepted, flags, target_lse, draft_lse,
     overlap, accept_hist).
     """
@@ -142,6 +184,7 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
             torch.empty((B, gamma), dtype=torch.float64, device=dev) if want_overlap else None,
             torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None,
         )
+    req = _requests(requests, B)
     need = lib.spec_verify_workspace_bytes(B, gamma, V, n_banned)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -149,7 +192,8 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
         _dev_ptr(target_logits, "target_logits"), _dev_ptr(draft_logits, "draft_logits"), dt,
         _dev_ptr(draft_tokens, "draft_tokens", torch.int32),
         _dev_ptr(banned_ids, "banned_ids", torch.int32), n_banned, B, gamma, V,
-        _sampler(target_sampler), _sampler(draft_sampler), int(seed), int(offset),
+        _sampler(target_sampler), _sampler(draft_sampler), None if req is None else req[0],
+        int(seed), int(offset),
         _dev_ptr(uniforms, "uniforms", torch.float64),
         _dev_ptr(out.tokens, "out_tokens", torch.int32),
         _dev_ptr(out.num_accepted, "out_num_accepted", torch.int32),
@@ -198,11 +242,13 @@ def spec_verify_greedy(target_logits, draft_tokens, banned_ids=None, want_hist=F
     return out
 
 
-def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, out=None, stream=None):
+def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, gamma_b=None, out=None,
+                       stream=None):
     """Chain KV-commit metadata of a verification round (see include/spec_verify.h).
 
     tokens [B, gamma+1] and num_accepted [B] from spec_verify_sample or
-    spec_verify_greedy, kv_len [B] int32, slots [B, gamma+1] int32 or None.
+    spec_verify_greedy, kv_len [B] int32, slots [B, gamma+1] int32 or None,
+    gamma_b [B] int32 proposals per request or None.
     Returns CommitOut(new_kv_len, anchor, n_free, free_slots); free_slots is
     None when slots is None.
     """
@@ -223,7 +269,8 @@ def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, out=None, strea
                         if slots is not None else None)
     rc = lib.spec_verify_commit(
         _dev_ptr(tokens, "tokens", torch.int32), _dev_ptr(num_accepted, "num_accepted", torch.int32),
-        _dev_ptr(kv_len, "kv_len", torch.int32), _dev_ptr(slots, "slots", torch.int32), B, gamma,
+        _dev_ptr(kv_len, "kv_len", torch.int32), _dev_ptr(slots, "slots", torch.int32),
+        _checked(gamma_b, "gamma_b", torch.int32, (B,)), B, gamma,
         _checked(out.new_kv_len, "new_kv_len", torch.int32, (B,)),
         _checked(out.anchor, "anchor", torch.int32, (B,)),
         _checked(out.n_free, "n_free", torch.int32, (B,)),

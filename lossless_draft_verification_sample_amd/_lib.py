@@ -25,6 +25,7 @@ SV_FLAG_Q_ZERO = 2
 SV_FLAG_NONFINITE = 4
 SV_FLAG_EMPTY = 8
 SV_FLAG_RESIDUAL_ZERO = 16
+SV_FLAG_BAD_PARAM = 32
 
 SV_MAX_BANNED = 2048
 
@@ -34,13 +35,22 @@ SV_K_GREEDY_ARGMAX = 2
 SV_K_GREEDY_SCAN = 3
 SV_K_OVERLAP = 4
 SV_K_COMMIT = 5
-SV_NUM_KERNELS = 6
-KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap", "commit"]
+SV_K_GREEDY_ROWS = 6
+SV_NUM_KERNELS = 7
+KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap", "commit",
+                "greedy_rows"]
 
 
 class SvSampler(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
                 ("top_p", ctypes.c_float)]
+
+
+class SvRequests(ctypes.Structure):
+    """sv_requests: device pointers (as integers) of per-request arrays."""
+    _fields_ = [("gamma", ctypes.c_void_p), ("target", ctypes.c_void_p),
+                ("draft", ctypes.c_void_p), ("banned_draft", ctypes.c_void_p),
+                ("n_banned_draft", ctypes.c_int32)]
 
 
 _c = ctypes
@@ -52,10 +62,12 @@ SIGNATURES = {
     "spec_verify_workspace_bytes": (_c.c_size_t, [_i32, _i32, _i32, _i32]),
     "spec_verify_sample": (_c.c_int, [
         _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
-        _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]),
+        _c.POINTER(SvRequests), _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        _c.c_size_t, _vp]),
     "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                       _vp, _vp, _vp]),
-    "spec_verify_commit": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "spec_verify_commit": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp,
+                                      _vp]),
     "spec_verify_strerror": (_c.c_char_p, [_c.c_int]),
     "spec_verify_profile_start": (_c.c_int, [_i32]),
     "spec_verify_profile_stop": (_c.c_int, [_vp, _vp]),

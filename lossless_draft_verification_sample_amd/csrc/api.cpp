@@ -136,7 +136,8 @@ const char* spec_verify_strerror(int status) {
 int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype dtype,
                        const int32_t* draft_tokens, const int32_t* banned_ids,
                        int32_t n_banned, int32_t B, int32_t gamma, int32_t V,
-                       sv_sampler target, sv_sampler draft, uint64_t seed, uint64_t offset,
+                       sv_sampler target, sv_sampler draft, const sv_requests* requests,
+                       uint64_t seed, uint64_t offset,
                        const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
                        uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
                        double* out_overlap, uint32_t* out_accept_hist,
@@ -147,6 +148,18 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
   if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return SV_EINVAL;
   if (n_banned < 0 || n_banned > SV_MAX_BANNED || (n_banned > 0 && !banned_ids)) return SV_EINVAL;
   if (!sampler_ok(target) || !sampler_ok(draft)) return SV_EINVAL;
+  sv::ReqArgs req{};
+  if (requests) {
+    if (requests->n_banned_draft < 0 || requests->n_banned_draft > SV_MAX_BANNED ||
+        (requests->n_banned_draft > 0 && !requests->banned_draft))
+      return SV_EINVAL;
+    req.gammas = requests->gamma;
+    req.ts = (const sv::SamplerReq*)requests->target;
+    req.ds = (const sv::SamplerReq*)requests->draft;
+    // a draft list (even an empty one) replaces banned_ids for the draft rows
+    req.banned_d = requests->banned_draft;
+    req.n_banned_d = requests->banned_draft ? requests->n_banned_draft : 0;
+  }
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)target_logits % es) || ((uintptr_t)draft_logits % es)) return SV_EINVAL;
   Layout L;
@@ -180,11 +193,19 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.tickets = tickets;
     a.ov_tickets = out_overlap ? ov_tickets : nullptr;
     a.accept_hist = out_accept_hist;
+    a.req = req;
     a.out_tlse = out_target_lse;
     a.out_dlse = out_draft_lse;
     a.force_generic = 0;
-    ProfScope p(SV_K_ROW_STATS, st);
-    if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
+    {
+      ProfScope p(SV_K_ROW_STATS, st);
+      if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
+    }
+    if (req.ts) {
+      // target rows of greedy requests: their argmax replaces the RowStat
+      ProfScope p(SV_K_GREEDY_ROWS, st);
+      if (sv::launch_greedy_rows(a, bf16, B, st)) return SV_EHIP;
+    }
   }
   {
     sv::DrawArgs a{};
@@ -198,8 +219,9 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.nsub = L.nsub;
     a.spw = L.spw;
     a.nwg = L.nwg;
-    a.t_temp = target.temperature;
-    a.d_temp = draft.temperature;
+    a.st = to_dev(target);
+    a.sd = to_dev(draft);
+    a.req = req;
     a.draft_tokens = draft_tokens;
     a.banned = bans;
     a.n_banned = n_banned;
@@ -227,8 +249,9 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.nsub = L.nsub;
     a.spp = L.ov_spp;
     a.parts = L.ov_parts;
-    a.t_temp = target.temperature;
-    a.d_temp = draft.temperature;
+    a.st = to_dev(target);
+    a.sd = to_dev(draft);
+    a.req = req;
     a.banned = bans;
     a.n_banned = n_banned;
     a.stats = stats;
@@ -269,7 +292,8 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
 }
 
 int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepted,
-                       const int32_t* kv_len, const int32_t* slots, int32_t B, int32_t gamma,
+                       const int32_t* kv_len, const int32_t* slots, const int32_t* gamma_b,
+                       int32_t B, int32_t gamma,
                        int32_t* new_kv_len, int32_t* anchor, int32_t* n_free,
                        int32_t* free_slots, void* stream) {
   if (!out_tokens || !out_num_accepted || !kv_len || !new_kv_len || !anchor) return SV_EINVAL;
@@ -278,7 +302,7 @@ int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepte
   if ((int64_t)B * (gamma + 1) >= INT32_MAX) return SV_ESIZE;
   hipStream_t st = (hipStream_t)stream;
   sv::CommitArgs a{out_tokens, out_num_accepted, kv_len, slots, B, gamma,
-                   new_kv_len, anchor, n_free, free_slots};
+                   new_kv_len, anchor, n_free, free_slots, gamma_b};
   ProfScope p(SV_K_COMMIT, st);
   if (sv::launch_commit(a, st)) return SV_EHIP;
   return SV_OK;

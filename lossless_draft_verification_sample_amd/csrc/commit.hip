@@ -27,20 +27,22 @@ __global__ __launch_bounds__(CM_THREADS) void commit_kernel(CommitArgs a) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int b = blockIdx.x * CM_NW + (int)threadIdx.x / WAVE;
   if (b >= a.B) return;
-  const int g = a.gamma, G1 = g + 1;
+  const int G1 = a.gamma + 1;
+  const int g = a.gammas ? a.gammas[b] : a.gamma;   // the request's proposals
   const int n = a.num_accepted[b];
   const int32_t k = a.kv_len[b];
   const int32_t tok = lane < G1 ? a.tokens[(int64_t)b * G1 + lane] : -1;
   const int32_t slot = (a.free_slots && lane < G1) ? a.slots[(int64_t)b * G1 + lane] : -1;
-  // an accepted count outside [0, gamma] is not a verifier output: the
-  // request is left as it was (nothing committed, nothing freed, no anchor)
-  const bool ok = n >= 0 && n <= g;
+  // an accepted count outside [0, g] (or a g outside [0, gamma]) is not a
+  // verifier output: the request is left as it was (nothing committed,
+  // nothing freed, no anchor)
+  const bool ok = g >= 0 && g <= a.gamma && n >= 0 && n <= g;
   const int nn = ok ? n : 0;
   const int32_t anchor = __shfl(tok, nn, WAVE);
   if (a.free_slots) {
     const int nf = ok ? g - n : 0;
     const int32_t moved = __shfl(slot, min(nn + 1 + lane, WAVE - 1), WAVE);
-    if (lane < g) a.free_slots[(int64_t)b * g + lane] = lane < nf ? moved : -1;
+    if (lane < a.gamma) a.free_slots[(int64_t)b * a.gamma + lane] = lane < nf ? moved : -1;
   }
   if (lane == 0) {
     a.new_kv_len[b] = ok ? k + 1 + n : k;

@@ -39,7 +39,9 @@ constexpr int OV_QCAP = 4 * WAVE;   // queued kept tokens per wave: one batch of
 struct OverlapShared {
   double etab[256];
   QueuedTok q[OV_NW][OV_QCAP];
-  uint32_t bm[OV_SPW_MAX * DRAW_SUB / 32];
+  uint32_t bm[OV_SPW_MAX * DRAW_SUB / 32];    // bans of the target row (of both rows
+                                            // unless the draft rows have their own list)
+  uint32_t bmd[OV_SPW_MAX * DRAW_SUB / 32];   // the draft rows' own bans (mixed batches)
   double w[OV_NW];
 };
 
@@ -52,6 +54,8 @@ struct OvPair {
   RowStat ts, ds;
   double tinv, dinv;  // 1/T of both rows
   int V, tok0, nsl, nb;
+  int dnb;            // bans in the draft rows' own list
+  bool sep;           // the draft rows have their own ban list (bmd)
   bool vec;
 };
 
@@ -67,6 +71,13 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
     const double ld = fma((double)zd, r.dinv, -r.ds.lse);
     return exp_tab(fmin(lt, ld), sh.etab);
   };
+  // ban bits of the eight tokens at offset o of the workgroup's range, per side
+  auto tbits = [&](int o) -> uint32_t { return r.nb > 0 ? bm_group(sh.bm, o) : 0u; };
+  auto dbits = [&](int o) -> uint32_t {
+    return r.sep ? (r.dnb > 0 ? bm_group(sh.bmd, o) : 0u) : tbits(o);
+  };
+  // the other row's bans need a test of their own only when the lists differ
+  auto obits = [&](int o) -> uint32_t { return !r.sep ? 0u : LEAD == 1 ? tbits(o) : dbits(o); };
   const void* lrow = LEAD == 1 ? r.drow : r.trow;   // leading row
   const void* orow = LEAD == 1 ? r.trow : r.drow;   // the other row
   const RowStat& ls = LEAD == 1 ? r.ds : r.ts;
@@ -90,8 +101,14 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
     }
 #pragma unroll
     for (int u = 0; u < OV_QCAP / WAVE; ++u) {
-      if (u * WAVE + lane < n && is_kept(zo[u], os, false))
-        acc += LEAD == 1 ? term(zo[u], zl[u]) : term(zl[u], zo[u]);
+      const int j = u * WAVE + lane;
+      if (j >= n) continue;
+      bool ob = false;
+      if (r.sep) {
+        const int o = sh.q[wv][j].x - r.tok0;
+        ob = (obits(o & ~7) >> (o & 7)) & 1u;
+      }
+      if (is_kept(zo[u], os, ob)) acc += LEAD == 1 ? term(zo[u], zl[u]) : term(zl[u], zo[u]);
     }
     wave_sync_lds();
   };
@@ -127,7 +144,9 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
       const int x0 = sbase + (lane + k * WAVE) * GRP;
       uint32_t m = 0u;
       if (x0 < r.V) {
-        const uint32_t ban = r.nb > 0 ? bm_group(sh.bm, x0 - r.tok0) : 0u;
+        const int o = x0 - r.tok0;
+        const uint32_t ban = LEAD == 1 ? dbits(o) : tbits(o);
+        const uint32_t ban2 = LEAD == 2 ? obits(o) : 0u;   // draft bans, dense pairs
 #pragma unroll
         for (int e = 0; e < GRP; ++e) {
           const bool bn = (ban >> e) & 1u;
@@ -138,7 +157,7 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
             kept = is_kept(group_val<Elem>(dg[k], e), r.ds, bn);
           else
             kept = is_kept(group_val<Elem>(tg[k], e), r.ts, bn) &&
-                   is_kept(group_val<Elem>(dg[k], e), r.ds, false);
+                   is_kept(group_val<Elem>(dg[k], e), r.ds, (ban2 >> e) & 1u);
           m |= (kept ? 1u : 0u) << e;
         }
       }
@@ -191,10 +210,11 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
           Group<Elem> og;
           load_group<Elem>(orow, x0, r.V, r.vec, og);
           const Group<Elem>& lg = LEAD == 1 ? dg[k] : tg[k];
+          const uint32_t ob = obits(x0 - r.tok0);
 #pragma unroll
           for (int e = 0; e < GRP; ++e) {
             const float zo = group_val<Elem>(og, e), zl = group_val<Elem>(lg, e);
-            if (((km[k] >> e) & 1u) && is_kept(zo, os, false))
+            if (((km[k] >> e) & 1u) && is_kept(zo, os, (ob >> e) & 1u))
               acc += LEAD == 1 ? term(zo, zl) : term(zl, zo);
           }
         }
@@ -208,13 +228,27 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
   return acc;
 }
 
-template <typename Elem>
+// MIXED: per-request draft lengths, samplers and draft ban lists; a pair the
+// request does not have (beyond its draft length, or a greedy request, or one
+// with settings out of range) gets NaN.
+template <typename Elem, bool MIXED>
 __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
   __shared__ OverlapShared sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
   const int pair = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
   const int b = pair / g, i = pair % g;
+  ReqInfo rq;
+  if constexpr (MIXED) {
+    rq = request_info(a.req, b, g, a.st, a.sd);
+    if (rq.bad || rq.greedy || i >= rq.g) {
+      if (part == 0 && tid == 0) a.out_overlap[pair] = __builtin_nan("");
+      return;
+    }
+  } else {
+    rq.st = a.st;
+    rq.sd = a.sd;
+  }
   OvPair r;
   r.V = a.V;
   r.vec = a.vec != 0;
@@ -222,8 +256,8 @@ __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
   r.ds = a.stats[(int64_t)b * RPR + G1 + i];
   r.trow = (const Elem*)a.target + ((int64_t)b * G1 + i) * a.V;
   r.drow = (const Elem*)a.draft + ((int64_t)b * g + i) * a.V;
-  r.tinv = 1.0 / (double)a.t_temp;
-  r.dinv = 1.0 / (double)a.d_temp;
+  r.tinv = 1.0 / (double)rq.st.temperature;
+  r.dinv = 1.0 / (double)rq.sd.temperature;
   const int sub0 = part * a.spp;
   r.tok0 = sub0 * DRAW_SUB;
   // an empty row has p (or q) = 0 everywhere: the overlap is 0
@@ -232,8 +266,13 @@ __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
   r.nb = (a.banned && !empty) ? a.n_banned : 0;
   const int32_t* bl = r.nb ? a.banned + (int64_t)b * a.n_banned : nullptr;
   const int32_t ban0 = tid < r.nb ? bl[tid] : -1;
+  r.sep = MIXED && a.req.banned_d != nullptr;
+  r.dnb = (r.sep && !empty) ? a.req.n_banned_d : 0;
+  const int32_t* dbl = r.dnb ? a.req.banned_d + (int64_t)b * a.req.n_banned_d : nullptr;
+  const int32_t dban0 = tid < r.dnb ? dbl[tid] : -1;
 
   exp_table_fill(sh.etab);
+  if (r.dnb > 0) mark_bans(sh.bmd, r.nsl * DRAW_SUB, dbl, r.dnb, dban0, r.tok0, r.V);
   if (r.nb > 0)
     mark_bans(sh.bm, r.nsl * DRAW_SUB, bl, r.nb, ban0, r.tok0, r.V);   // also publishes etab
   else
@@ -274,11 +313,19 @@ __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
 }
 
 int launch_overlap(const OverlapArgs& a, int bf16, int pairs, hipStream_t st) {
-  const dim3 grid((unsigned)(pairs * a.parts));
-  if (bf16)
-    hipLaunchKernelGGL(overlap_kernel<uint16_t>, grid, dim3(OV_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(overlap_kernel<float>, grid, dim3(OV_THREADS), 0, st, a);
+  const dim3 grid((unsigned)(pairs * a.parts)), block(OV_THREADS);
+  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d;
+  if (bf16) {
+    if (mixed)
+      hipLaunchKernelGGL((overlap_kernel<uint16_t, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((overlap_kernel<uint16_t, false>), grid, block, 0, st, a);
+  } else {
+    if (mixed)
+      hipLaunchKernelGGL((overlap_kernel<float, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((overlap_kernel<float, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

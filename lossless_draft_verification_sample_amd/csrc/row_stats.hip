@@ -575,7 +575,9 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
 // workgroups share, so a fourth one would not stream faster; it would only
 // force register spills in the epilogue and make the last round of rows
 // coarser (rows / (3 * CUs) is closer to a whole number for large batches).
-template <typename Elem>
+// MIXED: per-request draft lengths, samplers (greedy requests included) and
+// draft ban lists; the plain variant carries none of that logic.
+template <typename Elem, bool MIXED>
 __global__ __launch_bounds__(RS_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 void row_stats_kernel(RowStatsArgs a) {
   __shared__ RowShared sh;
@@ -587,13 +589,31 @@ void row_stats_kernel(RowStatsArgs a) {
   const Elem* rowp = is_target
                          ? (const Elem*)a.target + ((int64_t)b * G1 + i) * (int64_t)a.V
                          : (const Elem*)a.draft + ((int64_t)b * a.gamma + (i - G1)) * (int64_t)a.V;
-  const SamplerDev s = is_target ? a.st : a.sd;
+  ReqInfo rq;
+  if constexpr (MIXED) {
+    rq = request_info(a.req, b, a.gamma, a.st, a.sd);
+  } else {
+    rq.g = a.gamma;
+    rq.st = a.st;
+    rq.sd = a.sd;
+    rq.greedy = false;
+    rq.bad = false;
+  }
+  const SamplerDev s = is_target ? rq.st : rq.sd;
   const int V = a.V;
-  const int nb = a.banned ? a.n_banned : 0;
-  const int32_t* bl = a.banned ? a.banned + (int64_t)b * a.n_banned : nullptr;
-  // the proposal this row scores (none for the bonus row) and its logit
   const int pi = is_target ? i : i - G1;
-  const int32_t xprop = pi < a.gamma ? a.draft_tokens[(int64_t)b * a.gamma + pi] : -1;
+  // rows the request does not use: beyond its draft length, the draft rows of
+  // a greedy request, every row of a request with settings out of range
+  const bool used = !MIXED || (!rq.bad && !rq.greedy && pi <= rq.g && (is_target || pi < rq.g));
+  // draft rows take the draft ban list when there is one
+  const bool dbans = MIXED && !is_target && a.req.banned_d;
+  const int nb = !used ? 0 : dbans ? a.req.n_banned_d : (a.banned ? a.n_banned : 0);
+  const int32_t* bl = nb == 0 ? nullptr
+                      : dbans ? a.req.banned_d + (int64_t)b * a.req.n_banned_d
+                              : a.banned + (int64_t)b * a.n_banned;
+  // the proposal this row scores (none for the bonus row) and its logit
+  const int32_t xprop = (used && pi < (MIXED ? rq.g : a.gamma))
+                             ? a.draft_tokens[(int64_t)b * a.gamma + pi] : -1;
   const bool xvalid = xprop >= 0 && xprop < V;
   const float zx = (tid == 0 && xvalid) ? elem_value<Elem>(rowp[xprop]) : 0.0f;
   const int32_t ban0 = tid < nb ? bl[tid] : -1;
@@ -608,8 +628,13 @@ void row_stats_kernel(RowStatsArgs a) {
   out.px = 0.0;
 
   bool generic = (sizeof(Elem) == 4) || a.force_generic;
+  const bool stats_path = used;
+  if (!stats_path) generic = false;
+  // (the target rows of greedy requests are left to greedy_rows_kernel, which
+  // runs after this kernel and overwrites their RowStat)
+  if (MIXED && !used) out.flags = rq.bad ? FLAG_BAD_PARAM : 0u;
 
-  if (!generic) {
+  if (stats_path && !generic) {
     // the first HT_SLOTS bins hold the ban hash set until the stream starts
     const uint32_t fill = nb > 0 ? HT_EMPTY : 0u;
     for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = k < HT_SLOTS ? fill : 0u;
@@ -716,10 +741,15 @@ void row_stats_kernel(RowStatsArgs a) {
   }
 
   if (tid == 0) {
-    // probability of the row's proposal under the row's distribution
-    const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zx > -INFINITY &&
-                      zx < INFINITY && zx >= out.tau;
-    out.px = kept ? exp((double)zx / (double)s.temperature - out.lse) : 0.0;
+    if (stats_path) {
+      // probability of the row's proposal under the row's distribution
+      const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zx > -INFINITY &&
+                        zx < INFINITY && zx >= out.tau;
+      out.px = kept ? exp((double)zx / (double)s.temperature - out.lse) : 0.0;
+    } else {
+      out.px = 0.0;
+      out.lse = __builtin_nan("");
+    }
     a.stats[row] = out;
     if (i == 0 && a.tickets) a.tickets[b] = 0;
     if (i < a.gamma && a.ov_tickets) a.ov_tickets[(int64_t)b * a.gamma + i] = 0;
@@ -734,10 +764,19 @@ void row_stats_kernel(RowStatsArgs a) {
 }
 
 int launch_row_stats(const RowStatsArgs& a, int dtype_bf16, int rows, hipStream_t stream) {
-  if (dtype_bf16)
-    hipLaunchKernelGGL(row_stats_kernel<uint16_t>, dim3(rows), dim3(RS_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(row_stats_kernel<float>, dim3(rows), dim3(RS_THREADS), 0, stream, a);
+  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d;
+  const dim3 grid(rows), block(RS_THREADS);
+  if (dtype_bf16) {
+    if (mixed)
+      hipLaunchKernelGGL((row_stats_kernel<uint16_t, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((row_stats_kernel<uint16_t, false>), grid, block, 0, stream, a);
+  } else {
+    if (mixed)
+      hipLaunchKernelGGL((row_stats_kernel<float, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((row_stats_kernel<float, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

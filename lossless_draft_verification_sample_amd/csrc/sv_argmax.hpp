@@ -37,9 +37,10 @@ struct ArgResult {
   bool nonfinite;
 };
 
-// `tab` is the LDS hash set of the request's banned ids, or nullptr. The
-// scratch arrays hold NT / WAVE entries each. Every thread gets the result.
-template <typename Elem, int NT, int UNROLL>
+// `tab` is the LDS hash set of the request's banned ids (used only when BANS;
+// a ban-free row runs the loop without any lookup). The scratch arrays hold
+// NT / WAVE entries each. Every thread gets the result.
+template <typename Elem, int NT, int UNROLL, bool BANS>
 __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, float* sv,
                                 int32_t* si, uint32_t* su) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -48,7 +49,7 @@ __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, fl
   const int tid = threadIdx.x;
   ArgBest best{-INFINITY, INT32_MAX};
   auto take = [&](float v, int32_t i) {
-    if (v > best.v && !(tab && ht_has(tab, i))) {
+    if (v > best.v && !(BANS && ht_has(tab, i))) {
       best.v = v;
       best.i = i;
     }
@@ -129,7 +130,7 @@ __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, fl
     for (int i = tid; i < V; i += NT) {
       const float z = am_val<Elem>(rowp, i);
       if (z != z || z == INFINITY) bad = 1u;
-      if (z == -INFINITY && i < first_ninf && !(tab && ht_has(tab, i))) first_ninf = i;
+      if (z == -INFINITY && i < first_ninf && !(BANS && ht_has(tab, i))) first_ninf = i;
     }
     nonfinite = block_max<NT>(bad, su) != 0u;
     const int32_t fn = block_min<NT>(first_ninf, si);

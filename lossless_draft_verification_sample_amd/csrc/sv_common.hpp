@@ -11,6 +11,7 @@ constexpr uint32_t FLAG_Q_ZERO = 2u;
 constexpr uint32_t FLAG_NONFINITE = 4u;
 constexpr uint32_t FLAG_EMPTY = 8u;
 constexpr uint32_t FLAG_RESIDUAL_ZERO = 16u;
+constexpr uint32_t FLAG_BAD_PARAM = 32u;
 
 constexpr int WAVE = 64;
 
@@ -22,7 +23,8 @@ struct alignas(16) RowStat {
   float tau;       // truncation threshold on the logit value (-inf: none)
   double lse;      // log sum_{kept} exp(z / T)   (-inf for an empty row)
   uint32_t flags;  // FLAG_NONFINITE | FLAG_EMPTY
-  uint32_t path;   // 0 = count histogram, 1 = generic streaming path
+  uint32_t path;   // 0 = count histogram, 1 = generic streaming path; for the
+                   // target row of a greedy request: its argmax (-1: none)
   double px;       // probability of the row's proposal token (target row i < gamma:
                    // p_i(x_i); draft row i: q_i(x_i)); 0 when it has none
 };
@@ -40,6 +42,61 @@ struct SamplerDev {
   float top_p;
   float pad;
 };
+
+// Per-request sampler as the caller lays it out (sv_sampler of the C interface).
+struct SamplerReq {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+};
+
+// Per-request settings of a mixed batch: device arrays, nullptr = call-wide.
+struct ReqArgs {
+  const int32_t* gammas;      // [B] proposals of each request, 0..gamma
+  const SamplerReq* ts;       // [B] target samplers (temperature 0: greedy request)
+  const SamplerReq* ds;       // [B] draft samplers
+  const int32_t* banned_d;    // [B][n_banned_d] bans of the draft rows, or nullptr
+  int n_banned_d;
+};
+
+// One request's resolved settings.
+struct ReqInfo {
+  int g;             // proposals
+  SamplerDev st, sd;
+  bool greedy;       // target temperature 0
+  bool bad;          // a setting out of range: the request is not verified
+};
+
+__device__ __forceinline__ bool sampler_in_range(const SamplerDev& s, bool allow_greedy) {
+  const float T = s.temperature;
+  if (!(T >= 0.0f) || !(T < INFINITY) || (T == 0.0f && !allow_greedy)) return false;
+  return s.top_k >= 0 && s.top_p > 0.0f && s.top_p <= 1.0f;
+}
+
+__device__ __forceinline__ ReqInfo request_info(const ReqArgs& q, int b, int gamma,
+                                                const SamplerDev& st, const SamplerDev& sd) {
+  ReqInfo r;
+  r.g = q.gammas ? q.gammas[b] : gamma;
+  r.st = st;
+  r.sd = sd;
+  if (q.ts) {
+    const SamplerReq t = q.ts[b];
+    r.st.temperature = t.temperature;
+    r.st.top_k = t.top_k;
+    r.st.top_p = t.top_p;
+  }
+  if (q.ds) {
+    const SamplerReq t = q.ds[b];
+    r.sd.temperature = t.temperature;
+    r.sd.top_k = t.top_k;
+    r.sd.top_p = t.top_p;
+  }
+  r.greedy = r.st.temperature == 0.0f;
+  r.bad = r.g < 0 || r.g > gamma || !sampler_in_range(r.st, true) ||
+          (!r.greedy && !sampler_in_range(r.sd, false));
+  if (r.bad) r.g = 0;
+  return r;
+}
 
 // ---------------------------------------------------------------- numbers
 

@@ -32,6 +32,7 @@ struct RowStatsArgs {
   int32_t* tickets;             // [B] draw-kernel arrival counters, zeroed here
   int32_t* ov_tickets;          // [B][gamma] overlap arrival counters, zeroed here, or nullptr
   uint32_t* accept_hist;        // [gamma+1] zeroed here, or nullptr
+  ReqArgs req;
   float* out_tlse;
   float* out_dlse;
   int force_generic;
@@ -44,7 +45,6 @@ struct DrawArgs {
   int vec;                    // rows 16-byte aligned and V*size a multiple of 16
   int gamma, V, nsub;
   int spw, nwg;               // sub-chunks per workgroup, workgroups per request
-  float t_temp, d_temp;
   const int32_t* draft_tokens;
   const int32_t* banned;      // raw ban lists or nullptr
   int n_banned;
@@ -57,6 +57,8 @@ struct DrawArgs {
   int32_t* out_num_accepted;
   uint32_t* out_flags;
   uint32_t* accept_hist;      // [gamma+1], zero on entry, or nullptr
+  SamplerDev st, sd;          // call-wide samplers
+  ReqArgs req;
 };
 
 struct OverlapArgs {
@@ -65,13 +67,14 @@ struct OverlapArgs {
   int vec;                    // rows 16-byte aligned and V*size a multiple of 16
   int gamma, V, nsub;
   int spp, parts;             // sub-chunks per workgroup, workgroups per pair
-  float t_temp, d_temp;
   const int32_t* banned;      // raw ban lists or nullptr
   int n_banned;
   const RowStat* stats;
   double* partial;            // [B*gamma][parts] when parts > 1
   int32_t* tickets;           // [B*gamma], zero on entry, when parts > 1
   double* out_overlap;        // [B][gamma]
+  SamplerDev st, sd;          // call-wide samplers
+  ReqArgs req;
 };
 
 struct GreedyArgs {
@@ -97,6 +100,7 @@ struct CommitArgs {
   int32_t* anchor;              // [B]
   int32_t* n_free;              // [B] or nullptr
   int32_t* free_slots;          // [B][gamma] or nullptr
+  const int32_t* gammas;        // [B] proposals of each request, or nullptr (all gamma)
 };
 
 int launch_row_stats(const RowStatsArgs& a, int dtype_bf16, int rows, hipStream_t s);
@@ -104,6 +108,7 @@ int launch_draw(const DrawArgs& a, int B, hipStream_t s);
 int launch_overlap(const OverlapArgs& a, int bf16, int pairs, hipStream_t s);
 int launch_greedy_argmax(const GreedyArgs& a, hipStream_t s);
 int launch_greedy_scan(const GreedyArgs& a, hipStream_t s);
+int launch_greedy_rows(const RowStatsArgs& a, int dtype_bf16, int B, hipStream_t s);
 int launch_commit(const CommitArgs& a, hipStream_t s);
 
 }  // namespace sv

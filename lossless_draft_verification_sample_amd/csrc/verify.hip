@@ -41,19 +41,21 @@ struct DrawRow {
   float tcut;         // no target token below this is kept (+inf: empty row)
 };
 
-__device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n) {
+// The rows of the final draw of request b after n acceptances: the target row
+// n, and the draft row n at a rejection (n < the request's draft length g).
+__device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n, const ReqInfo& rq) {
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
   DrawRow r;
   const int64_t V = a.V;
   const size_t es = a.bf16 ? 2 : 4;
   r.trow = (const char*)a.target + ((int64_t)b * G1 + n) * V * es;
   r.ts = a.stats[(int64_t)b * RPR + n];
-  r.tinv = 1.0 / (double)a.t_temp;
+  r.tinv = 1.0 / (double)rq.st.temperature;
   r.tcut = (r.ts.flags & FLAG_EMPTY) ? INFINITY : r.ts.tau;
-  if (n < g) {
+  if (n < rq.g) {
     r.drow = (const char*)a.draft + ((int64_t)b * g + n) * V * es;
     r.ds = a.stats[(int64_t)b * RPR + G1 + n];
-    r.dinv = 1.0 / (double)a.d_temp;
+    r.dinv = 1.0 / (double)rq.sd.temperature;
   } else {
     r.drow = nullptr;
   }
@@ -126,21 +128,24 @@ struct Walk {
   int32_t x;       // proposal of this lane (lanes < gamma)
 };
 
-__device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b) {
+// gq: the request's draft length (proposals 0..gq-1 and target rows 0..gq are
+// its own); the final-draw uniform is slot gamma whatever gq is.
+__device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b, int gq) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
   const RowStat* st = a.stats + (int64_t)b * RPR;
   uint32_t rf = 0u;
   double p = 0.0, q = 0.0, u = 0.0;
   int32_t x = -1;
-  if (lane <= g) {
+  if (lane <= g)
+    u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
+                   : philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)lane);
+  if (lane <= gq) {
     const RowStat t = st[lane];
     rf |= t.flags;
     p = t.px;
-    u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
-                   : philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)lane);
   }
-  if (lane < g) {
+  if (lane < gq) {
     const RowStat d = st[G1 + lane];
     rf |= d.flags;
     q = d.px;
@@ -149,17 +154,17 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b) {
   rf &= FLAG_NONFINITE | FLAG_EMPTY;
 #pragma unroll
   for (int off = WAVE / 2; off > 0; off >>= 1) rf |= __shfl_xor(rf, off, WAVE);
-  const bool range = lane < g && (x < 0 || x >= a.V);
-  const bool qzero = lane < g && !range && !(q > 0.0);
-  const bool acc = lane < g && !range && !qzero && u * q <= p;
+  const bool range = lane < gq && (x < 0 || x >= a.V);
+  const bool qzero = lane < gq && !range && !(q > 0.0);
+  const bool acc = lane < gq && !range && !qzero && u * q <= p;
   const uint64_t accm = __ballot(acc);
   const uint64_t rangem = __ballot(range);
   const uint64_t qzm = __ballot(qzero);
   Walk w;
-  w.n = __ffsll((unsigned long long)~accm) - 1;   // lane g never accepts: n <= g
+  w.n = __ffsll((unsigned long long)~accm) - 1;   // lane gq never accepts: n <= gq
   w.flags = rf;
   if (rangem) w.flags |= FLAG_TOKEN_RANGE;
-  if (w.n < g && ((qzm >> w.n) & 1ull)) w.flags |= FLAG_Q_ZERO;
+  if (w.n < gq && ((qzm >> w.n) & 1ull)) w.flags |= FLAG_Q_ZERO;
   const uint64_t ub = (uint64_t)__double_as_longlong(u);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ub, g);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ub >> 32), g);
@@ -177,6 +182,7 @@ struct DrawShared {
     QueuedTok q[DR_NW][DR_QCAP];      // rejections at a truncated target
   };
   uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
+  uint32_t bmd[DRAW_SPW_MAX * DRAW_SUB / 32];   // draft-only bans (mixed batches)
   double w[DRAW_SPW_MAX];
   double p[DRAW_SPW_MAX];
   double scr[2 * DR_NW];
@@ -186,7 +192,71 @@ struct DrawShared {
   double sel_before;
 };
 
+// Outputs of a request of a mixed batch that needs no draw, written by one
+// wave: a request with settings out of range (nothing accepted, no token), or
+// a greedy request (the walk of greedy verification over the argmaxes that
+// greedy_rows_kernel left in the target rows' RowStat).
+__device__ __forceinline__ void finish_without_draw(const DrawArgs& a, int b, const ReqInfo& rq) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
+  int32_t* ot = a.out_tokens + (int64_t)b * G1;
+  if (rq.bad) {
+    if (lane < G1) ot[lane] = -1;
+    if (lane == 0) {
+      a.out_num_accepted[b] = 0;
+      if (a.out_flags) a.out_flags[b] = FLAG_BAD_PARAM;
+      if (a.accept_hist) atomicAdd(&a.accept_hist[0], 1u);
+    }
+    return;
+  }
+  const RowStat* st = a.stats + (int64_t)b * RPR;
+  uint32_t rf = 0u;
+  int32_t am = -1, x = -1;
+  bool match = false;
+  if (lane <= rq.g) {
+    const RowStat t = st[lane];
+    rf = t.flags & FLAG_NONFINITE;
+    am = (int32_t)t.path;
+    match = t.px == 1.0;
+  }
+  if (lane < rq.g) x = a.draft_tokens[(int64_t)b * g + lane];
+  const bool range = lane < rq.g && (x < 0 || x >= a.V);
+#pragma unroll
+  for (int off = WAVE / 2; off > 0; off >>= 1) rf |= __shfl_xor(rf, off, WAVE);
+  const uint64_t mm = __ballot(lane < rq.g && match && !range);
+  const int n = __ffsll((unsigned long long)~mm) - 1;   // <= rq.g
+  uint32_t flags = rf;
+  if (__ballot(range)) flags |= FLAG_TOKEN_RANGE;
+  const int32_t token = __shfl(am, n, WAVE);
+  if (token < 0) flags |= FLAG_EMPTY;
+  if (lane < G1) ot[lane] = lane < n ? x : (lane == n ? token : -1);
+  if (lane == 0) {
+    a.out_num_accepted[b] = n;
+    if (a.out_flags) a.out_flags[b] = flags;
+    if (a.accept_hist) atomicAdd(&a.accept_hist[n], 1u);
+  }
+}
+
+// Sets the logits of the banned tokens of a group (bit e: token e) to -inf.
 template <typename Elem>
+__device__ __forceinline__ void mask_group(Group<Elem>& g, uint32_t bits) {
+  if (!bits) return;
+#pragma unroll
+  for (int e = 0; e < GRP; ++e) {
+    if ((bits >> e) & 1u) {
+      if constexpr (sizeof(Elem) == 2) {
+        const int sh = 16 * (e & 1);
+        g.w[0][e >> 1] = (g.w[0][e >> 1] & ~(0xFFFFu << sh)) | (0xFF80u << sh);
+      } else {
+        g.w[e >> 2][e & 3] = 0xFF800000u;
+      }
+    }
+  }
+}
+
+// MIXED: per-request draft lengths, samplers (greedy requests included) and
+// draft ban lists; the plain variant carries none of that logic.
+template <typename Elem, bool MIXED>
 __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
@@ -198,10 +268,30 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   const int nb = a.banned ? a.n_banned : 0;
   const int32_t* bl = a.banned ? a.banned + (int64_t)b * a.n_banned : nullptr;
   const int32_t ban0 = tid < nb ? bl[tid] : -1;
+  ReqInfo rq;
+  if constexpr (MIXED) {
+    rq = request_info(a.req, b, g, a.st, a.sd);
+    if (rq.bad || rq.greedy) {
+      if (part == 0 && wv == 0) finish_without_draw(a, b, rq);
+      return;
+    }
+  } else {
+    rq.g = g;
+    rq.st = a.st;
+    rq.sd = a.sd;
+    rq.greedy = false;
+    rq.bad = false;
+  }
+  // the draft rows' own ban list, if the batch has one
+  const int dnb = (MIXED && a.req.banned_d) ? a.req.n_banned_d : 0;
+  const int32_t* dbl = dnb ? a.req.banned_d + (int64_t)b * a.req.n_banned_d : nullptr;
+  const int32_t dban0 = tid < dnb ? dbl[tid] : -1;
 
   exp_table_fill(sh.etab);
-  const Walk wk = accept_walk(a, b);
-  const DrawRow r = draw_row(a, b, wk.n);
+  const Walk wk = accept_walk(a, b, rq.g);
+  const DrawRow r = draw_row(a, b, wk.n, rq);
+  const bool dmask = dnb > 0 && r.drow;
+  if (dmask) mark_bans(sh.bmd, nsl * DRAW_SUB, dbl, dnb, dban0, tok0, a.V);
   if (nb > 0)
     mark_bans(sh.bm, nsl * DRAW_SUB, bl, nb, ban0, tok0, a.V);   // also publishes etab
   else
@@ -316,6 +406,13 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
           qd[u] = load_logit<Elem>(r.drow, t.x);
         }
       }
+      if (dmask) {
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          const int o = qx[u] - tok0;
+          if (qx[u] >= 0 && ((sh.bmd[o >> 5] >> (o & 31)) & 1u)) qd[u] = -INFINITY;
+        }
+      }
       double qw[QU], qp[QU];
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
@@ -346,7 +443,10 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
 #pragma unroll
       for (int k = 0; k < GPL; ++k) {
         tg[k] = tn[k];
-        if constexpr (MODE == 2) dg[k] = dn[k];
+        if constexpr (MODE == 2) {
+          dg[k] = dn[k];
+          if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, sbase + (lane + k * WAVE) * GRP - tok0));
+        }
       }
       if (sl + DR_NW < nsl) issue(sl + DR_NW);
       uint32_t km[GPL];
@@ -363,8 +463,12 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
           // more kept tokens than the queue holds: draft groups where needed,
           // evaluated in place
 #pragma unroll
-          for (int k = 0; k < GPL; ++k)
-            if (km[k]) load_group<Elem>(r.drow, sbase + (lane + k * WAVE) * GRP, a.V, a.vec, dg[k]);
+          for (int k = 0; k < GPL; ++k) {
+            if (!km[k]) continue;
+            const int x0 = sbase + (lane + k * WAVE) * GRP;
+            load_group<Elem>(r.drow, x0, a.V, a.vec, dg[k]);
+            if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, x0 - tok0));
+          }
           double sw = 0.0, sp = 0.0;
 #pragma unroll
           for (int k = 0; k < GPL; ++k)
@@ -486,6 +590,10 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
       load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
       if (r.drow) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
     }
+    if (dmask) {
+      mark_bans(sh.bmd, DRAW_SUB, dbl, dnb, dban0, s0, a.V);
+      if (x0 < a.V) mask_group<Elem>(dg, bm_group(sh.bmd, x0 - s0));
+    }
     if (nb > 0) mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
     double v[GRP];
     const uint32_t km = x0 < a.V ? kept_mask<Elem>(r, tg, nb > 0 ? bm_group(sh.bm, x0 - s0) : 0u) : 0u;
@@ -524,11 +632,19 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
 }
 
 int launch_draw(const DrawArgs& a, int B, hipStream_t st) {
-  const dim3 grid((unsigned)(a.nwg * B));
-  if (a.bf16)
-    hipLaunchKernelGGL(draw_kernel<uint16_t>, grid, dim3(DR_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(draw_kernel<float>, grid, dim3(DR_THREADS), 0, st, a);
+  const dim3 grid((unsigned)(a.nwg * B)), block(DR_THREADS);
+  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d;
+  if (a.bf16) {
+    if (mixed)
+      hipLaunchKernelGGL((draw_kernel<uint16_t, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((draw_kernel<uint16_t, false>), grid, block, 0, st, a);
+  } else {
+    if (mixed)
+      hipLaunchKernelGGL((draw_kernel<float, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((draw_kernel<float, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -57,6 +57,7 @@ from .verifier import (  # noqa: F401
     residual_weights,
     row_distribution,
     sample_categorical,
+    sampler_valid,
     verify_batch,
     verify_block,
     verify_greedy,

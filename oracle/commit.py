@@ -35,13 +35,14 @@ rows written; nothing is freed when every proposal survives).
 import numpy as np
 
 
-def commit_chain(tokens, num_accepted, kv_len, slots=None):
+def commit_chain(tokens, num_accepted, kv_len, slots=None, gammas=None):
     """Per-request commit metadata of one chain verification round.
 
     tokens [B, gamma+1] and num_accepted [B] as the verifier returns them,
-    kv_len [B] materialised rows before the round, slots [B, gamma+1] or None.
-    Returns (new_kv_len [B], anchor [B], n_free [B], free_slots [B, gamma] or
-    None).
+    kv_len [B] materialised rows before the round, slots [B, gamma+1] or None,
+    gammas [B] proposals of each request (None: all gamma; the pass then wrote
+    rows at positions K .. K+gammas[b] only). Returns (new_kv_len [B], anchor
+    [B], n_free [B], free_slots [B, gamma] or None).
     """
     tokens = np.asarray(tokens)
     num_accepted = np.asarray(num_accepted)
@@ -54,10 +55,16 @@ def commit_chain(tokens, num_accepted, kv_len, slots=None):
     free = None if slots is None else np.full((B, gamma), -1, dtype=np.int64)
     for b in range(B):
         n = int(num_accepted[b])
+        g = gamma if gammas is None else int(gammas[b])
+        if not (0 <= g <= gamma and 0 <= n <= g):
+            # not a verifier output: nothing committed, nothing freed
+            new_kv_len[b] = int(kv_len[b])
+            anchor[b] = -1
+            continue
         new_kv_len[b] = int(kv_len[b]) + 1 + n        # anchor row + accepted rows
         anchor[b] = int(tokens[b, n])                  # correction or bonus, pending
-        n_free[b] = gamma - n                          # rows of the rejected proposals
+        n_free[b] = g - n                              # rows of the rejected proposals
         if free is not None:
-            for j in range(n + 1, gamma + 1):          # positions K+n+1 .. K+gamma
+            for j in range(n + 1, g + 1):              # positions K+n+1 .. K+g
                 free[b, j - (n + 1)] = int(slots[b][j])
     return new_kv_len, anchor, n_free, free

@@ -66,13 +66,13 @@ def _sample(lib, **kw):
     from lossless_draft_verification_sample_amd._lib import SvSampler
     a = dict(target=FAKE, draft=FAKE, dtype=1, tokens=FAKE, banned=None, n_banned=0, B=2,
              gamma=3, V=100, ts=SvSampler(1.0, 0, 1.0), ds=SvSampler(1.0, 0, 1.0), seed=0,
-             offset=0, uniforms=None, out_tokens=FAKE, out_n=FAKE, out_flags=None,
+             offset=0, requests=None, uniforms=None, out_tokens=FAKE, out_n=FAKE, out_flags=None,
              out_tl=None, out_dl=None, out_ov=None, out_hist=None, ws=None, ws_bytes=0,
              stream=None)
     a.update(kw)
     return lib.spec_verify_sample(
         a["target"], a["draft"], a["dtype"], a["tokens"], a["banned"], a["n_banned"], a["B"],
-        a["gamma"], a["V"], a["ts"], a["ds"], a["seed"], a["offset"], a["uniforms"],
+        a["gamma"], a["V"], a["ts"], a["ds"], a["requests"], a["seed"], a["offset"], a["uniforms"],
         a["out_tokens"], a["out_n"], a["out_flags"], a["out_tl"], a["out_dl"], a["out_ov"],
         a["out_hist"], a["ws"], a["ws_bytes"], a["stream"])
 
@@ -101,6 +101,11 @@ def test_sample_argument_errors(lib):
     assert _sample(lib, dtype=2) == L.SV_EDTYPE
     assert _sample(lib, dtype=0, target=FAKE + 2) == L.SV_EINVAL   # fp32 needs 4-byte alignment
     assert _sample(lib, B=2**30, gamma=63) == L.SV_ESIZE
+    import ctypes
+    bad_req = L.SvRequests(None, None, None, None, 3)          # n_banned_draft without a list
+    assert _sample(lib, requests=ctypes.byref(bad_req)) == L.SV_EINVAL
+    big = L.SvRequests(None, None, None, FAKE, 2049)
+    assert _sample(lib, requests=ctypes.byref(big)) == L.SV_EINVAL
 
 
 def test_greedy_argument_errors(lib):
@@ -127,8 +132,8 @@ def test_commit_argument_errors(lib):
 
     def call(**kw):
         a = dict(ok, **kw)
-        return c(a["tok"], a["n"], a["kv"], a["slots"], a["B"], a["g"], a["nk"], a["an"], a["nf"],
-                 a["fs"], None)
+        return c(a["tok"], a["n"], a["kv"], a["slots"], None, a["B"], a["g"], a["nk"], a["an"],
+                 a["nf"], a["fs"], None)
     for name, kw in {"tokens": dict(tok=None), "num_accepted": dict(n=None), "kv_len": dict(kv=None),
                      "new_kv_len": dict(nk=None), "anchor": dict(an=None),
                      "free without slots": dict(fs=FAKE), "B": dict(B=0), "gamma0": dict(g=0),

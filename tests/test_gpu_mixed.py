@@ -1,0 +1,193 @@
+"""Parity of mixed batches (per-request draft lengths, samplers with greedy
+requests among sampled ones, draft-only ban lists, settings out of range)
+with oracle.verify_batch. Same bar as test_gpu_parity: tokens, accept counts
+and flags bit-exact outside the 1e-10 decision band, lse within 1e-5, NaN
+exactly where a request does not use a row."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import lossless_draft_verification_sample_amd._lib as L
+    L.load()
+
+
+def _dev(a, dtype=np.int32):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).to(pu.torch_dev())
+
+
+def _mixed_setup(wl, seed, n_greedy=3, bad=True, draft_bans=True):
+    cfg = wl.cfg
+    B, g, V = cfg.B, cfg.gamma, cfg.V
+    rng = np.random.default_rng(seed)
+    choices = [(0.8, 0, 0.9), (1.0, 0, 1.0), (0.7, 50, 1.0), (1.3, 0, 0.95), (0.9, 20, 0.8),
+               (0.5, 0, 1.0)]
+    ts = [choices[int(rng.integers(len(choices)))] for _ in range(B)]
+    ds = [choices[int(rng.integers(len(choices)))] for _ in range(B)]
+    greedy = rng.choice(B, n_greedy, replace=False)
+    for b in greedy:
+        ts[b] = (0.0, 0, 1.0)
+    gammas = rng.integers(0, g + 1, B).astype(np.int32)
+    gammas[0] = g
+    gammas[1] = 0
+    if bad:
+        ts[2] = (1.0, 0, 1.5)          # top_p out of range
+        gammas[3] = g + 2              # more proposals than the batch holds
+    banned = rng.integers(-1, V, (B, 24)).astype(np.int32)
+    banned_draft = rng.integers(-1, V, (B, 9)).astype(np.int32) if draft_bans else None
+    # proposals: sampled requests draw from their transformed q; greedy ones
+    # mostly copy the target argmax
+    xs = np.zeros((B, g), dtype=np.int32)
+    for b in range(B):
+        db = [t for t in (banned_draft if draft_bans else banned)[b].tolist() if t >= 0]
+        tb = [t for t in banned[b].tolist() if t >= 0]
+        for i in range(g):
+            if ts[b][0] == 0.0:
+                am = oracle.greedy_argmax(wl.target[b, i].astype(np.float64), tb)
+                xs[b, i] = am if rng.random() < 0.75 else int(rng.integers(V))
+            elif oracle.sampler_valid(oracle.Sampler(*ds[b]), False):
+                q = oracle.row_distribution(wl.draft[b, i].astype(np.float64),
+                                            oracle.Sampler(*ds[b]), db).p
+                xs[b, i] = oracle.sample_categorical(q, 1.0 - rng.random())[0]
+    return ts, ds, gammas, banned, banned_draft, xs
+
+
+def _run(wl, xs, ts, ds, gammas, banned, banned_draft, seed=4, offset=2, diagnostics=False,
+         requests_override=None):
+    import torch
+    import lossless_draft_verification_sample_amd as sv
+    cfg = wl.cfg
+    dev = pu.torch_dev()
+    t = pu.logits_tensor(wl.target, wl.target_bits, cfg.dtype, dev)
+    d = pu.logits_tensor(wl.draft, wl.draft_bits, cfg.dtype, dev)
+    req = requests_override or sv.Requests(
+        gamma=None if gammas is None else _dev(gammas),
+        target=sv.sampler_array(ts, dev), draft=sv.sampler_array(ds, dev),
+        banned_draft=None if banned_draft is None else _dev(banned_draft))
+    out = sv.spec_verify_sample(t, d, _dev(xs), (1.0, 0, 1.0), (1.0, 0, 1.0),
+                                banned_ids=None if banned is None else _dev(banned),
+                                seed=seed, offset=offset, requests=req,
+                                want_overlap=diagnostics, want_hist=diagnostics)
+    torch.cuda.synchronize()
+    res = {k: getattr(out, k).cpu().numpy() for k in ("tokens", "num_accepted")}
+    res["flags"] = out.flags.cpu().numpy().astype(np.uint32)
+    res["target_lse"] = out.target_lse.cpu().numpy().astype(np.float64)
+    res["draft_lse"] = out.draft_lse.cpu().numpy().astype(np.float64)
+    if diagnostics:
+        res["overlap"] = out.overlap.cpu().numpy()
+        res["accept_hist"] = out.accept_hist.cpu().numpy().astype(np.int64)
+    return res
+
+
+def _oracle(wl, xs, ts, ds, gammas, banned, banned_draft, seed=4, offset=2):
+    cfg = wl.cfg
+    u = pu.philox_uniforms(seed, offset, cfg.B, cfg.gamma)
+    return oracle.verify_batch(wl.target.astype(np.float64), wl.draft.astype(np.float64), xs, u,
+                               [oracle.Sampler(*s) for s in ts], [oracle.Sampler(*s) for s in ds],
+                               banned, banned_draft, gammas)
+
+
+def _compare(got, ref, where):
+    bnd = ref.margin <= pu.EXACT_BAND
+    for b in range(len(ref.tokens)):
+        assert got["flags"][b] == ref.flags[b], (where, b, got["flags"][b], ref.flags[b])
+        if not bnd[b]:
+            assert np.array_equal(got["tokens"][b], ref.tokens[b]), (where, b, got["tokens"][b],
+                                                                     ref.tokens[b])
+            assert got["num_accepted"][b] == ref.num_accepted[b], (where, b)
+        for name, r in (("target_lse", ref.target_lse[b]), ("draft_lse", ref.draft_lse[b])):
+            g = got[name][b]
+            assert np.array_equal(np.isnan(g), np.isnan(r)), (where, b, name, g, r)
+            fin = np.isfinite(r)
+            assert np.array_equal(np.isfinite(g), fin), (where, b, name)
+            assert np.all(np.abs(g[fin] - r[fin]) <= 1e-5 * np.maximum(1.0, np.abs(r[fin]))), where
+    assert int(bnd.sum()) <= 1, where
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20011), ("bf16", 40000), ("f32", 9001)])
+def test_mixed_batch_matches_oracle(dtype, V):
+    wl = pu.make("c5", B=12, gamma=5, V=V, dtype=dtype, seed=90 + V % 13)
+    ts, ds, gammas, banned, banned_draft, xs = _mixed_setup(wl, seed=V)
+    got = _run(wl, xs, ts, ds, gammas, banned, banned_draft)
+    ref = _oracle(wl, xs, ts, ds, gammas, banned, banned_draft)
+    _compare(got, ref, f"{dtype} V={V}")
+    assert got["flags"][2] == oracle.FLAG_BAD_PARAM and got["flags"][3] == oracle.FLAG_BAD_PARAM
+    assert got["num_accepted"][1] == 0
+
+
+def test_shared_bans_and_no_ragged_lengths():
+    wl = pu.make("c2", B=10, V=8000, seed=92)
+    ts, ds, _, banned, _, xs = _mixed_setup(wl, seed=5, bad=False, draft_bans=False)
+    got = _run(wl, xs, ts, ds, None, banned, None)
+    ref = _oracle(wl, xs, ts, ds, None, banned, None)
+    _compare(got, ref, "shared bans")
+
+
+def test_uniform_requests_reproduce_the_plain_call():
+    import lossless_draft_verification_sample_amd as sv
+    wl = pu.make("c5", B=8, V=30011, seed=93)
+    cfg = wl.cfg
+    s = pu.sampler_of(cfg)
+    xs = pu.oracle_proposals(wl)
+    plain = pu.run_gpu_sample(wl, xs, seed=4, offset=2)
+    dev = pu.torch_dev()
+    req = sv.Requests(gamma=_dev(np.full(cfg.B, cfg.gamma)), target=sv.sampler_array([s] * cfg.B, dev),
+                      draft=sv.sampler_array([s] * cfg.B, dev))
+    import torch
+    out = sv.spec_verify_sample(pu.logits_tensor(wl.target, wl.target_bits, cfg.dtype, dev),
+                                pu.logits_tensor(wl.draft, wl.draft_bits, cfg.dtype, dev), _dev(xs),
+                                s, s, banned_ids=_dev(wl.banned), seed=4, offset=2, requests=req)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.tokens.cpu().numpy(), plain["tokens"])
+    assert np.array_equal(out.num_accepted.cpu().numpy(), plain["num_accepted"])
+    assert np.array_equal(out.flags.cpu().numpy().astype(np.uint32), plain["flags"])
+    assert np.array_equal(out.target_lse.cpu().numpy(), plain["target_lse"].astype(np.float32))
+
+
+def test_mixed_overlap_and_histogram():
+    wl = pu.make("c5", B=10, gamma=4, V=12011, seed=94)
+    ts, ds, gammas, banned, banned_draft, xs = _mixed_setup(wl, seed=6)
+    got = _run(wl, xs, ts, ds, gammas, banned, banned_draft, diagnostics=True)
+    ref = _oracle(wl, xs, ts, ds, gammas, banned, banned_draft)
+    assert np.array_equal(got["accept_hist"], np.bincount(got["num_accepted"], minlength=5))
+    for b in range(wl.cfg.B):
+        sampled = not (ref.flags[b] & oracle.FLAG_BAD_PARAM) and ts[b][0] != 0.0
+        for i in range(wl.cfg.gamma):
+            a = got["overlap"][b, i]
+            if not sampled or i >= gammas[b]:
+                assert np.isnan(a), (b, i, a)
+                continue
+            tb = [t for t in banned[b].tolist() if t >= 0]
+            db = [t for t in banned_draft[b].tolist() if t >= 0]
+            pd = oracle.row_distribution(wl.target[b, i].astype(np.float64), oracle.Sampler(*ts[b]), tb)
+            qd = oracle.row_distribution(wl.draft[b, i].astype(np.float64), oracle.Sampler(*ds[b]), db)
+            if min(pd.topp_margin, qd.topp_margin) <= pu.EXACT_BAND:
+                continue
+            assert abs(a - oracle.overlap(pd.p, qd.p)) <= 1e-9, (b, i)
+
+
+def test_mixed_commit():
+    import torch
+    import lossless_draft_verification_sample_amd as sv
+    wl = pu.make("c5", B=12, gamma=5, V=8009, seed=95)
+    ts, ds, gammas, banned, banned_draft, xs = _mixed_setup(wl, seed=7)
+    got = _run(wl, xs, ts, ds, gammas, banned, banned_draft)
+    B, G1 = got["tokens"].shape
+    kv = np.arange(B) * 10
+    slots = np.arange(B * G1).reshape(B, G1) + 100
+    out = sv.spec_verify_commit(_dev(got["tokens"]), _dev(got["num_accepted"]), _dev(kv), _dev(slots),
+                                gamma_b=_dev(gammas))
+    torch.cuda.synchronize()
+    ref = oracle.commit_chain(got["tokens"], got["num_accepted"], kv, slots, gammas)
+    for g, r in zip(out, ref):
+        assert np.array_equal(g.cpu().numpy().astype(np.int64), r)

@@ -58,3 +58,19 @@ def test_invariants_random_rounds():
         assert np.all(n_free[full] == 0)
     _, _, _, none = commit_chain(toks, n, kv, None)
     assert none is None
+
+
+def test_ragged_lengths():
+    # a request with g_b proposals wrote rows for positions K .. K+g_b only
+    toks = np.array([[5, 6, -1, -1], [7, -1, -1, -1], [1, 2, 3, 4]])
+    n = np.array([1, 0, 3])
+    kv = np.array([10, 20, 30])
+    slots = np.array([[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11]])
+    gammas = np.array([2, 0, 3])
+    new_kv, anchor, n_free, free = commit_chain(toks, n, kv, slots, gammas)
+    assert new_kv.tolist() == [12, 21, 34] and anchor.tolist() == [6, 7, 4]
+    assert n_free.tolist() == [1, 0, 0]
+    assert free.tolist() == [[2, -1, -1], [-1, -1, -1], [-1, -1, -1]]
+    # an accepted count beyond the request's own length is not a verifier output
+    new_kv, anchor, n_free, _ = commit_chain(toks, np.array([3, 0, 3]), kv, slots, gammas)
+    assert new_kv[0] == 10 and anchor[0] == -1 and n_free[0] == 0
