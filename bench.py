@@ -22,6 +22,11 @@ accepted-prefix histogram; the line then carries a `diagnostics` object that
 rates the overlap kernel the same way (algorithmic bytes: the row of each pair
 that is read in full, both rows when neither is truncated).
 
+With --mixed the batch carries per-request settings (sv_requests): every
+fourth request is greedy, draft lengths are gamma, gamma-1, gamma-2 in turn,
+and temperature, top-k and top-p vary per request; `value` then counts the
+rows the requests use (2 g_b + 1 per sampled request, g_b + 1 per greedy one).
+
 With --commit every step is followed by spec_verify_commit (chain KV-commit
 metadata from the step's outputs, with synthetic KV lengths and slots); the
 line then carries a `commit` object with that kernel's time and bytes.
@@ -118,6 +123,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--diagnostics", action="store_true",
                     help="also compute per-position overlaps and the accepted-prefix histogram")
+    ap.add_argument("--mixed", action="store_true",
+                    help="per-request draft lengths and samplers, a quarter of the requests greedy")
     ap.add_argument("--commit", action="store_true",
                     help="follow every step with the chain KV-commit metadata kernel")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -189,12 +196,26 @@ def main():
                             torch.empty((cfg.B,), dtype=torch.int32, device=dev),
                             torch.empty((cfg.B, cfg.gamma), dtype=torch.int32, device=dev))
 
+    requests = None
+    if args.mixed:
+        if cfg.mode != "sample":
+            raise SystemExit("--mixed needs a sampling workload")
+        temps, topps, topks = (0.6, 0.8, 1.0, 1.2), (0.9, 0.95, 1.0), (0, 50)
+        per = [(temps[b % 4], topks[b % 2], topps[b % 3]) for b in range(cfg.B)]
+        for b in range(0, cfg.B, 4):
+            per[b] = (0.0, 0, 1.0)
+        gam = np.array([cfg.gamma - (b % 3) for b in range(cfg.B)], dtype=np.int32).clip(0)
+        requests = sv.Requests(gamma=torch.from_numpy(gam).to(dev),
+                               target=sv.sampler_array(per, dev), draft=sv.sampler_array(per, dev))
+        greedy = np.array([t[0] == 0.0 for t in per])
+        rows = int(np.where(greedy, gam + 1, 2 * gam + 1).sum())
+
     def step(k):
         c = k % COPIES
         if cfg.mode == "sample":
             sv.spec_verify_sample(copies[c], dcopies[c], toks, samp, samp, bans,
                                   seed=cfg.philox_seed, offset=cfg.philox_offset,
-                                  workspace=ws, out=out)
+                                  requests=requests, workspace=ws, out=out)
         else:
             sv.spec_verify_greedy(copies[c], toks, out=out)
         if args.commit:
@@ -229,7 +250,10 @@ def main():
     dom = "row_stats" if cfg.mode == "sample" else "greedy_argmax"
     dom_ms, dom_n = prof[dom]
     dom_avg_ms = dom_ms / max(dom_n, 1)
-    achieved = algo_bytes / (dom_avg_ms / 1e3) / 1e9
+    # every used row is read once by the dominant kernel (in a mixed batch the
+    # target rows of greedy requests too, for their argmax)
+    dom_bytes = rows * cfg.V * s
+    achieved = dom_bytes / (dom_avg_ms / 1e3) / 1e9
     traffic = traffic_record(dom, cfg.name)
 
     n_acc = out.num_accepted.cpu().numpy()
@@ -260,6 +284,11 @@ def main():
         "mean_emitted_per_request": float(n_acc.mean() + 1),
         "flags_nonzero": int((flags != 0).sum()),
     }
+    if args.mixed:
+        res["config"]["mixed"] = ("a quarter greedy; draft lengths gamma, gamma-1, gamma-2; "
+                                  "T in {0.6, 0.8, 1.0, 1.2}, top-k in {0, 50}, top-p in "
+                                  "{0.9, 0.95, 1.0} per request")
+        res["roofline"]["algorithmic_bytes"] = dom_bytes
     if args.diagnostics:
         res["config"]["diagnostics"] = True
         diag = {"accept_hist": out.accept_hist.cpu().numpy().tolist()}

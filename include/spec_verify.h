@@ -255,8 +255,7 @@ const char* spec_verify_strerror(int status);
 #define SV_K_GREEDY_SCAN 3
 #define SV_K_OVERLAP 4
 #define SV_K_COMMIT 5
-#define SV_K_GREEDY_ROWS 6
-#define SV_NUM_KERNELS 7
+#define SV_NUM_KERNELS 6
 int spec_verify_profile_start(int32_t max_launches_per_kernel);
 int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 

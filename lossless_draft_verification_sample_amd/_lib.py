@@ -35,10 +35,8 @@ SV_K_GREEDY_ARGMAX = 2
 SV_K_GREEDY_SCAN = 3
 SV_K_OVERLAP = 4
 SV_K_COMMIT = 5
-SV_K_GREEDY_ROWS = 6
-SV_NUM_KERNELS = 7
-KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap", "commit",
-                "greedy_rows"]
+SV_NUM_KERNELS = 6
+KERNEL_NAMES = ["row_stats", "draw", "greedy_argmax", "greedy_scan", "overlap", "commit"]
 
 
 class SvSampler(ctypes.Structure):

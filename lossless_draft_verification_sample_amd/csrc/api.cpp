@@ -197,15 +197,8 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.out_tlse = out_target_lse;
     a.out_dlse = out_draft_lse;
     a.force_generic = 0;
-    {
-      ProfScope p(SV_K_ROW_STATS, st);
-      if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
-    }
-    if (req.ts) {
-      // target rows of greedy requests: their argmax replaces the RowStat
-      ProfScope p(SV_K_GREEDY_ROWS, st);
-      if (sv::launch_greedy_rows(a, bf16, B, st)) return SV_EHIP;
-    }
+    ProfScope p(SV_K_ROW_STATS, st);
+    if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
   }
   {
     sv::DrawArgs a{};

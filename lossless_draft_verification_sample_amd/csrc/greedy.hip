@@ -57,61 +57,6 @@ int launch_greedy_argmax(const GreedyArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// The target rows of the greedy requests of a mixed sampling batch: their
-// argmax (the request's target bans apply) goes into the row's RowStat
-// (path = argmax, px = 1 iff the row's proposal is the argmax, so that the
-// sampling walk's test u * q <= p with q = 1 accepts exactly on a match).
-// Rows of other requests, and rows beyond a request's draft length, return
-// at once. Runs after row_stats_kernel, whose RowStat of these rows it replaces.
-template <typename Elem>
-__global__ __launch_bounds__(GA_THREADS) void greedy_rows_kernel(RowStatsArgs a) {
-  __shared__ uint32_t tab[HT_SLOTS];
-  __shared__ float sv_[GA_THREADS / WAVE];
-  __shared__ int32_t si_[GA_THREADS / WAVE];
-  __shared__ uint32_t su_[GA_THREADS / WAVE];
-  __shared__ uint32_t xban;
-  const int G1 = a.gamma + 1, RPR = 2 * a.gamma + 1;
-  const int b = blockIdx.x / G1, i = blockIdx.x % G1;
-  const ReqInfo rq = request_info(a.req, b, a.gamma, a.st, a.sd);
-  if (rq.bad || !rq.greedy || i > rq.g) return;
-  const int tid = threadIdx.x, V = a.V;
-  const Elem* rowp = (const Elem*)a.target + ((int64_t)b * G1 + i) * (int64_t)V;
-  const int nb = a.banned ? a.n_banned : 0;
-  const uint32_t* bans = nullptr;
-  if (nb > 0) {
-    const int32_t* bl = a.banned + (int64_t)b * a.n_banned;
-    const int32_t first = tid < nb ? bl[tid] : -1;
-    for (uint32_t k = tid; k < HT_SLOTS; k += GA_THREADS) tab[k] = HT_EMPTY;
-    __syncthreads();
-    (void)ht_build(tab, bl, nb, V, first, -1, &xban);
-    __syncthreads();
-    bans = tab;
-  }
-  const ArgResult r =
-      bans ? row_argmax<Elem, GA_THREADS, GA_UNROLL, true>(rowp, V, bans, sv_, si_, su_)
-           : row_argmax<Elem, GA_THREADS, GA_UNROLL, false>(rowp, V, nullptr, sv_, si_, su_);
-  if (tid == 0) {
-    const int32_t x = i < rq.g ? a.draft_tokens[(int64_t)b * a.gamma + i] : -1;
-    RowStat out;
-    out.m = -INFINITY;
-    out.tau = -INFINITY;
-    out.lse = __builtin_nan("");
-    out.flags = (r.nonfinite ? FLAG_NONFINITE : 0u) | (r.arg < 0 ? FLAG_EMPTY : 0u);
-    out.path = (uint32_t)r.arg;
-    out.px = (x >= 0 && x == r.arg) ? 1.0 : 0.0;
-    a.stats[(int64_t)b * RPR + i] = out;
-  }
-}
-
-int launch_greedy_rows(const RowStatsArgs& a, int dtype_bf16, int B, hipStream_t st) {
-  const dim3 grid((unsigned)(B * (a.gamma + 1)));
-  if (dtype_bf16)
-    hipLaunchKernelGGL(greedy_rows_kernel<uint16_t>, grid, dim3(GA_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(greedy_rows_kernel<float>, grid, dim3(GA_THREADS), 0, st, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
 __global__ __launch_bounds__(WAVE) void greedy_scan_kernel(GreedyArgs a) {
   const int b = blockIdx.x * WAVE + threadIdx.x;
   if (b >= a.B) return;

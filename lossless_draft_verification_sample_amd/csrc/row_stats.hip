@@ -42,6 +42,7 @@
 // i < gamma: p_i(x_i); draft row i: q_i(x_i)), which is all the acceptance walk
 // needs from the row.
 
+#include "sv_argmax.hpp"
 #include "sv_bans.hpp"
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
@@ -575,6 +576,30 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
 // workgroups share, so a fourth one would not stream faster; it would only
 // force register spills in the epilogue and make the last round of rows
 // coarser (rows / (3 * CUs) is closer to a whole number for large batches).
+// The target row of a greedy request in a mixed batch: its argmax (the
+// request's target bans and NaN excluded) as the row's RowStat: path = the
+// argmax, px = 1 iff the row's proposal is the argmax (the sampling walk's
+// test u * q <= p with q = 1 then accepts exactly on a match). Not inlined:
+// its registers stay out of the statistics path's allocation.
+template <typename Elem>
+__device__ __attribute__((noinline)) void greedy_row_stat(const Elem* rowp, int V, const int32_t* bl,
+                                                          int nb, int32_t first, RowShared& sh,
+                                                          RowStat& out) {
+  const uint32_t* tab = nullptr;
+  if (nb > 0) {
+    for (uint32_t k = threadIdx.x; k < HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
+    __syncthreads();
+    (void)ht_build(sh.hist, bl, nb, V, first, -1, &sh.xban);
+    __syncthreads();
+    tab = sh.hist;
+  }
+  const ArgResult r =
+      tab ? row_argmax<Elem, RS_THREADS, 4, true>(rowp, V, tab, sh.fscr, sh.iscr, sh.uscr)
+          : row_argmax<Elem, RS_THREADS, 4, false>(rowp, V, nullptr, sh.fscr, sh.iscr, sh.uscr);
+  out.path = (uint32_t)r.arg;
+  out.flags = (r.nonfinite ? FLAG_NONFINITE : 0u) | (r.arg < 0 ? FLAG_EMPTY : 0u);
+}
+
 // MIXED: per-request draft lengths, samplers (greedy requests included) and
 // draft ban lists; the plain variant carries none of that logic.
 template <typename Elem, bool MIXED>
@@ -604,7 +629,8 @@ void row_stats_kernel(RowStatsArgs a) {
   const int pi = is_target ? i : i - G1;
   // rows the request does not use: beyond its draft length, the draft rows of
   // a greedy request, every row of a request with settings out of range
-  const bool used = !MIXED || (!rq.bad && !rq.greedy && pi <= rq.g && (is_target || pi < rq.g));
+  const bool used = !MIXED || (!rq.bad && pi <= rq.g && (is_target ? true : !rq.greedy && pi < rq.g));
+  const bool greedy_row = MIXED && used && rq.greedy;   // a target row: its argmax
   // draft rows take the draft ban list when there is one
   const bool dbans = MIXED && !is_target && a.req.banned_d;
   const int nb = !used ? 0 : dbans ? a.req.n_banned_d : (a.banned ? a.n_banned : 0);
@@ -628,11 +654,12 @@ void row_stats_kernel(RowStatsArgs a) {
   out.px = 0.0;
 
   bool generic = (sizeof(Elem) == 4) || a.force_generic;
-  const bool stats_path = used;
+  const bool stats_path = used && !greedy_row;
   if (!stats_path) generic = false;
-  // (the target rows of greedy requests are left to greedy_rows_kernel, which
-  // runs after this kernel and overwrites their RowStat)
-  if (MIXED && !used) out.flags = rq.bad ? FLAG_BAD_PARAM : 0u;
+  if constexpr (MIXED) {
+    if (!used) out.flags = rq.bad ? FLAG_BAD_PARAM : 0u;
+    if (greedy_row) greedy_row_stat<Elem>(rowp, V, bl, nb, ban0, sh, out);
+  }
 
   if (stats_path && !generic) {
     // the first HT_SLOTS bins hold the ban hash set until the stream starts
@@ -747,7 +774,8 @@ void row_stats_kernel(RowStatsArgs a) {
                         zx < INFINITY && zx >= out.tau;
       out.px = kept ? exp((double)zx / (double)s.temperature - out.lse) : 0.0;
     } else {
-      out.px = 0.0;
+      // greedy: the proposal survives (p = 1) iff it is the argmax
+      out.px = (greedy_row && xvalid && (int32_t)out.path == xprop) ? 1.0 : 0.0;
       out.lse = __builtin_nan("");
     }
     a.stats[row] = out;

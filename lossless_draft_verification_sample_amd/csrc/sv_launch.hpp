@@ -108,7 +108,6 @@ int launch_draw(const DrawArgs& a, int B, hipStream_t s);
 int launch_overlap(const OverlapArgs& a, int bf16, int pairs, hipStream_t s);
 int launch_greedy_argmax(const GreedyArgs& a, hipStream_t s);
 int launch_greedy_scan(const GreedyArgs& a, hipStream_t s);
-int launch_greedy_rows(const RowStatsArgs& a, int dtype_bf16, int B, hipStream_t s);
 int launch_commit(const CommitArgs& a, hipStream_t s);
 
 }  // namespace sv

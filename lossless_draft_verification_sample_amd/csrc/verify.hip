@@ -195,7 +195,7 @@ struct DrawShared {
 // Outputs of a request of a mixed batch that needs no draw, written by one
 // wave: a request with settings out of range (nothing accepted, no token), or
 // a greedy request (the walk of greedy verification over the argmaxes that
-// greedy_rows_kernel left in the target rows' RowStat).
+// the row pass left in the target rows' RowStat).
 __device__ __forceinline__ void finish_without_draw(const DrawArgs& a, int b, const ReqInfo& rq) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
