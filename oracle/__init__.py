@@ -14,6 +14,10 @@ Parity status of each function (what pins it to something other than itself):
                      closed form (1 - a^(g+1)) / (1 - a) and the survival form by
                      Monte Carlo; chi-square of emitted tokens against p.
   verify_greedy      pinned: brute-force loop over small rows (bans included).
+  repetition_penalty pinned: theta = 1 is the identity, sign handling, never
+                     raises a logit, bf16 results are bf16 values (round_to_bf16
+                     against the bit-level definition and NumPy), and sampled
+                     outputs follow the penalized p.
   verify_batch       pinned: each request equals the same request verified
                      alone by verify_sample / verify_greedy on its own rows;
                      a request with g_b proposals equals a gamma = g_b batch.
@@ -54,9 +58,12 @@ from .verifier import (  # noqa: F401
     accept,
     first_token_law,
     greedy_argmax,
+    repetition_penalty,
     residual_weights,
+    round_to_bf16,
     row_distribution,
     sample_categorical,
+    penalty_valid,
     sampler_valid,
     verify_batch,
     verify_block,

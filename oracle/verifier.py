@@ -71,13 +71,36 @@ class RowDist:
     topp_margin: float = math.inf   # distance of the top-p cut to its edge (inf if off)
 
 
-def row_distribution(z, sampler, banned_ids=()):
+def round_to_bf16(x):
+    """The bf16 value nearest to float32 x (ties to the even mantissa), as a
+    float: the 16 low bits of the float32 pattern are rounded away."""
+    bits = int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+    lsb = (bits >> 16) & 1
+    r = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return float(np.array([r & 0xFFFFFFFF], dtype=np.uint32).view(np.float32)[0])
+
+
+def repetition_penalty(z, theta, dtype):
+    """Repetition penalty of one logit: the multiplicative penalty of Keskar et
+    al. 2019 ("CTRL", section 4.1) in the sign-aware form inference engines
+    use, z / theta for z > 0 and z * theta otherwise, theta >= 1. Computed in
+    float32 and, for a bf16 row, rounded to bf16 like any op on a bf16 logits
+    tensor, so the penalized logit is a value of the row's own dtype."""
+    z32 = np.float32(z)
+    t32 = np.float32(theta)
+    v = float(z32 / t32) if z32 > 0 else float(z32 * t32)
+    return round_to_bf16(v) if dtype == "bf16" else v
+
+
+def row_distribution(z, sampler, banned_ids=(), penalized=(), penalty=1.0, dtype="f32"):
     """Sampler-transformed distribution of one logit row.
 
     [ATLAS] "Greedy, sampling and the real sampler" and [DRAFT] "Distribution,
-    seeded output and quality": temperature, truncation and bans must live
-    inside p and q. Steps, in order:
+    seeded output and quality": temperature, truncation, bans and repetition
+    penalties must live inside p and q. Steps, in order:
       (i)   admissible set K: finite logits that are not banned (-inf = masked);
+      (i')  repetition penalty (repetition_penalty) of the admissible tokens in
+            `penalized` (each token once), for a row of dtype `dtype`;
       (ii)  tempered logits s = z / T;
       (iii) top-k: keep z >= the k-th largest admissible logit (multiplicity
             counted, ties kept);
@@ -99,6 +122,13 @@ def row_distribution(z, sampler, banned_ids=()):
         tok = int(tok)
         if 0 <= tok < V:
             kept[tok] = False
+
+    # (i') repetition penalty
+    if _f32(penalty) != 1.0:
+        z = z.copy()
+        for tok in sorted(set(int(t) for t in penalized)):
+            if 0 <= tok < V and kept[tok]:
+                z[tok] = repetition_penalty(z[tok], penalty, dtype)
 
     # (ii) temperature
     s = np.full(V, -np.inf)
@@ -309,13 +339,14 @@ def verify_block(p_rows, q_rows, xs, u):
     return tokens, n, f, margin, acc_prob
 
 
-def greedy_argmax(z, banned_ids=()):
+def greedy_argmax(z, banned_ids=(), penalized=(), penalty=1.0, dtype="f32"):
     """Argmax of one target row for greedy verification ([DRAFT] "Greedy
     verification"; [ATLAS] "Greedy, sampling and the real sampler": bans are
     part of the real sampler). Admissible tokens are those not banned whose
     logit is not NaN; the result is the lowest admissible id holding the
     largest admissible logit (-inf included, so a row of -inf still has an
-    argmax), or -1 when nothing is admissible.
+    argmax), or -1 when nothing is admissible. Tokens in `penalized` compete
+    with their repetition_penalty value.
     """
     z = np.asarray(z, dtype=np.float64)
     adm = ~np.isnan(z)
@@ -323,6 +354,11 @@ def greedy_argmax(z, banned_ids=()):
         tok = int(tok)
         if 0 <= tok < z.size:
             adm[tok] = False
+    if _f32(penalty) != 1.0:
+        z = z.copy()
+        for tok in sorted(set(int(t) for t in penalized)):
+            if 0 <= tok < z.size and adm[tok] and np.isfinite(z[tok]):
+                z[tok] = repetition_penalty(z[tok], penalty, dtype)
     if not adm.any():
         return -1
     m = z[adm].max()
@@ -387,8 +423,14 @@ def sampler_valid(s, allow_greedy):
     return k >= 0 and 0.0 < P <= 1.0
 
 
+def penalty_valid(theta):
+    t = _f32(theta)
+    return math.isfinite(t) and t >= 1.0
+
+
 def verify_batch(target, draft, draft_tokens, uniforms, target_samplers, draft_samplers,
-                 banned=None, banned_draft=None, gammas=None):
+                 banned=None, banned_draft=None, gammas=None, history=None, penalties=None,
+                 penalties_draft=None, dtype="f32"):
     """A mixed batch: per-request draft lengths, samplers and draft bans.
 
     target [B, gamma+1, V], draft [B, gamma, V], draft_tokens [B, gamma] and
@@ -403,6 +445,13 @@ def verify_batch(target, draft, draft_tokens, uniforms, target_samplers, draft_s
     greedy_argmax. A draft length or sampler setting out of range gives flag
     FLAG_BAD_PARAM, no accepted proposal and no token. lse of rows a request
     does not use (and of every row of a greedy request) is NaN.
+
+    Repetition penalties: history [B, H] (-1 = padding) holds each request's
+    generated tokens before the round; penalties [B] / penalties_draft [B]
+    are the target / draft factors theta >= 1 (None: 1 = off). Row i of a
+    request penalizes its history and the proposals x_0 .. x_{i-1} that
+    precede position i (the tokens its sampler had seen); `dtype` ("bf16" or
+    "f32") is the logits' dtype, in which the penalized values are rounded.
 
     [ATLAS] "Implementation roadmap and tests" (continuous batching with
     per-request metadata); [ATLAS] "Greedy, sampling and the real sampler".
@@ -425,23 +474,43 @@ def verify_batch(target, draft, draft_tokens, uniforms, target_samplers, draft_s
         gb = gamma if gammas is None else int(gammas[b])
         ts, ds = target_samplers[b], draft_samplers[b]
         greedy = _f32(ts.temperature) == 0.0
-        if not (0 <= gb <= gamma) or not sampler_valid(ts, True) or (
-                not greedy and not sampler_valid(ds, False)):
+        th_t = 1.0 if penalties is None else float(penalties[b])
+        th_d = 1.0 if penalties_draft is None else float(penalties_draft[b])
+        if not (0 <= gb <= gamma) or not sampler_valid(ts, True) or not penalty_valid(th_t) or (
+                not greedy and (not sampler_valid(ds, False) or not penalty_valid(th_d))):
             flags[b] = FLAG_BAD_PARAM
             continue
+        hist = [] if history is None else [int(t) for t in np.asarray(history[b]).tolist() if t >= 0]
         tb = () if banned is None else [t for t in np.asarray(banned[b]).tolist() if t >= 0]
         db = tb if banned_draft is None else [t for t in np.asarray(banned_draft[b]).tolist()
                                               if t >= 0]
         xs = [int(x) for x in draft_tokens[b, :gb]]
         if greedy:
-            r = verify_greedy(target[b:b + 1, :gb + 1], np.array([xs], dtype=np.int64).reshape(1, gb),
-                              None if banned is None else [tb])
-            tokens[b, :gb + 1] = r.tokens[0]
-            num_acc[b] = r.num_accepted[0]
-            flags[b] = r.flags[0]
+            # verify_greedy's walk over penalized argmaxes
+            f = 0
+            am = []
+            for i in range(gb + 1):
+                row = target[b, i]
+                if np.any(np.isnan(row) | (row == np.inf)):
+                    f |= FLAG_NONFINITE
+                am.append(greedy_argmax(row, tb, hist + xs[:i], th_t, dtype))
+            if any(x < 0 or x >= V for x in xs):
+                f |= FLAG_TOKEN_RANGE
+            n = gb
+            for i in range(gb):
+                if xs[i] != am[i]:
+                    n = i
+                    break
+                tokens[b, i] = xs[i]
+            tokens[b, n] = am[n]
+            if am[n] < 0:
+                f |= FLAG_EMPTY
+            num_acc[b] = n
+            flags[b] = f
             continue
-        pt = [row_distribution(target[b, i], ts, tb) for i in range(gb + 1)]
-        qd = [row_distribution(draft[b, i], ds, db) for i in range(gb)]
+        pt = [row_distribution(target[b, i], ts, tb, hist + xs[:i], th_t, dtype)
+              for i in range(gb + 1)]
+        qd = [row_distribution(draft[b, i], ds, db, hist + xs[:i], th_d, dtype) for i in range(gb)]
         f = 0
         mg = math.inf
         for d in pt + qd:
