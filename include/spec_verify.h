@@ -84,7 +84,8 @@ typedef struct {
 #define SV_FLAG_RESIDUAL_ZERO 16u /* residual mass was 0 at a rejection; drawn from p */
 #define SV_FLAG_BAD_PARAM 32u     /* a per-request setting of sv_requests is out of range */
 
-#define SV_MAX_BANNED 2048 /* largest n_banned accepted */
+#define SV_MAX_BANNED 2048  /* largest n_banned accepted */
+#define SV_MAX_HISTORY 4096 /* largest sv_requests.n_history accepted */
 
 /* Per-request settings of a mixed batch ("Speculative Decoding - Turn guesses
  * into parallel work", section "Implementation roadmap and tests": continuous
@@ -104,8 +105,21 @@ typedef struct {
  *   draft         draft sampler of each request (ignored for greedy requests).
  *   banned_draft  [B][n_banned_draft] bans of the draft rows; banned_ids then
  *                 applies to the target rows only (same list rules).
- * A request whose gamma[b] or sampler fields are out of range (the ranges of
- * sv_sampler; temperature 0 only as a target) is not verified: flag
+ *   history       [B][n_history] tokens each request generated before this
+ *                 round (-1 or ids outside [0, V) are padding), for the
+ *                 repetition penalty; n_history <= SV_MAX_HISTORY.
+ *   penalty       [B] repetition penalty theta >= 1 of the target rows (1:
+ *                 off); penalty_draft [B] likewise for the draft rows. Row i
+ *                 of a request penalizes its history and the proposals
+ *                 x_0 .. x_{i-1} before position i (the tokens its sampler had
+ *                 seen), each id once, banned ids excepted: a logit z becomes
+ *                 z / theta if z > 0, else z * theta (Keskar et al. 2019,
+ *                 "CTRL", section 4.1, sign-aware form), computed in float32
+ *                 and rounded to bf16 for bf16 logits; the penalty comes after
+ *                 the bans and before temperature and truncation.
+ * A request whose gamma[b], sampler fields or penalties are out of range (the
+ * ranges of sv_sampler; temperature 0 only as a target; a penalty below 1 or
+ * not finite) is not verified: flag
  * SV_FLAG_BAD_PARAM, no accepted proposal, out_tokens row all -1. Rows a
  * request does not use report NaN in out_target_lse / out_draft_lse, and so
  * do the rows of greedy requests; out_overlap is NaN at positions a request
@@ -116,6 +130,10 @@ typedef struct {
   const sv_sampler* draft;
   const int32_t* banned_draft;
   int32_t n_banned_draft;
+  const int32_t* history;
+  int32_t n_history;
+  const float* penalty;
+  const float* penalty_draft;
 } sv_requests;
 
 /* Workspace bytes needed by spec_verify_sample for these sizes (0 on bad sizes;

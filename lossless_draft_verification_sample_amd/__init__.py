@@ -37,8 +37,11 @@ GreedyOut = namedtuple("GreedyOut", "tokens num_accepted flags accept_hist", def
 CommitOut = namedtuple("CommitOut", "new_kv_len anchor n_free free_slots")
 # Per-request settings of a mixed batch (see sv_requests in include/spec_verify.h):
 # gamma [B] int32, target / draft [B, 12] uint8 sv_sampler records (sampler_array),
-# banned_draft [B, m] int32; None keeps the call-wide value.
-Requests = namedtuple("Requests", "gamma target draft banned_draft", defaults=(None,) * 4)
+# banned_draft [B, m] int32, history [B, H] int32, penalty / penalty_draft [B]
+# float32 repetition penalties; None keeps the call-wide value (no penalty).
+Requests = namedtuple("Requests",
+                      "gamma target draft banned_draft history penalty penalty_draft",
+                      defaults=(None,) * 7)
 
 
 class SpecVerifyError(RuntimeError):
@@ -119,9 +122,17 @@ def _requests(req, B):
         nbd = int(req.banned_draft.shape[1])
         if tuple(req.banned_draft.shape) != (B, nbd):
             raise ValueError("requests.banned_draft must be [B, n]")
+    nh = 0
+    if req.history is not None:
+        nh = int(req.history.shape[1])
+        if tuple(req.history.shape) != (B, nh):
+            raise ValueError("requests.history must be [B, H]")
     r = SvRequests(_dev_ptr(req.gamma, "requests.gamma", torch.int32),
                    _dev_ptr(req.target, "requests.target"), _dev_ptr(req.draft, "requests.draft"),
-                   _dev_ptr(req.banned_draft, "requests.banned_draft", torch.int32), nbd)
+                   _dev_ptr(req.banned_draft, "requests.banned_draft", torch.int32), nbd,
+                   _dev_ptr(req.history, "requests.history", torch.int32), nh,
+                   _checked(req.penalty, "requests.penalty", torch.float32, (B,)),
+                   _checked(req.penalty_draft, "requests.penalty_draft", torch.float32, (B,)))
     return ctypes.byref(r), r
 
 

@@ -28,6 +28,7 @@ SV_FLAG_RESIDUAL_ZERO = 16
 SV_FLAG_BAD_PARAM = 32
 
 SV_MAX_BANNED = 2048
+SV_MAX_HISTORY = 4096
 
 SV_K_ROW_STATS = 0
 SV_K_DRAW = 1
@@ -48,7 +49,9 @@ class SvRequests(ctypes.Structure):
     """sv_requests: device pointers (as integers) of per-request arrays."""
     _fields_ = [("gamma", ctypes.c_void_p), ("target", ctypes.c_void_p),
                 ("draft", ctypes.c_void_p), ("banned_draft", ctypes.c_void_p),
-                ("n_banned_draft", ctypes.c_int32)]
+                ("n_banned_draft", ctypes.c_int32), ("history", ctypes.c_void_p),
+                ("n_history", ctypes.c_int32), ("penalty", ctypes.c_void_p),
+                ("penalty_draft", ctypes.c_void_p)]
 
 
 _c = ctypes

@@ -23,6 +23,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-ffp-contract=off",
+    # IEEE float32 division: the repetition penalty divides logits
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",

@@ -159,6 +159,13 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     // a draft list (even an empty one) replaces banned_ids for the draft rows
     req.banned_d = requests->banned_draft;
     req.n_banned_d = requests->banned_draft ? requests->n_banned_draft : 0;
+    if (requests->n_history < 0 || requests->n_history > SV_MAX_HISTORY ||
+        (requests->n_history > 0 && !requests->history))
+      return SV_EINVAL;
+    req.history = requests->n_history > 0 ? requests->history : nullptr;
+    req.n_history = req.history ? requests->n_history : 0;
+    req.pen_t = requests->penalty;
+    req.pen_d = requests->penalty_draft;
   }
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)target_logits % es) || ((uintptr_t)draft_logits % es)) return SV_EINVAL;
@@ -248,6 +255,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.banned = bans;
     a.n_banned = n_banned;
     a.stats = stats;
+    a.draft_tokens = draft_tokens;
     a.partial = ov_partial;
     a.tickets = ov_tickets;
     a.out_overlap = out_overlap;

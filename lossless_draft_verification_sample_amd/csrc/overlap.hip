@@ -36,12 +36,16 @@ constexpr int OV_GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave o
 
 constexpr int OV_QCAP = 4 * WAVE;   // queued kept tokens per wave: one batch of 4 loads per lane
 
+// The bitmaps of mixed batches take LDS only in the MIXED variant.
+template <bool MIXED>
 struct OverlapShared {
+  static constexpr int BMW = OV_SPW_MAX * DRAW_SUB / 32;
   double etab[256];
   QueuedTok q[OV_NW][OV_QCAP];
-  uint32_t bm[OV_SPW_MAX * DRAW_SUB / 32];    // bans of the target row (of both rows
-                                            // unless the draft rows have their own list)
-  uint32_t bmd[OV_SPW_MAX * DRAW_SUB / 32];   // the draft rows' own bans (mixed batches)
+  uint32_t bm[BMW];                  // bans of the target row (of both rows unless the
+                                     // draft rows have their own list)
+  uint32_t bmd[MIXED ? BMW : 1];     // the draft rows' own bans
+  uint32_t bmp[MIXED ? BMW : 1];     // repetition-penalized ids
   double w[OV_NW];
 };
 
@@ -57,14 +61,16 @@ struct OvPair {
   int dnb;            // bans in the draft rows' own list
   bool sep;           // the draft rows have their own ban list (bmd)
   bool vec;
+  bool tpen, dpen;    // the target / draft logits of the ids in bmp are penalized
+  float pt, pd;       // their repetition penalties
 };
 
 // The wave's sum of min(p, q) over its sub-chunks wv, wv + OV_NW, ... .
 // LEAD 0: the target row is truncated and leads: it is read in full and the
 // draft row only where the target keeps a token; LEAD 1: the reverse; LEAD 2:
 // neither is truncated and both rows are read in full.
-template <typename Elem, int LEAD>
-__device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, int wv, int lane) {
+template <typename Elem, int LEAD, typename Shared>
+__device__ __forceinline__ double ov_stream(const OvPair& r, Shared& sh, int wv, int lane) {
   constexpr bool FULL_T = LEAD != 1, FULL_D = LEAD != 0;
   auto term = [&](float zt, float zd) {
     const double lt = fma((double)zt, r.tinv, -r.ts.lse);
@@ -78,6 +84,10 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
   };
   // the other row's bans need a test of their own only when the lists differ
   auto obits = [&](int o) -> uint32_t { return !r.sep ? 0u : LEAD == 1 ? tbits(o) : dbits(o); };
+  // the repetition penalty of the ids marked in bmp, per side
+  auto pen_bits = [&](int o) -> uint32_t { return bm_group(sh.bmp, o); };
+  const bool lpen = LEAD == 1 ? r.dpen : r.tpen, open_ = LEAD == 1 ? r.tpen : r.dpen;
+  const float lth = LEAD == 1 ? r.pd : r.pt, oth = LEAD == 1 ? r.pt : r.pd;
   const void* lrow = LEAD == 1 ? r.drow : r.trow;   // leading row
   const void* orow = LEAD == 1 ? r.trow : r.drow;   // the other row
   const RowStat& ls = LEAD == 1 ? r.ds : r.ts;
@@ -97,6 +107,11 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
         const QueuedTok t = sh.q[wv][j];
         zl[u] = t.z;
         zo[u] = load_logit<Elem>(orow, t.x);
+        if (open_) {
+          const int o = t.x - r.tok0;
+          if (((sh.bmp[o >> 5] >> (o & 31)) & 1u) && zo[u] > -INFINITY && zo[u] < INFINITY)
+            zo[u] = pen_apply(zo[u], oth, sizeof(Elem) == 2);
+        }
       }
     }
 #pragma unroll
@@ -132,8 +147,15 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
     Group<Elem> tg[OV_GPL], dg[OV_GPL];
 #pragma unroll
     for (int k = 0; k < OV_GPL; ++k) {
-      if constexpr (FULL_T) tg[k] = tn[k];
-      if constexpr (FULL_D) dg[k] = dn[k];
+      const int x0 = sbase + (lane + k * WAVE) * GRP;
+      if constexpr (FULL_T) {
+        tg[k] = tn[k];
+        if (r.tpen && x0 < r.V) penalize_group<Elem>(tg[k], pen_bits(x0 - r.tok0), r.pt);
+      }
+      if constexpr (FULL_D) {
+        dg[k] = dn[k];
+        if (r.dpen && x0 < r.V) penalize_group<Elem>(dg[k], pen_bits(x0 - r.tok0), r.pd);
+      }
     }
     if (sl + OV_NW < r.nsl) issue(sl + OV_NW);
     // kept in the leading row (in both rows when neither leads); bans apply to
@@ -209,6 +231,7 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
           const int x0 = sbase + (lane + k * WAVE) * GRP;
           Group<Elem> og;
           load_group<Elem>(orow, x0, r.V, r.vec, og);
+          if (open_) penalize_group<Elem>(og, pen_bits(x0 - r.tok0), oth);
           const Group<Elem>& lg = LEAD == 1 ? dg[k] : tg[k];
           const uint32_t ob = obits(x0 - r.tok0);
 #pragma unroll
@@ -233,7 +256,7 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, OverlapShared& sh, 
 // with settings out of range) gets NaN.
 template <typename Elem, bool MIXED>
 __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
-  __shared__ OverlapShared sh;
+  __shared__ OverlapShared<MIXED> sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
   const int pair = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
@@ -267,12 +290,35 @@ __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
   const int32_t* bl = r.nb ? a.banned + (int64_t)b * a.n_banned : nullptr;
   const int32_t ban0 = tid < r.nb ? bl[tid] : -1;
   r.sep = MIXED && a.req.banned_d != nullptr;
+  // repetition penalty of the pair's rows: the history and the proposals
+  // before position i
+  const int H = (MIXED && a.req.history) ? a.req.n_history : 0;
+  r.pt = MIXED ? rq.pt : 1.0f;
+  r.pd = MIXED ? rq.pd : 1.0f;
+  r.tpen = MIXED && !empty && r.pt != 1.0f && H + i > 0;
+  r.dpen = MIXED && !empty && r.pd != 1.0f && H + i > 0;
   r.dnb = (r.sep && !empty) ? a.req.n_banned_d : 0;
   const int32_t* dbl = r.dnb ? a.req.banned_d + (int64_t)b * a.req.n_banned_d : nullptr;
   const int32_t dban0 = tid < r.dnb ? dbl[tid] : -1;
 
   exp_table_fill(sh.etab);
   if (r.dnb > 0) mark_bans(sh.bmd, r.nsl * DRAW_SUB, dbl, r.dnb, dban0, r.tok0, r.V);
+  if (r.tpen || r.dpen) {
+    // the pair's penalized ids in the workgroup's range (as mark_pen, written
+    // out here: the shared helper crashed this compiler's inliner in this kernel)
+    const int len = r.nsl * DRAW_SUB;
+    for (int k = tid; k < len / 32; k += OV_THREADS) sh.bmp[k] = 0u;
+    __syncthreads();
+    for (int j = tid; j < H + i; j += OV_THREADS) {
+      const int32_t id = j < H ? a.req.history[(int64_t)b * a.req.n_history + j]
+                               : a.draft_tokens[(int64_t)b * g + (j - H)];
+      if (id >= r.tok0 && id < r.V && id - r.tok0 < len) {
+        const int o = id - r.tok0;
+        atomicOr(&sh.bmp[o >> 5], 1u << (o & 31));
+      }
+    }
+    __syncthreads();
+  }
   if (r.nb > 0)
     mark_bans(sh.bm, r.nsl * DRAW_SUB, bl, r.nb, ban0, r.tok0, r.V);   // also publishes etab
   else
@@ -314,7 +360,8 @@ __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
 
 int launch_overlap(const OverlapArgs& a, int bf16, int pairs, hipStream_t st) {
   const dim3 grid((unsigned)(pairs * a.parts)), block(OV_THREADS);
-  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d;
+  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d || a.req.pen_t ||
+                     a.req.pen_d || a.req.history;
   if (bf16) {
     if (mixed)
       hipLaunchKernelGGL((overlap_kernel<uint16_t, true>), grid, block, 0, st, a);

@@ -100,6 +100,7 @@ struct RowShared {
   float tiny_top;
   WaveSlot x1[RS_THREADS / WAVE], x2[RS_THREADS / WAVE], x3[RS_THREADS / WAVE];
   uint32_t xban;       // the row's proposal token is banned
+  uint32_t xpen;       // the row's proposal token is penalized
   double dscr[RS_THREADS / WAVE];
   float fscr[RS_THREADS / WAVE];
   uint32_t uscr[RS_THREADS / WAVE];
@@ -192,11 +193,18 @@ __device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
 
 // Admissibility test of the generic path: finite and not in the ban set.
 struct GenericCtx {
-  const uint32_t* tab;   // LDS hash set, or nullptr when the request bans nothing
+  const uint32_t* tab;    // LDS hash set, or nullptr when the request bans nothing
+  const uint32_t* ptab;   // LDS hash set of the penalized ids, or nullptr
+  float theta;            // their repetition penalty
+  bool bf16;              // penalized values are rounded to bf16
   __device__ __forceinline__ bool admissible(float z, int id) const {
     // finite and not banned; NaN fails both comparisons
     if (!(z > -INFINITY && z < INFINITY)) return false;
     return !tab || !ht_has(tab, id);
+  }
+  // the logit of an admissible token after the repetition penalty
+  __device__ __forceinline__ float value(float z, int id) const {
+    return (ptab && ht_has(ptab, id)) ? pen_apply(z, theta, bf16) : z;
   }
 };
 
@@ -226,6 +234,7 @@ __device__ __forceinline__ void row_generic(const Elem* rowp, int V, const Sampl
   for_each_elem<Elem>(rowp, V, [&](float z, int id) {
     if (z != z || z == INFINITY) bad = 1u;
     if (!g.admissible(z, id)) return;
+    z = g.value(z, id);
     ++cnt;
     mn = fminf(mn, z);
     if (z > mx) mx = z;
@@ -257,14 +266,17 @@ __device__ __forceinline__ void row_generic(const Elem* rowp, int V, const Sampl
   auto mass_ge = [&](float thr) -> double {
     double a = 0.0;
     for_each_elem<Elem>(rowp, V, [&](float z, int id) {
-      if (z >= thr && g.admissible(z, id)) a += exp2((double)z * c2 - rmax);
+      if (!g.admissible(z, id)) return;
+      z = g.value(z, id);
+      if (z >= thr) a += exp2((double)z * c2 - rmax);
     });
     return block_sum<RS_THREADS>(a, sh.dscr);
   };
   auto count_ge = [&](float thr) -> uint32_t {
     uint32_t a = 0;
     for_each_elem<Elem>(rowp, V, [&](float z, int id) {
-      if (z >= thr && g.admissible(z, id)) ++a;
+      if (!g.admissible(z, id)) return;
+      if (g.value(z, id) >= thr) ++a;
     });
     return block_sum<RS_THREADS>(a, sh.uscr);
   };
@@ -576,26 +588,71 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
 // workgroups share, so a fourth one would not stream faster; it would only
 // force register spills in the epilogue and make the last round of rows
 // coarser (rows / (3 * CUs) is closer to a whole number for large batches).
+// The ids a row penalizes: entry j < H of the request's history `hist`, then
+// the proposals props[0 .. npen-H-1] that precede the row's position.
+__device__ __forceinline__ int32_t pen_id(const int32_t* hist, int H, const int32_t* props, int j) {
+  return j < H ? hist[j] : props[j - H];
+}
+
+// Inserts the row's penalized ids (valid, not banned) into the LDS hash set
+// `ptab` (all slots HT_EMPTY beforehand). Bit k of the result is set when this
+// thread's k-th entry (j = threadIdx.x + k * RS_THREADS) entered the set, so
+// every distinct id has one owner. Sets *xpen when the row's proposal x is one.
+__device__ __forceinline__ uint32_t pen_build(uint32_t* ptab, const uint32_t* bantab,
+                                              const int32_t* hist, int H, const int32_t* props,
+                                              int npen, int V, int32_t x, uint32_t* xpen) {
+  uint32_t own = 0u;
+  int k = 0;
+  for (int j = threadIdx.x; j < npen; j += RS_THREADS, ++k) {
+    const int32_t id = pen_id(hist, H, props, j);
+    if (id < 0 || id >= V) continue;
+    if (bantab && ht_has(bantab, id)) continue;   // banned wins
+    if (id == x) *xpen = 1u;
+    uint32_t slot = ht_slot(id);
+    while (true) {
+      const uint32_t old = atomicCAS(&ptab[slot], HT_EMPTY, (uint32_t)id);
+      if (old == HT_EMPTY) {
+        own |= 1u << k;
+        break;
+      }
+      if (old == (uint32_t)id) break;
+      slot = (slot + 1u) & (HT_SLOTS - 1u);
+    }
+  }
+  return own;
+}
+
 // The target row of a greedy request in a mixed batch: its argmax (the
 // request's target bans and NaN excluded) as the row's RowStat: path = the
 // argmax, px = 1 iff the row's proposal is the argmax (the sampling walk's
 // test u * q <= p with q = 1 then accepts exactly on a match). Not inlined:
 // its registers stay out of the statistics path's allocation.
 template <typename Elem>
-__device__ __attribute__((noinline)) void greedy_row_stat(const Elem* rowp, int V, const int32_t* bl,
-                                                          int nb, int32_t first, RowShared& sh,
+__device__ __attribute__((noinline)) void greedy_row_stat(const Elem* rowp, int V,
+                                                          const int32_t* bl, int nb, int32_t first,
+                                                          const int32_t* hist, int H,
+                                                          const int32_t* props, int npen,
+                                                          float theta, RowShared& sh,
                                                           RowStat& out) {
   const uint32_t* tab = nullptr;
-  if (nb > 0) {
-    for (uint32_t k = threadIdx.x; k < HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
+  const uint32_t* ptab = nullptr;
+  if (nb > 0 || npen > 0) {
+    for (uint32_t k = threadIdx.x; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
     __syncthreads();
+  }
+  if (nb > 0) {
     (void)ht_build(sh.hist, bl, nb, V, first, -1, &sh.xban);
     __syncthreads();
     tab = sh.hist;
   }
-  const ArgResult r =
-      tab ? row_argmax<Elem, RS_THREADS, 4, true>(rowp, V, tab, sh.fscr, sh.iscr, sh.uscr)
-          : row_argmax<Elem, RS_THREADS, 4, false>(rowp, V, nullptr, sh.fscr, sh.iscr, sh.uscr);
+  if (npen > 0) {
+    (void)pen_build(sh.hist + HT_SLOTS, tab, hist, H, props, npen, V, -1, &sh.xpen);
+    __syncthreads();
+    ptab = sh.hist + HT_SLOTS;
+  }
+  // one instantiation with run-time tests of both sets keeps this call small
+  const ArgResult r = row_argmax<Elem, RS_THREADS, 4, true, true>(rowp, V, tab, sh.fscr, sh.iscr,
+                                                                  sh.uscr, ptab, theta);
   out.path = (uint32_t)r.arg;
   out.flags = (r.nonfinite ? FLAG_NONFINITE : 0u) | (r.arg < 0 ? FLAG_EMPTY : 0u);
 }
@@ -643,7 +700,16 @@ void row_stats_kernel(RowStatsArgs a) {
   const bool xvalid = xprop >= 0 && xprop < V;
   const float zx = (tid == 0 && xvalid) ? elem_value<Elem>(rowp[xprop]) : 0.0f;
   const int32_t ban0 = tid < nb ? bl[tid] : -1;
-  if (tid == 0) sh.xban = 0u;
+  if (tid == 0) {
+    sh.xban = 0u;
+    sh.xpen = 0u;
+  }
+  // repetition penalty of the row: its history and the proposals before it
+  const float theta = is_target ? rq.pt : rq.pd;
+  const int H = (MIXED && a.req.history) ? a.req.n_history : 0;
+  const int npen = (MIXED && used && theta != 1.0f) ? H + pi : 0;
+  const int32_t* hist = H ? a.req.history + (int64_t)b * a.req.n_history : nullptr;
+  const int32_t* props = a.draft_tokens + (int64_t)b * a.gamma;
 
   RowStat out;
   out.m = -INFINITY;
@@ -658,13 +724,15 @@ void row_stats_kernel(RowStatsArgs a) {
   if (!stats_path) generic = false;
   if constexpr (MIXED) {
     if (!used) out.flags = rq.bad ? FLAG_BAD_PARAM : 0u;
-    if (greedy_row) greedy_row_stat<Elem>(rowp, V, bl, nb, ban0, sh, out);
+    if (greedy_row) greedy_row_stat<Elem>(rowp, V, bl, nb, ban0, hist, H, props, npen, theta, sh, out);
   }
 
   if (stats_path && !generic) {
     // the first HT_SLOTS bins hold the ban hash set until the stream starts
     const uint32_t fill = nb > 0 ? HT_EMPTY : 0u;
-    for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS) sh.hist[k] = k < HT_SLOTS ? fill : 0u;
+    const uint32_t pfill = npen > 0 ? HT_EMPTY : 0u;
+    for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS)
+      sh.hist[k] = k < HT_SLOTS ? fill : (k < 2 * HT_SLOTS ? pfill : 0u);
     if (tid == 0) {
       sh.zero_cnt = 0u;
       sh.nonfinite = 0u;
@@ -674,13 +742,22 @@ void row_stats_kernel(RowStatsArgs a) {
     __syncthreads();
 
     const uint16_t* rp = (const uint16_t*)rowp;
-    uint32_t own = 0u, ban_bits = 0u;
+    uint32_t own = 0u, ban_bits = 0u, own_p = 0u;
     if (nb > 0) {
       own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
       // the banned logits are gathered now and subtracted after the stream
       if (own & 1u) ban_bits = rp[ban0];
       __syncthreads();
-      for (uint32_t k = tid; k < HT_SLOTS; k += RS_THREADS) sh.hist[k] = 0u;
+    }
+    if (MIXED && npen > 0) {
+      // penalized ids: their counts move from z to the penalized value after
+      // the stream (the set sits behind the ban set, in the same storage)
+      own_p = pen_build(sh.hist + HT_SLOTS, nb > 0 ? sh.hist : nullptr, hist, H, props, npen, V,
+                        xprop, &sh.xpen);
+      __syncthreads();
+    }
+    if (nb > 0 || (MIXED && npen > 0)) {
+      for (uint32_t k = tid; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = 0u;
       __syncthreads();
     }
     const uintptr_t addr = (uintptr_t)rp;
@@ -733,6 +810,26 @@ void row_stats_kernel(RowStatsArgs a) {
       else if (ae < HB_BASE)
         sh.special = 1u;   // a banned tiny value: the generic path sorts it out
     }
+    if constexpr (MIXED) {
+      // each distinct penalized id moves one count from its logit to the
+      // penalized logit (a bf16 value); values outside the counted window on
+      // either side send the row to the generic path
+      int kp = 0;
+      for (int j = tid; j < npen; j += RS_THREADS, ++kp) {
+        if (!((own_p >> kp) & 1u)) continue;
+        const uint32_t bits = rp[pen_id(hist, H, props, j)];
+        const float z = bf16_to_f32(bits);
+        if (!(z > -INFINITY && z < INFINITY)) continue;   // not admissible: nothing to move
+        const uint32_t nbits = __float_as_uint(pen_apply(z, theta, true)) >> 16;
+        const uint32_t t0 = (bits & 0x7FFFu) - HB_BASE, t1 = (nbits & 0x7FFFu) - HB_BASE;
+        if (t0 < HB_WIN && t1 < HB_WIN) {
+          atomicSub(&sh.hist[t0 + ((bits >> 15) ? HB_NEG : 0u)], 1u);
+          atomicAdd(&sh.hist[t1 + ((nbits >> 15) ? HB_NEG : 0u)], 1u);
+        } else {
+          sh.special = 1u;
+        }
+      }
+    }
     if (tid == 0) {
       // tiny values in ascending order: the epilogue sums them in this order
       const int n = (int)min(sh.tiny_n, TINY_MAX);
@@ -755,13 +852,20 @@ void row_stats_kernel(RowStatsArgs a) {
   if (generic) {
     __syncthreads();
     // the ban set moves into the (now free) histogram storage
-    GenericCtx g{nullptr};
-    if (nb > 0) {
-      for (uint32_t k = tid; k < HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
+    GenericCtx g{nullptr, nullptr, theta, sizeof(Elem) == 2};
+    if (nb > 0 || (MIXED && npen > 0)) {
+      for (uint32_t k = tid; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
       __syncthreads();
+    }
+    if (nb > 0) {
       (void)ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
       __syncthreads();
       g.tab = sh.hist;
+    }
+    if (MIXED && npen > 0) {
+      (void)pen_build(sh.hist + HT_SLOTS, g.tab, hist, H, props, npen, V, xprop, &sh.xpen);
+      __syncthreads();
+      g.ptab = sh.hist + HT_SLOTS;
     }
     out.flags &= ~FLAG_EMPTY;
     row_generic<Elem>(rowp, V, s, g, sh, out);
@@ -770,9 +874,11 @@ void row_stats_kernel(RowStatsArgs a) {
   if (tid == 0) {
     if (stats_path) {
       // probability of the row's proposal under the row's distribution
-      const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zx > -INFINITY &&
-                        zx < INFINITY && zx >= out.tau;
-      out.px = kept ? exp((double)zx / (double)s.temperature - out.lse) : 0.0;
+      const float zp = (MIXED && sh.xpen && zx > -INFINITY && zx < INFINITY)
+                           ? pen_apply(zx, theta, sizeof(Elem) == 2) : zx;
+      const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zp > -INFINITY &&
+                        zp < INFINITY && zp >= out.tau;
+      out.px = kept ? exp((double)zp / (double)s.temperature - out.lse) : 0.0;
     } else {
       // greedy: the proposal survives (p = 1) iff it is the argmax
       out.px = (greedy_row && xvalid && (int32_t)out.path == xprop) ? 1.0 : 0.0;
@@ -792,7 +898,8 @@ void row_stats_kernel(RowStatsArgs a) {
 }
 
 int launch_row_stats(const RowStatsArgs& a, int dtype_bf16, int rows, hipStream_t stream) {
-  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d;
+  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d || a.req.pen_t ||
+                     a.req.pen_d || a.req.history;
   const dim3 grid(rows), block(RS_THREADS);
   if (dtype_bf16) {
     if (mixed)

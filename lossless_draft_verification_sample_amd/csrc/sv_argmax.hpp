@@ -37,19 +37,28 @@ struct ArgResult {
   bool nonfinite;
 };
 
-// `tab` is the LDS hash set of the request's banned ids (used only when BANS;
-// a ban-free row runs the loop without any lookup). The scratch arrays hold
-// NT / WAVE entries each. Every thread gets the result.
-template <typename Elem, int NT, int UNROLL, bool BANS>
+// `tab` is the LDS hash set of the request's banned ids (looked up only when
+// BANS and tab is set; a ban-free instantiation runs the loop without any
+// lookup). With PEN, the ids in the hash set `ptab` (when set) compete with
+// their repetition-penalized logit (pen_apply with `theta`); the penalty
+// never raises a logit, so it is applied only when a value beats the lane's
+// best. The scratch arrays hold NT / WAVE entries each. Every thread gets the
+// result.
+template <typename Elem, int NT, int UNROLL, bool BANS, bool PEN = false>
 __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, float* sv,
-                                int32_t* si, uint32_t* su) {
+                                int32_t* si, uint32_t* su, const uint32_t* ptab = nullptr,
+                                float theta = 1.0f) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   constexpr int PER = 16 / sizeof(Elem);
   const int tid = threadIdx.x;
   ArgBest best{-INFINITY, INT32_MAX};
   auto take = [&](float v, int32_t i) {
-    if (v > best.v && !(BANS && ht_has(tab, i))) {
+    if (v > best.v && !(BANS && tab && ht_has(tab, i))) {
+      if (PEN && ptab && ht_has(ptab, i)) {
+        v = pen_apply(v, theta, sizeof(Elem) == 2);
+        if (!(v > best.v)) return;
+      }
       best.v = v;
       best.i = i;
     }
@@ -130,7 +139,7 @@ __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, fl
     for (int i = tid; i < V; i += NT) {
       const float z = am_val<Elem>(rowp, i);
       if (z != z || z == INFINITY) bad = 1u;
-      if (z == -INFINITY && i < first_ninf && !(BANS && ht_has(tab, i))) first_ninf = i;
+      if (z == -INFINITY && i < first_ninf && !(BANS && tab && ht_has(tab, i))) first_ninf = i;
     }
     nonfinite = block_max<NT>(bad, su) != 0u;
     const int32_t fn = block_min<NT>(first_ninf, si);

@@ -57,6 +57,10 @@ struct ReqArgs {
   const SamplerReq* ds;       // [B] draft samplers
   const int32_t* banned_d;    // [B][n_banned_d] bans of the draft rows, or nullptr
   int n_banned_d;
+  const int32_t* history;     // [B][n_history] generated tokens before the round, or nullptr
+  int n_history;
+  const float* pen_t;         // [B] repetition penalty of the target rows, or nullptr (1)
+  const float* pen_d;         // [B] repetition penalty of the draft rows, or nullptr (1)
 };
 
 // One request's resolved settings.
@@ -65,7 +69,21 @@ struct ReqInfo {
   SamplerDev st, sd;
   bool greedy;       // target temperature 0
   bool bad;          // a setting out of range: the request is not verified
+  float pt, pd;      // repetition penalties of the target and draft rows (1: none)
 };
+
+// Repetition penalty of one finite logit (Keskar et al. 2019, "CTRL", section
+// 4.1, in its sign-aware form): z / theta for z > 0, z * theta otherwise,
+// theta >= 1, in IEEE float32; for bf16 rows the result is rounded to bf16
+// (nearest, ties to even), as an op on a bf16 logits tensor would round it.
+__device__ __forceinline__ float pen_apply(float z, float theta, bool to_bf16) {
+  float v = z > 0.0f ? z / theta : z * theta;
+  if (to_bf16) {
+    const uint32_t b = __float_as_uint(v);
+    v = __uint_as_float((b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u);
+  }
+  return v;
+}
 
 __device__ __forceinline__ bool sampler_in_range(const SamplerDev& s, bool allow_greedy) {
   const float T = s.temperature;
@@ -92,8 +110,11 @@ __device__ __forceinline__ ReqInfo request_info(const ReqArgs& q, int b, int gam
     r.sd.top_p = t.top_p;
   }
   r.greedy = r.st.temperature == 0.0f;
-  r.bad = r.g < 0 || r.g > gamma || !sampler_in_range(r.st, true) ||
-          (!r.greedy && !sampler_in_range(r.sd, false));
+  r.pt = q.pen_t ? q.pen_t[b] : 1.0f;
+  r.pd = q.pen_d ? q.pen_d[b] : 1.0f;
+  const bool pt_ok = r.pt >= 1.0f && r.pt < INFINITY, pd_ok = r.pd >= 1.0f && r.pd < INFINITY;
+  r.bad = r.g < 0 || r.g > gamma || !sampler_in_range(r.st, true) || !pt_ok ||
+          (!r.greedy && (!sampler_in_range(r.sd, false) || !pd_ok));
   if (r.bad) r.g = 0;
   return r;
 }

@@ -69,6 +69,7 @@ struct OverlapArgs {
   int spp, parts;             // sub-chunks per workgroup, workgroups per pair
   const int32_t* banned;      // raw ban lists or nullptr
   int n_banned;
+  const int32_t* draft_tokens;  // [B][gamma]
   const RowStat* stats;
   double* partial;            // [B*gamma][parts] when parts > 1
   int32_t* tickets;           // [B*gamma], zero on entry, when parts > 1

@@ -115,6 +115,43 @@ struct alignas(16) KeptTok {
   int32_t pad;
 };
 
+// Marks, in an LDS bitmap of len / 32 words over [c0, c0 + len), the ids a row
+// penalizes: entries 0..H-1 of `hist` and the proposals props[0..np-1] (ids
+// outside [0, V) are padding, duplicates set the same bit).
+__device__ __forceinline__ void mark_pen(uint32_t* bm, int len, const int32_t* hist, int H,
+                                         const int32_t* props, int np, int c0, int V) {
+  for (int k = threadIdx.x; k < len / 32; k += blockDim.x) bm[k] = 0u;
+  __syncthreads();
+  for (int j = threadIdx.x; j < H + np; j += blockDim.x) {
+    const int32_t id = j < H ? hist[j] : props[j - H];
+    if (id >= c0 && id < V && id - c0 < len) {
+      const int o = id - c0;
+      atomicOr(&bm[o >> 5], 1u << (o & 31));
+    }
+  }
+  __syncthreads();
+}
+
+// Replaces the finite logits of the marked tokens of a group (bit e: token e)
+// by their repetition-penalized value.
+template <typename Elem>
+__device__ __forceinline__ void penalize_group(Group<Elem>& g, uint32_t bits, float theta) {
+  if (!bits) return;
+#pragma unroll
+  for (int e = 0; e < GRP; ++e) {
+    if (!((bits >> e) & 1u)) continue;
+    const float z = group_val<Elem>(g, e);
+    if (!(z > -INFINITY && z < INFINITY)) continue;
+    const uint32_t v = __float_as_uint(pen_apply(z, theta, sizeof(Elem) == 2));
+    if constexpr (sizeof(Elem) == 2) {
+      const int sh = 16 * (e & 1);
+      g.w[0][e >> 1] = (g.w[0][e >> 1] & ~(0xFFFFu << sh)) | ((v >> 16) << sh);
+    } else {
+      g.w[e >> 2][e & 3] = v;
+    }
+  }
+}
+
 // A token kept in a leading row, queued in LDS until the other row's logit at
 // the same position is read.
 struct alignas(8) QueuedTok {

@@ -183,6 +183,7 @@ struct DrawShared {
   };
   uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
   uint32_t bmd[DRAW_SPW_MAX * DRAW_SUB / 32];   // draft-only bans (mixed batches)
+  uint32_t bmp[DRAW_SPW_MAX * DRAW_SUB / 32];   // repetition-penalized ids (mixed batches)
   double w[DRAW_SPW_MAX];
   double p[DRAW_SPW_MAX];
   double scr[2 * DR_NW];
@@ -254,10 +255,13 @@ __device__ __forceinline__ void mask_group(Group<Elem>& g, uint32_t bits) {
   }
 }
 
-// MIXED: per-request draft lengths, samplers (greedy requests included) and
-// draft ban lists; the plain variant carries none of that logic.
+// MIXED: per-request draft lengths, samplers (greedy requests included),
+// draft ban lists and repetition penalties; the plain variant carries none of
+// that logic. The bf16 MIXED variant is held to 128 VGPRs (four waves per
+// SIMD, so all workgroups of a launch stay resident; one spill).
 template <typename Elem, bool MIXED>
-__global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
+__global__ __launch_bounds__(DR_THREADS, (MIXED && sizeof(Elem) == 2) ? 4 : 1)
+void draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
   const int b = blockIdx.x / a.nwg, part = blockIdx.x % a.nwg;
@@ -292,6 +296,14 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
   const DrawRow r = draw_row(a, b, wk.n, rq);
   const bool dmask = dnb > 0 && r.drow;
   if (dmask) mark_bans(sh.bmd, nsl * DRAW_SUB, dbl, dnb, dban0, tok0, a.V);
+  // repetition penalty of the draw's rows: the history and the n accepted
+  // proposals that precede position n
+  const int H = (MIXED && a.req.history) ? a.req.n_history : 0;
+  const int32_t* hist = H ? a.req.history + (int64_t)b * a.req.n_history : nullptr;
+  const int32_t* props = a.draft_tokens + (int64_t)b * g;
+  const bool tpen = MIXED && rq.pt != 1.0f && H + wk.n > 0;
+  const bool dpen = MIXED && r.drow && rq.pd != 1.0f && H + wk.n > 0;
+  if (tpen || dpen) mark_pen(sh.bmp, nsl * DRAW_SUB, hist, H, props, wk.n, tok0, a.V);
   if (nb > 0)
     mark_bans(sh.bm, nsl * DRAW_SUB, bl, nb, ban0, tok0, a.V);   // also publishes etab
   else
@@ -413,6 +425,15 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
           if (qx[u] >= 0 && ((sh.bmd[o >> 5] >> (o & 31)) & 1u)) qd[u] = -INFINITY;
         }
       }
+      if (dpen) {
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          const int o = qx[u] - tok0;
+          if (qx[u] >= 0 && ((sh.bmp[o >> 5] >> (o & 31)) & 1u) && qd[u] > -INFINITY &&
+              qd[u] < INFINITY)
+            qd[u] = pen_apply(qd[u], rq.pd, sizeof(Elem) == 2);
+        }
+      }
       double qw[QU], qp[QU];
 #pragma unroll
       for (int u = 0; u < QU; ++u) {
@@ -442,10 +463,15 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
       Group<Elem> tg[GPL], dg[GPL];
 #pragma unroll
       for (int k = 0; k < GPL; ++k) {
+        const int o = sbase + (lane + k * WAVE) * GRP - tok0;
         tg[k] = tn[k];
+        if (tpen && sbase + (lane + k * WAVE) * GRP < a.V)
+          penalize_group<Elem>(tg[k], bm_group(sh.bmp, o), rq.pt);
         if constexpr (MODE == 2) {
           dg[k] = dn[k];
-          if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, sbase + (lane + k * WAVE) * GRP - tok0));
+          if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, o));
+          if (dpen && sbase + (lane + k * WAVE) * GRP < a.V)
+            penalize_group<Elem>(dg[k], bm_group(sh.bmp, o), rq.pd);
         }
       }
       if (sl + DR_NW < nsl) issue(sl + DR_NW);
@@ -468,6 +494,7 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
             const int x0 = sbase + (lane + k * WAVE) * GRP;
             load_group<Elem>(r.drow, x0, a.V, a.vec, dg[k]);
             if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, x0 - tok0));
+            if (dpen) penalize_group<Elem>(dg[k], bm_group(sh.bmp, x0 - tok0), rq.pd);
           }
           double sw = 0.0, sp = 0.0;
 #pragma unroll
@@ -594,6 +621,13 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
       mark_bans(sh.bmd, DRAW_SUB, dbl, dnb, dban0, s0, a.V);
       if (x0 < a.V) mask_group<Elem>(dg, bm_group(sh.bmd, x0 - s0));
     }
+    if (tpen || dpen) {
+      mark_pen(sh.bmp, DRAW_SUB, hist, H, props, n, s0, a.V);
+      if (x0 < a.V) {
+        if (tpen) penalize_group<Elem>(tg, bm_group(sh.bmp, x0 - s0), rq.pt);
+        if (dpen) penalize_group<Elem>(dg, bm_group(sh.bmp, x0 - s0), rq.pd);
+      }
+    }
     if (nb > 0) mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
     double v[GRP];
     const uint32_t km = x0 < a.V ? kept_mask<Elem>(r, tg, nb > 0 ? bm_group(sh.bm, x0 - s0) : 0u) : 0u;
@@ -633,7 +667,8 @@ __global__ __launch_bounds__(DR_THREADS) void draw_kernel(DrawArgs a) {
 
 int launch_draw(const DrawArgs& a, int B, hipStream_t st) {
   const dim3 grid((unsigned)(a.nwg * B)), block(DR_THREADS);
-  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d;
+  const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d || a.req.pen_t ||
+                     a.req.pen_d || a.req.history;
   if (a.bf16) {
     if (mixed)
       hipLaunchKernelGGL((draw_kernel<uint16_t, true>), grid, block, 0, st, a);

@@ -191,3 +191,102 @@ def test_mixed_commit():
     ref = oracle.commit_chain(got["tokens"], got["num_accepted"], kv, slots, gammas)
     for g, r in zip(out, ref):
         assert np.array_equal(g.cpu().numpy().astype(np.int64), r)
+
+
+def _penalty_setup(wl, seed, H=40):
+    """History rich in each request's high-logit tokens, per-request factors
+    (1 = off for some), one request with an invalid factor."""
+    cfg = wl.cfg
+    rng = np.random.default_rng(seed)
+    hist = np.full((cfg.B, H), -1, dtype=np.int32)
+    for b in range(cfg.B):
+        top = np.argsort(-wl.target[b, 0])[:H // 2]
+        hist[b, :H // 2] = top
+        hist[b, H // 2:H - 4] = rng.integers(0, cfg.V, H // 2 - 4)
+    pen_t = rng.choice(np.array([1.0, 1.3, 2.0], np.float32), cfg.B)
+    pen_d = rng.choice(np.array([1.0, 1.2, 1.8], np.float32), cfg.B)
+    pen_t[4] = 0.5                                   # out of range: not verified
+    return hist, pen_t, pen_d
+
+
+def _run_pen(wl, xs, ts, ds, gammas, banned, banned_draft, hist, pen_t, pen_d, diagnostics=False):
+    import torch
+    import lossless_draft_verification_sample_amd as sv
+    dev = pu.torch_dev()
+    req = sv.Requests(gamma=None if gammas is None else _dev(gammas),
+                      target=sv.sampler_array(ts, dev), draft=sv.sampler_array(ds, dev),
+                      banned_draft=None if banned_draft is None else _dev(banned_draft),
+                      history=_dev(hist),
+                      penalty=torch.from_numpy(pen_t).to(dev),
+                      penalty_draft=torch.from_numpy(pen_d).to(dev))
+    return _run(wl, xs, ts, ds, gammas, banned, banned_draft, diagnostics=diagnostics,
+                requests_override=req)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20011), ("f32", 7001)])
+def test_repetition_penalty_matches_oracle(dtype, V):
+    wl = pu.make("c5", B=12, gamma=5, V=V, dtype=dtype, seed=96 + V % 11)
+    ts, ds, gammas, banned, banned_draft, xs = _mixed_setup(wl, seed=V + 1)
+    hist, pen_t, pen_d = _penalty_setup(wl, seed=V + 2)
+    got = _run_pen(wl, xs, ts, ds, gammas, banned, banned_draft, hist, pen_t, pen_d)
+    cfg = wl.cfg
+    u = pu.philox_uniforms(4, 2, cfg.B, cfg.gamma)
+    ref = oracle.verify_batch(wl.target.astype(np.float64), wl.draft.astype(np.float64), xs, u,
+                              [oracle.Sampler(*s) for s in ts], [oracle.Sampler(*s) for s in ds],
+                              banned, banned_draft, gammas, hist, pen_t, pen_d, dtype)
+    _compare(got, ref, f"penalty {dtype}")
+    assert got["flags"][4] & oracle.FLAG_BAD_PARAM
+    # the test has power: without penalties the outputs differ
+    ref0 = oracle.verify_batch(wl.target.astype(np.float64), wl.draft.astype(np.float64), xs, u,
+                               [oracle.Sampler(*s) for s in ts], [oracle.Sampler(*s) for s in ds],
+                               banned, banned_draft, gammas, None, None, None, dtype)
+    fin = np.isfinite(ref.target_lse) & np.isfinite(ref0.target_lse)
+    assert (not np.array_equal(ref.tokens, ref0.tokens)) or np.abs(
+        ref.target_lse[fin] - ref0.target_lse[fin]).max() > 1e-3
+
+
+def test_penalty_outside_the_counted_window():
+    # a penalized logit of -300 becomes -600: beyond the bf16 count window, so
+    # the row takes the generic path
+    wl = pu.make("c5", B=3, gamma=2, V=5003, seed=97)
+    from lossless_draft_verification_sample_amd import synth
+    t = wl.target.copy()
+    t[:, :, 17] = -300.0
+    wl.target = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(t))
+    wl.target_bits = synth.f32_to_bf16_bits(wl.target)
+    ts = [(1.0, 0, 1.0)] * 3
+    ds = [(1.0, 0, 1.0)] * 3
+    xs = pu.oracle_proposals(wl, draft_sampler=(1.0, 0, 1.0))
+    hist = np.array([[17, 3], [17, -1], [-1, -1]], dtype=np.int32)
+    pen = np.array([2.0, 2.0, 2.0], np.float32)
+    got = _run_pen(wl, xs, ts, ds, None, None, None, hist, pen, pen)
+    u = pu.philox_uniforms(4, 2, 3, 2)
+    ref = oracle.verify_batch(wl.target.astype(np.float64), wl.draft.astype(np.float64), xs, u,
+                              [oracle.Sampler(*s) for s in ts], [oracle.Sampler(*s) for s in ds],
+                              None, None, None, hist, pen, pen, "bf16")
+    _compare(got, ref, "penalty window")
+
+
+def test_overlap_with_penalties():
+    wl = pu.make("c5", B=8, gamma=4, V=9001, seed=98)
+    ts, ds, gammas, banned, banned_draft, xs = _mixed_setup(wl, seed=8, bad=False)
+    hist, pen_t, pen_d = _penalty_setup(wl, seed=9)
+    pen_t[4] = 1.5
+    got = _run_pen(wl, xs, ts, ds, gammas, banned, banned_draft, hist, pen_t, pen_d,
+                   diagnostics=True)
+    for b in range(wl.cfg.B):
+        if ts[b][0] == 0.0:
+            assert np.all(np.isnan(got["overlap"][b]))
+            continue
+        tb = [t for t in banned[b].tolist() if t >= 0]
+        db = [t for t in banned_draft[b].tolist() if t >= 0]
+        hb = [t for t in hist[b].tolist() if t >= 0]
+        for i in range(int(gammas[b])):
+            pen_set = hb + xs[b, :i].tolist()
+            pd = oracle.row_distribution(wl.target[b, i].astype(np.float64), oracle.Sampler(*ts[b]), tb,
+                                         pen_set, float(pen_t[b]), "bf16")
+            qd = oracle.row_distribution(wl.draft[b, i].astype(np.float64), oracle.Sampler(*ds[b]), db,
+                                         pen_set, float(pen_d[b]), "bf16")
+            if min(pd.topp_margin, qd.topp_margin) <= pu.EXACT_BAND:
+                continue
+            assert abs(got["overlap"][b, i] - oracle.overlap(pd.p, qd.p)) <= 1e-9, (b, i)
