@@ -27,6 +27,10 @@ fourth request is greedy, draft lengths are gamma, gamma-1, gamma-2 in turn,
 and temperature, top-k and top-p vary per request; `value` then counts the
 rows the requests use (2 g_b + 1 per sampled request, g_b + 1 per greedy one).
 
+With --penalty every request also carries a 64-token history (its first
+target row's 32 largest logits and 32 random ids) and repetition penalties
+1.2 (target) and 1.1 (draft).
+
 With --commit every step is followed by spec_verify_commit (chain KV-commit
 metadata from the step's outputs, with synthetic KV lengths and slots); the
 line then carries a `commit` object with that kernel's time and bytes.
@@ -125,6 +129,8 @@ def main():
                     help="also compute per-position overlaps and the accepted-prefix histogram")
     ap.add_argument("--mixed", action="store_true",
                     help="per-request draft lengths and samplers, a quarter of the requests greedy")
+    ap.add_argument("--penalty", action="store_true",
+                    help="repetition penalties over a 64-token history per request")
     ap.add_argument("--commit", action="store_true",
                     help="follow every step with the chain KV-commit metadata kernel")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -209,6 +215,17 @@ def main():
                                target=sv.sampler_array(per, dev), draft=sv.sampler_array(per, dev))
         greedy = np.array([t[0] == 0.0 for t in per])
         rows = int(np.where(greedy, gam + 1, 2 * gam + 1).sum())
+    if args.penalty:
+        if cfg.mode != "sample":
+            raise SystemExit("--penalty needs a sampling workload")
+        prng = np.random.default_rng(cfg.seed + 7)
+        hist = np.concatenate([np.argsort(-wl.target[:, 0], axis=1)[:, :32],
+                               prng.integers(0, cfg.V, (cfg.B, 32))], axis=1).astype(np.int32)
+        base = requests if requests is not None else sv.Requests()
+        requests = base._replace(
+            history=torch.from_numpy(hist).to(dev),
+            penalty=torch.full((cfg.B,), 1.2, dtype=torch.float32, device=dev),
+            penalty_draft=torch.full((cfg.B,), 1.1, dtype=torch.float32, device=dev))
 
     def step(k):
         c = k % COPIES
@@ -284,6 +301,8 @@ def main():
         "mean_emitted_per_request": float(n_acc.mean() + 1),
         "flags_nonzero": int((flags != 0).sum()),
     }
+    if args.penalty:
+        res["config"]["repetition_penalty"] = "64-token history, 1.2 target, 1.1 draft"
     if args.mixed:
         res["config"]["mixed"] = ("a quarter greedy; draft lengths gamma, gamma-1, gamma-2; "
                                   "T in {0.6, 0.8, 1.0, 1.2}, top-k in {0, 50}, top-p in "

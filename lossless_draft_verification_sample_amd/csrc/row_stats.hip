@@ -598,13 +598,15 @@ __device__ __forceinline__ int32_t pen_id(const int32_t* hist, int H, const int3
 // `ptab` (all slots HT_EMPTY beforehand). Bit k of the result is set when this
 // thread's k-th entry (j = threadIdx.x + k * RS_THREADS) entered the set, so
 // every distinct id has one owner. Sets *xpen when the row's proposal x is one.
+// `first` is entry threadIdx.x, loaded by the caller.
 __device__ __forceinline__ uint32_t pen_build(uint32_t* ptab, const uint32_t* bantab,
                                               const int32_t* hist, int H, const int32_t* props,
-                                              int npen, int V, int32_t x, uint32_t* xpen) {
+                                              int npen, int V, int32_t first, int32_t x,
+                                              uint32_t* xpen) {
   uint32_t own = 0u;
   int k = 0;
   for (int j = threadIdx.x; j < npen; j += RS_THREADS, ++k) {
-    const int32_t id = pen_id(hist, H, props, j);
+    const int32_t id = j == (int)threadIdx.x ? first : pen_id(hist, H, props, j);
     if (id < 0 || id >= V) continue;
     if (bantab && ht_has(bantab, id)) continue;   // banned wins
     if (id == x) *xpen = 1u;
@@ -646,7 +648,8 @@ __device__ __attribute__((noinline)) void greedy_row_stat(const Elem* rowp, int 
     tab = sh.hist;
   }
   if (npen > 0) {
-    (void)pen_build(sh.hist + HT_SLOTS, tab, hist, H, props, npen, V, -1, &sh.xpen);
+    const int32_t p0 = threadIdx.x < (unsigned)npen ? pen_id(hist, H, props, threadIdx.x) : -1;
+    (void)pen_build(sh.hist + HT_SLOTS, tab, hist, H, props, npen, V, p0, -1, &sh.xpen);
     __syncthreads();
     ptab = sh.hist + HT_SLOTS;
   }
@@ -710,6 +713,7 @@ void row_stats_kernel(RowStatsArgs a) {
   const int npen = (MIXED && used && theta != 1.0f) ? H + pi : 0;
   const int32_t* hist = H ? a.req.history + (int64_t)b * a.req.n_history : nullptr;
   const int32_t* props = a.draft_tokens + (int64_t)b * a.gamma;
+  const int32_t pen0 = tid < npen ? pen_id(hist, H, props, tid) : -1;   // loaded early
 
   RowStat out;
   out.m = -INFINITY;
@@ -742,7 +746,7 @@ void row_stats_kernel(RowStatsArgs a) {
     __syncthreads();
 
     const uint16_t* rp = (const uint16_t*)rowp;
-    uint32_t own = 0u, ban_bits = 0u, own_p = 0u;
+    uint32_t own = 0u, ban_bits = 0u, own_p = 0u, pen_bits = 0u;
     if (nb > 0) {
       own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
       // the banned logits are gathered now and subtracted after the stream
@@ -753,7 +757,9 @@ void row_stats_kernel(RowStatsArgs a) {
       // penalized ids: their counts move from z to the penalized value after
       // the stream (the set sits behind the ban set, in the same storage)
       own_p = pen_build(sh.hist + HT_SLOTS, nb > 0 ? sh.hist : nullptr, hist, H, props, npen, V,
-                        xprop, &sh.xpen);
+                        pen0, xprop, &sh.xpen);
+      // the penalized logits are gathered now and moved after the stream
+      if (own_p & 1u) pen_bits = rp[pen0];
       __syncthreads();
     }
     if (nb > 0 || (MIXED && npen > 0)) {
@@ -817,7 +823,7 @@ void row_stats_kernel(RowStatsArgs a) {
       int kp = 0;
       for (int j = tid; j < npen; j += RS_THREADS, ++kp) {
         if (!((own_p >> kp) & 1u)) continue;
-        const uint32_t bits = rp[pen_id(hist, H, props, j)];
+        const uint32_t bits = kp == 0 ? pen_bits : (uint32_t)rp[pen_id(hist, H, props, j)];
         const float z = bf16_to_f32(bits);
         if (!(z > -INFINITY && z < INFINITY)) continue;   // not admissible: nothing to move
         const uint32_t nbits = __float_as_uint(pen_apply(z, theta, true)) >> 16;
@@ -863,7 +869,7 @@ void row_stats_kernel(RowStatsArgs a) {
       g.tab = sh.hist;
     }
     if (MIXED && npen > 0) {
-      (void)pen_build(sh.hist + HT_SLOTS, g.tab, hist, H, props, npen, V, xprop, &sh.xpen);
+      (void)pen_build(sh.hist + HT_SLOTS, g.tab, hist, H, props, npen, V, pen0, xprop, &sh.xpen);
       __syncthreads();
       g.ptab = sh.hist + HT_SLOTS;
     }
