@@ -628,14 +628,14 @@ __device__ __forceinline__ uint32_t pen_build(uint32_t* ptab, const uint32_t* ba
 // request's target bans and NaN excluded) as the row's RowStat: path = the
 // argmax, px = 1 iff the row's proposal is the argmax (the sampling walk's
 // test u * q <= p with q = 1 then accepts exactly on a match). Not inlined:
-// its registers stay out of the statistics path's allocation.
+// its registers stay out of the statistics path's allocation. Returns
+// (path, flags) by value, so that the caller's RowStat stays in registers.
 template <typename Elem>
-__device__ __attribute__((noinline)) void greedy_row_stat(const Elem* rowp, int V,
-                                                          const int32_t* bl, int nb, int32_t first,
-                                                          const int32_t* hist, int H,
-                                                          const int32_t* props, int npen,
-                                                          float theta, RowShared& sh,
-                                                          RowStat& out) {
+__device__ __attribute__((noinline)) uint2 greedy_row_stat(const Elem* rowp, int V,
+                                                           const int32_t* bl, int nb, int32_t first,
+                                                           const int32_t* hist, int H,
+                                                           const int32_t* props, int npen,
+                                                           float theta, RowShared& sh) {
   const uint32_t* tab = nullptr;
   const uint32_t* ptab = nullptr;
   if (nb > 0 || npen > 0) {
@@ -656,8 +656,25 @@ __device__ __attribute__((noinline)) void greedy_row_stat(const Elem* rowp, int 
   // one instantiation with run-time tests of both sets keeps this call small
   const ArgResult r = row_argmax<Elem, RS_THREADS, 4, true, true>(rowp, V, tab, sh.fscr, sh.iscr,
                                                                   sh.uscr, ptab, theta);
-  out.path = (uint32_t)r.arg;
-  out.flags = (r.nonfinite ? FLAG_NONFINITE : 0u) | (r.arg < 0 ? FLAG_EMPTY : 0u);
+  return make_uint2((uint32_t)r.arg,
+                    (r.nonfinite ? FLAG_NONFINITE : 0u) | (r.arg < 0 ? FLAG_EMPTY : 0u));
+}
+
+// Thread 0 of a row: its RowStat, the optional lse outputs, and the counters
+// the later kernels expect at zero.
+__device__ __forceinline__ void row_finish(const RowStatsArgs& a, int row, const RowStat& out) {
+  const int G1 = a.gamma + 1, RPR = 2 * a.gamma + 1;
+  const int b = row / RPR, i = row % RPR;
+  a.stats[row] = out;
+  if (i == 0 && a.tickets) a.tickets[b] = 0;
+  if (i < a.gamma && a.ov_tickets) a.ov_tickets[(int64_t)b * a.gamma + i] = 0;
+  if (row == 0 && a.accept_hist)
+    for (int k = 0; k <= a.gamma; ++k) a.accept_hist[k] = 0u;
+  if (i < G1) {
+    if (a.out_tlse) a.out_tlse[(int64_t)b * G1 + i] = (float)out.lse;
+  } else {
+    if (a.out_dlse) a.out_dlse[(int64_t)b * a.gamma + (i - G1)] = (float)out.lse;
+  }
 }
 
 // MIXED: per-request draft lengths, samplers (greedy requests included) and
@@ -723,15 +740,25 @@ void row_stats_kernel(RowStatsArgs a) {
   out.path = 0u;
   out.px = 0.0;
 
-  bool generic = (sizeof(Elem) == 4) || a.force_generic;
-  const bool stats_path = used && !greedy_row;
-  if (!stats_path) generic = false;
   if constexpr (MIXED) {
-    if (!used) out.flags = rq.bad ? FLAG_BAD_PARAM : 0u;
-    if (greedy_row) greedy_row_stat<Elem>(rowp, V, bl, nb, ban0, hist, H, props, npen, theta, sh, out);
+    if (!used || greedy_row) {
+      // no statistics: an unused row, or the argmax of a greedy request's
+      // target row (its proposal survives, p = 1, iff it is the argmax)
+      out.lse = __builtin_nan("");
+      if (!used) out.flags = rq.bad ? FLAG_BAD_PARAM : 0u;
+      if (greedy_row) {
+        const uint2 gr = greedy_row_stat<Elem>(rowp, V, bl, nb, ban0, hist, H, props, npen, theta, sh);
+        out.path = gr.x;
+        out.flags = gr.y;
+        out.px = (xvalid && (int32_t)gr.x == xprop) ? 1.0 : 0.0;
+      }
+      if (tid == 0) row_finish(a, row, out);
+      return;
+    }
   }
 
-  if (stats_path && !generic) {
+  bool generic = (sizeof(Elem) == 4) || a.force_generic;
+  if (!generic) {
     // the first HT_SLOTS bins hold the ban hash set until the stream starts
     const uint32_t fill = nb > 0 ? HT_EMPTY : 0u;
     const uint32_t pfill = npen > 0 ? HT_EMPTY : 0u;
@@ -765,6 +792,44 @@ void row_stats_kernel(RowStatsArgs a) {
     if (nb > 0 || (MIXED && npen > 0)) {
       for (uint32_t k = tid; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = 0u;
       __syncthreads();
+      // Each distinct banned id leaves the counts once (its owner subtracts
+      // it), and each distinct penalized id moves one count from its logit to
+      // the penalized logit (a bf16 value). This happens before the stream
+      // adds the row's counts: the counts are unsigned and wrap, so a bin
+      // that dips below zero here is exact again once the stream has added
+      // the logit it removed.
+      int kb = 0;
+      for (int j = tid; j < nb; j += RS_THREADS, ++kb) {
+        if (!((own >> kb) & 1u)) continue;
+        const uint32_t bits = kb == 0 ? ban_bits : (uint32_t)rp[bl[j]];
+        const uint32_t ae = bits & 0x7FFFu;
+        const uint32_t t = ae - HB_BASE;
+        if (t < HB_WIN)
+          atomicSub(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
+        else if (ae == 0u)
+          atomicSub(&sh.zero_cnt, 1u);
+        else if (ae < HB_BASE)
+          sh.special = 1u;   // a banned tiny value: the generic path sorts it out
+      }
+      if constexpr (MIXED) {
+        // values outside the counted window on either side of a move send
+        // the row to the generic path
+        int kp = 0;
+        for (int j = tid; j < npen; j += RS_THREADS, ++kp) {
+          if (!((own_p >> kp) & 1u)) continue;
+          const uint32_t bits = kp == 0 ? pen_bits : (uint32_t)rp[pen_id(hist, H, props, j)];
+          const float z = bf16_to_f32(bits);
+          if (!(z > -INFINITY && z < INFINITY)) continue;   // not admissible: nothing to move
+          const uint32_t nbits = __float_as_uint(pen_apply(z, theta, true)) >> 16;
+          const uint32_t t0 = (bits & 0x7FFFu) - HB_BASE, t1 = (nbits & 0x7FFFu) - HB_BASE;
+          if (t0 < HB_WIN && t1 < HB_WIN) {
+            atomicSub(&sh.hist[t0 + ((bits >> 15) ? HB_NEG : 0u)], 1u);
+            atomicAdd(&sh.hist[t1 + ((nbits >> 15) ? HB_NEG : 0u)], 1u);
+          } else {
+            sh.special = 1u;
+          }
+        }
+      }
     }
     const uintptr_t addr = (uintptr_t)rp;
     int head = (int)(((16u - (addr & 15u)) & 15u) >> 1);
@@ -802,40 +867,6 @@ void row_stats_kernel(RowStatsArgs a) {
     }
     __syncthreads();
 
-    // remove each distinct banned id once (its owner subtracts it)
-    int kb = 0;
-    for (int j = tid; j < nb; j += RS_THREADS, ++kb) {
-      if (!((own >> kb) & 1u)) continue;
-      const uint32_t bits = kb == 0 ? ban_bits : (uint32_t)rp[bl[j]];
-      const uint32_t ae = bits & 0x7FFFu;
-      const uint32_t t = ae - HB_BASE;
-      if (t < HB_WIN)
-        atomicSub(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
-      else if (ae == 0u)
-        atomicSub(&sh.zero_cnt, 1u);
-      else if (ae < HB_BASE)
-        sh.special = 1u;   // a banned tiny value: the generic path sorts it out
-    }
-    if constexpr (MIXED) {
-      // each distinct penalized id moves one count from its logit to the
-      // penalized logit (a bf16 value); values outside the counted window on
-      // either side send the row to the generic path
-      int kp = 0;
-      for (int j = tid; j < npen; j += RS_THREADS, ++kp) {
-        if (!((own_p >> kp) & 1u)) continue;
-        const uint32_t bits = kp == 0 ? pen_bits : (uint32_t)rp[pen_id(hist, H, props, j)];
-        const float z = bf16_to_f32(bits);
-        if (!(z > -INFINITY && z < INFINITY)) continue;   // not admissible: nothing to move
-        const uint32_t nbits = __float_as_uint(pen_apply(z, theta, true)) >> 16;
-        const uint32_t t0 = (bits & 0x7FFFu) - HB_BASE, t1 = (nbits & 0x7FFFu) - HB_BASE;
-        if (t0 < HB_WIN && t1 < HB_WIN) {
-          atomicSub(&sh.hist[t0 + ((bits >> 15) ? HB_NEG : 0u)], 1u);
-          atomicAdd(&sh.hist[t1 + ((nbits >> 15) ? HB_NEG : 0u)], 1u);
-        } else {
-          sh.special = 1u;
-        }
-      }
-    }
     if (tid == 0) {
       // tiny values in ascending order: the epilogue sums them in this order
       const int n = (int)min(sh.tiny_n, TINY_MAX);
@@ -878,28 +909,13 @@ void row_stats_kernel(RowStatsArgs a) {
   }
 
   if (tid == 0) {
-    if (stats_path) {
-      // probability of the row's proposal under the row's distribution
-      const float zp = (MIXED && sh.xpen && zx > -INFINITY && zx < INFINITY)
-                           ? pen_apply(zx, theta, sizeof(Elem) == 2) : zx;
-      const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zp > -INFINITY &&
-                        zp < INFINITY && zp >= out.tau;
-      out.px = kept ? exp((double)zp / (double)s.temperature - out.lse) : 0.0;
-    } else {
-      // greedy: the proposal survives (p = 1) iff it is the argmax
-      out.px = (greedy_row && xvalid && (int32_t)out.path == xprop) ? 1.0 : 0.0;
-      out.lse = __builtin_nan("");
-    }
-    a.stats[row] = out;
-    if (i == 0 && a.tickets) a.tickets[b] = 0;
-    if (i < a.gamma && a.ov_tickets) a.ov_tickets[(int64_t)b * a.gamma + i] = 0;
-    if (row == 0 && a.accept_hist)
-      for (int k = 0; k <= a.gamma; ++k) a.accept_hist[k] = 0u;
-    if (is_target) {
-      if (a.out_tlse) a.out_tlse[(int64_t)b * G1 + i] = (float)out.lse;
-    } else {
-      if (a.out_dlse) a.out_dlse[(int64_t)b * a.gamma + (i - G1)] = (float)out.lse;
-    }
+    // probability of the row's proposal under the row's distribution
+    const float zp = (MIXED && sh.xpen && zx > -INFINITY && zx < INFINITY)
+                         ? pen_apply(zx, theta, sizeof(Elem) == 2) : zx;
+    const bool kept = xvalid && !sh.xban && !(out.flags & FLAG_EMPTY) && zp > -INFINITY &&
+                      zp < INFINITY && zp >= out.tau;
+    out.px = kept ? exp((double)zp / (double)s.temperature - out.lse) : 0.0;
+    row_finish(a, row, out);
   }
 }
 
