@@ -260,6 +260,16 @@ def main():
         step(k)
     torch.cuda.synchronize()
     prof = sv.spec_verify_profile_stop()
+    # per-call device time and its spread: events around every step of a
+    # third loop (the records between calls add gaps, not call time)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for k in range(args.steps):
+        evs[k][0].record()
+        step(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    call_us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
     ms_step = elapsed_ms / args.steps
     value = rows * args.steps / (elapsed_ms / 1e3)
     s = 2 if cfg.dtype == "bf16" else 4
@@ -297,6 +307,9 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "avg_kernel_ms": dom_avg_ms, "launches": dom_n, "traffic": traffic},
         "kernel_ms_per_step": {k: v[0] / v[1] for k, v in prof.items() if v[1]},
+        "call_us": {"p10": float(np.percentile(call_us, 10)),
+                    "p50": float(np.median(call_us)),
+                    "p90": float(np.percentile(call_us, 90))},
         "mean_accepted": float(n_acc.mean()),
         "mean_emitted_per_request": float(n_acc.mean() + 1),
         "flags_nonzero": int((flags != 0).sum()),

@@ -759,9 +759,17 @@ void row_stats_kernel(RowStatsArgs a) {
 
   bool generic = (sizeof(Elem) == 4) || a.force_generic;
   if (!generic) {
+    // The logits of the thread's first ban and penalty entries are gathered
+    // first, so that their latency hides behind the fill and the set builds.
+    const uint16_t* rp = (const uint16_t*)rowp;
+    const uint32_t ban_bits = (ban0 >= 0 && ban0 < V) ? (uint32_t)rp[ban0] : 0u;
+    const uint32_t pen_bits = (MIXED && pen0 >= 0 && pen0 < V) ? (uint32_t)rp[pen0] : 0u;
     // the first HT_SLOTS bins hold the ban hash set until the stream starts
     const uint32_t fill = nb > 0 ? HT_EMPTY : 0u;
     const uint32_t pfill = npen > 0 ? HT_EMPTY : 0u;
+    // 16-byte stores: the two set regions end on 16-byte boundaries
+    static_assert(HT_SLOTS % 4 == 0 && 2 * HT_SLOTS <= HB_BINS &&
+                  HB_BINS - 2 * HT_SLOTS <= RS_THREADS, "fill tiling");
     for (uint32_t k = tid; k < HB_BINS; k += RS_THREADS)
       sh.hist[k] = k < HT_SLOTS ? fill : (k < 2 * HT_SLOTS ? pfill : 0u);
     if (tid == 0) {
@@ -772,21 +780,15 @@ void row_stats_kernel(RowStatsArgs a) {
     }
     __syncthreads();
 
-    const uint16_t* rp = (const uint16_t*)rowp;
-    uint32_t own = 0u, ban_bits = 0u, own_p = 0u, pen_bits = 0u;
+    uint32_t own = 0u, own_p = 0u;
     if (nb > 0) {
       own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
-      // the banned logits are gathered now and subtracted after the stream
-      if (own & 1u) ban_bits = rp[ban0];
       __syncthreads();
     }
     if (MIXED && npen > 0) {
-      // penalized ids: their counts move from z to the penalized value after
-      // the stream (the set sits behind the ban set, in the same storage)
+      // penalized ids (the set sits behind the ban set, in the same storage)
       own_p = pen_build(sh.hist + HT_SLOTS, nb > 0 ? sh.hist : nullptr, hist, H, props, npen, V,
                         pen0, xprop, &sh.xpen);
-      // the penalized logits are gathered now and moved after the stream
-      if (own_p & 1u) pen_bits = rp[pen0];
       __syncthreads();
     }
     if (nb > 0 || (MIXED && npen > 0)) {
