@@ -84,6 +84,48 @@ def traffic_record(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
+def read_ceiling(dev, nbytes, chunk_bytes, iters=50):
+    """Plain read bandwidth of this GPU on `nbytes` of device memory (two
+    buffers alternate, so the last-level cache serves no repeat): a
+    grid-stride sweep, and one `chunk_bytes` chunk per workgroup, the access
+    shape of the row kernels. GB/s from events around `iters` launches."""
+    import ctypes
+    import torch
+    from lossless_draft_verification_sample_amd import build as b
+    lib = ctypes.CDLL(os.path.join(b.PKG_DIR, b.CALIB_LIB_NAME))
+    lib.sv_calib_read_blocks.restype = ctypes.c_int64
+    lib.sv_calib_read_blocks.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    lib.sv_calib_read.restype = ctypes.c_int
+    lib.sv_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.randint(0, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"bytes": nbytes, "chunk_bytes": chunk_bytes}
+    for name, mode, grid in (("grid_stride", 0, 256 * 8), ("chunk_per_workgroup", 1, 0)):
+        nblk = lib.sv_calib_read_blocks(nbytes, mode, chunk_bytes, grid)
+        sink = torch.empty(nblk, dtype=torch.int32, device=dev)
+
+        def call(k):
+            rc = lib.sv_calib_read(bufs[k % 2].data_ptr(), nbytes, mode, chunk_bytes, grid,
+                                   sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"sv_calib_read failed ({rc})")
+        for k in range(20):
+            call(k)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for k in range(iters):
+            call(k)
+        e.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(e) / iters * 1e3
+        out[name] = {"us": us, "gbps": nbytes / (us / 1e6) / 1e9, "workgroups": nblk}
+    log(f"[bench] read ceiling {out}")
+    return out
+
+
 def cpu_baseline(wl, xs, budget_s):
     """The float64 oracle, as it stands, on the first requests of the workload."""
     import oracle
@@ -133,6 +175,10 @@ def main():
                     help="repetition penalties over a 64-token history per request")
     ap.add_argument("--commit", action="store_true",
                     help="follow every step with the chain KV-commit metadata kernel")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="also time the read-only calibration kernels (libsvcalib.so): "
+                         "a grid-stride sweep and one row-sized chunk per workgroup over "
+                         "the step's logit bytes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -350,6 +396,8 @@ def main():
                          "bytes_per_launch": cm_bytes,
                          "achieved_gbps": cm_bytes / (cm_avg / 1e3) / 1e9,
                          "bound": "launch latency (one wave per request)"}
+    if args.read_ceiling:
+        res["read_ceiling"] = read_ceiling(dev, algo_bytes, cfg.V * s)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2**20 // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)

@@ -1,4 +1,5 @@
-"""Build libspecverify.so (the HIP library behind include/spec_verify.h) for gfx950.
+"""Build libspecverify.so (the HIP library behind include/spec_verify.h) and
+libsvcalib.so (an HBM read-bandwidth calibration kernel) for gfx950.
 
     python -m lossless_draft_verification_sample_amd.build
 
@@ -14,6 +15,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libspecverify.so"
 SOURCES = ["row_stats.hip", "verify.hip", "overlap.hip", "greedy.hip", "commit.hip", "api.cpp"]
+# HBM read-bandwidth calibration (bench.py --read-ceiling); not on the path
+CALIB_LIB_NAME = "libsvcalib.so"
+CALIB_SOURCES = ["calib/read_ceiling.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -40,9 +44,15 @@ def hipcc():
 
 
 def build(verbose=False, out_dir=PKG_DIR):
-    out = os.path.join(out_dir, LIB_NAME)
+    out = _compile(LIB_NAME, SOURCES, verbose, out_dir)
+    _compile(CALIB_LIB_NAME, CALIB_SOURCES, verbose, out_dir)
+    return out
+
+
+def _compile(lib_name, sources, verbose, out_dir):
+    out = os.path.join(out_dir, lib_name)
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in sources]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
