@@ -418,15 +418,13 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
     for (uint32_t k = 0; k < tn; ++k)   // sorted beforehand: a fixed order
       zmass += exp_neg(((double)bf16_to_f32(sh.tiny[k]) - mw) * invT);
   }
-  double ml = zmass;
-  {
-    double e = e0;
+  // the thread's mass: sum over j >= jtop of c[j] * e0 * ratio^(j - jtop), in
+  // Horner form from the smallest value up (one fp64 accumulator)
+  double hm = 0.0;
 #pragma unroll
-    for (int j = 0; j < HB_TPR; ++j) {
-      if (j > jtop) e *= ratio;
-      if (c[j]) ml += (double)c[j] * e;
-    }
-  }
+  for (int j = HB_TPR - 1; j >= 0; --j)
+    if (j >= jtop) hm = hm * ratio + (double)c[j];
+  const double ml = zmass + e0 * hm;
   const double mass_incl = wave_scan_dpp(ml, 0.0, [](double x, double y) { return x + y; });
 
   // exchange 1: per-wave count, top rank and mass
