@@ -19,7 +19,7 @@ constexpr size_t WS_ALIGN = 256;
 size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
-  size_t stats, sums, tickets, ov_partial, ov_tickets, total;
+  size_t stats, unif, sums, tickets, ov_partial, ov_tickets, total;
   int nsub, spw, nwg;
   int ov_spp, ov_parts;
 };
@@ -56,6 +56,8 @@ bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
   size_t off = 0;
   L->stats = off;
   off = align_up(off + (size_t)rows * sizeof(sv::RowStat));
+  L->unif = off;
+  off = align_up(off + (size_t)B * (size_t)(gamma + 1) * sizeof(double));
   L->sums = off;
   off = align_up(off + (size_t)B * (size_t)nsub * sizeof(sv::ChunkSums));
   L->tickets = off;
@@ -177,6 +179,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   sv::RowStat* stats = (sv::RowStat*)(ws + L.stats);
+  double* unif = (double*)(ws + L.unif);
   sv::ChunkSums* sums = (sv::ChunkSums*)(ws + L.sums);
   int32_t* tickets = (int32_t*)(ws + L.tickets);
   double* ov_partial = (double*)(ws + L.ov_partial);
@@ -204,6 +207,9 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.out_tlse = out_target_lse;
     a.out_dlse = out_draft_lse;
     a.force_generic = 0;
+    a.ustore = uniforms ? nullptr : unif;
+    a.seed = seed;
+    a.offset = offset;
     ProfScope p(SV_K_ROW_STATS, st);
     if (sv::launch_row_stats(a, bf16, rows, st)) return SV_EHIP;
   }
@@ -226,9 +232,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     a.banned = bans;
     a.n_banned = n_banned;
     a.stats = stats;
-    a.uniforms = uniforms;
-    a.seed = seed;
-    a.offset = offset;
+    a.uniforms = uniforms ? uniforms : unif;
     a.sums = sums;
     a.tickets = tickets;
     a.out_tokens = out_tokens;

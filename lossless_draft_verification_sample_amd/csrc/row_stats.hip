@@ -40,7 +40,9 @@
 //
 // Each row also evaluates the probability of its proposal token (target row
 // i < gamma: p_i(x_i); draft row i: q_i(x_i)), which is all the acceptance walk
-// needs from the row.
+// needs from the row, and target row i draws the request's uniform of slot i
+// (Philox, unless the caller passed the uniforms), so that the walk only loads
+// them.
 
 #include "sv_argmax.hpp"
 #include "sv_bans.hpp"
@@ -729,6 +731,14 @@ void row_stats_kernel(RowStatsArgs a) {
   const int32_t* hist = H ? a.req.history + (int64_t)b * a.req.n_history : nullptr;
   const int32_t* props = a.draft_tokens + (int64_t)b * a.gamma;
   const int32_t pen0 = tid < npen ? pen_id(hist, H, props, tid) : -1;   // loaded early
+  // Target row i also draws uniform slot i of its request for the acceptance
+  // walk (slot gamma: the final draw). Lane 0 of the last wave computes it,
+  // in the bf16 stream while its first loads are in flight.
+  bool u_pending = a.ustore && is_target && tid == RS_THREADS - WAVE;
+  auto emit_u = [&]() {
+    a.ustore[(int64_t)b * G1 + i] = philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)i);
+    u_pending = false;
+  };
 
   RowStat out;
   out.m = -INFINITY;
@@ -750,6 +760,7 @@ void row_stats_kernel(RowStatsArgs a) {
         out.flags = gr.y;
         out.px = (xvalid && (int32_t)gr.x == xprop) ? 1.0 : 0.0;
       }
+      if (u_pending) emit_u();
       if (tid == 0) row_finish(a, row, out);
       return;
     }
@@ -847,6 +858,7 @@ void row_stats_kernel(RowStatsArgs a) {
         const int k = k0 + u * RS_THREADS;
         if (k < nchunk) v[u] = __builtin_nontemporal_load(body + k);
       }
+      if (u_pending) emit_u();
 #pragma unroll
       for (int u = 0; u < RS_UNROLL; ++u) {
         const int k = k0 + u * RS_THREADS;
@@ -908,6 +920,7 @@ void row_stats_kernel(RowStatsArgs a) {
     row_generic<Elem>(rowp, V, s, g, sh, out);
   }
 
+  if (u_pending) emit_u();
   if (tid == 0) {
     // probability of the row's proposal under the row's distribution
     const float zp = (MIXED && sh.xpen && zx > -INFINITY && zx < INFINITY)

@@ -36,6 +36,10 @@ struct RowStatsArgs {
   float* out_tlse;
   float* out_dlse;
   int force_generic;
+  // Philox uniforms of the acceptance walk and the final draw, [B][gamma+1]:
+  // target row i writes slot i. nullptr when the caller supplies the uniforms.
+  double* ustore;
+  uint64_t seed, offset;
 };
 
 struct DrawArgs {
@@ -49,8 +53,7 @@ struct DrawArgs {
   const int32_t* banned;      // raw ban lists or nullptr
   int n_banned;
   const RowStat* stats;
-  const double* uniforms;     // [B][gamma+1] or nullptr (Philox)
-  uint64_t seed, offset;
+  const double* uniforms;     // [B][gamma+1]: the caller's, or those of the row pass
   ChunkSums* sums;            // [B][nsub]
   int32_t* tickets;           // [B], zero on entry
   int32_t* out_tokens;

@@ -137,9 +137,7 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b, int gq) {
   uint32_t rf = 0u;
   double p = 0.0, q = 0.0, u = 0.0;
   int32_t x = -1;
-  if (lane <= g)
-    u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
-                   : philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)lane);
+  if (lane <= g) u = a.uniforms[(int64_t)b * G1 + lane];
   if (lane <= gq) {
     const RowStat t = st[lane];
     rf |= t.flags;
