@@ -15,7 +15,9 @@ Prints one JSON line. `value` is verified logit rows per second
 (row_stats, or greedy_argmax) on algorithmic bytes (every logit read once)
 divided by its average duration, measured with HIP events recorded by the
 library around each of its launches on the launch stream. `cpu_baseline` times
-the float64 oracle on a bounded sample of the same workload on one host core.
+the float64 oracle on a bounded sample of the same workload on one host core;
+`cpu_baseline_pool` runs it over the whole batch split across up to 16 host
+processes.
 
 With --diagnostics every step also asks for the per-position overlaps and the
 accepted-prefix histogram; the line then carries a `diagnostics` object that
@@ -156,6 +158,76 @@ def cpu_baseline(wl, xs, budget_s):
     return {"value": rows / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {cfg.B} requests ({rows} rows), float64 NumPy on one "
                       f"host core, {t_total:.1f} s; bf16->f64 upcast not timed"}
+
+
+def _oracle_worker(conn):
+    """One host process of the pooled oracle run (module level, so that spawned
+    processes can import it): receives its requests, upcasts them, reports
+    ready, and on "go" runs the oracle and sends back its own seconds."""
+    import oracle
+    mode, tgt, dft, xs, u, banned, samp = conn.recv()
+    tgt = tgt.astype(np.float64)
+    dft = None if dft is None else dft.astype(np.float64)
+    conn.send("ready")
+    conn.recv()
+    t0 = time.perf_counter()
+    if mode == "sample":
+        s = oracle.Sampler(*samp)
+        oracle.verify_sample(tgt, dft, xs, u, s, s, banned)
+    else:
+        oracle.verify_greedy(tgt, xs)
+    conn.send(time.perf_counter() - t0)
+
+
+def cpu_baseline_pool(wl, xs, max_workers=16, timeout_s=300.0):
+    """The same float64 oracle over the whole batch, its requests split across up
+    to 16 host processes. Each process gets and upcasts its share before the
+    clock starts (as the one-core figure leaves out the upcast); the wall clock
+    runs from the common start signal until the last process is done."""
+    import multiprocessing as mp
+    import oracle
+    cfg = wl.cfg
+    n = max(1, min(max_workers, os.cpu_count() or 1, cfg.B))
+    rows_per_req = (2 * cfg.gamma + 1) if cfg.mode == "sample" else (cfg.gamma + 1)
+    u_all = (np.array(oracle.uniforms(cfg.philox_seed, cfg.philox_offset, cfg.B, cfg.gamma))
+             if cfg.mode == "sample" else None)
+    bounds = np.linspace(0, cfg.B, n + 1).astype(int)
+    ctx = mp.get_context("spawn")
+    procs, conns = [], []
+    try:
+        for k in range(n):
+            sl = slice(bounds[k], bounds[k + 1])
+            mine, theirs = ctx.Pipe()
+            p = ctx.Process(target=_oracle_worker, args=(theirs,), daemon=True)
+            p.start()
+            mine.send((cfg.mode, wl.target[sl], wl.draft[sl] if cfg.mode == "sample" else None,
+                       xs[sl], None if u_all is None else u_all[sl],
+                       None if wl.banned is None else wl.banned[sl],
+                       (cfg.temperature, cfg.top_k, cfg.top_p)))
+            procs.append(p)
+            conns.append(mine)
+
+        def recv(c):
+            if not c.poll(timeout_s):
+                raise RuntimeError("oracle worker timed out")
+            return c.recv()
+        for c in conns:
+            assert recv(c) == "ready"
+        t0 = time.perf_counter()
+        for c in conns:
+            c.send("go")
+        inner = [recv(c) for c in conns]
+        wall = time.perf_counter() - t0
+    finally:
+        for p in procs:
+            p.join(timeout=10)
+            if p.is_alive():
+                p.terminate()
+    rows = cfg.B * rows_per_req
+    return {"value": rows / wall, "unit": "rows/s", "cores": n, "kind": "oracle",
+            "sample": f"all {cfg.B} requests ({rows} rows) split over {n} host processes, "
+                      f"float64 NumPy, {wall:.2f} s wall clock from a common start (longest "
+                      f"process {max(inner):.2f} s); bf16->f64 upcast not timed"}
 
 
 def main():
@@ -409,6 +481,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(wl, xs, args.cpu_budget)
+        log("[bench] timing the oracle on a pool of host processes")
+        res["cpu_baseline_pool"] = cpu_baseline_pool(wl, xs)
     print(json.dumps(res), flush=True)
 
 
