@@ -55,9 +55,10 @@ namespace sv {
 #define SV_RS_THREADS 512
 #endif
 #ifndef SV_RS_UNROLL
-#define SV_RS_UNROLL 8
+#define SV_RS_UNROLL 4
 #endif
-// One workgroup per row; each thread keeps eight 16-byte loads in flight.
+// One workgroup per row; each thread keeps four to eight 16-byte loads in
+// flight (two buffers of RS_UNROLL chunks: one loading, one being counted).
 constexpr int RS_THREADS = SV_RS_THREADS;
 constexpr int RS_UNROLL = SV_RS_UNROLL;
 
@@ -851,14 +852,18 @@ void row_stats_kernel(RowStatsArgs a) {
     if (tid < V - tail0) hb_count_one(rp[tail0 + tid], sh);
     const u32x4* body = (const u32x4*)(rp + head);
 
-    for (int k0 = tid; k0 < nchunk; k0 += RS_THREADS * RS_UNROLL) {
-      u32x4 v[RS_UNROLL];
+    // Software-pipelined stream: the loads of the next RS_UNROLL chunks are in
+    // flight while the current ones are counted.
+    constexpr int STEP = RS_THREADS * RS_UNROLL;
+    u32x4 va[RS_UNROLL], vb[RS_UNROLL];
+    auto ld = [&](u32x4 (&v)[RS_UNROLL], int k0) {
 #pragma unroll
       for (int u = 0; u < RS_UNROLL; ++u) {
         const int k = k0 + u * RS_THREADS;
         if (k < nchunk) v[u] = __builtin_nontemporal_load(body + k);
       }
-      if (u_pending) emit_u();
+    };
+    auto proc = [&](const u32x4 (&v)[RS_UNROLL], int k0) {
 #pragma unroll
       for (int u = 0; u < RS_UNROLL; ++u) {
         const int k = k0 + u * RS_THREADS;
@@ -876,6 +881,18 @@ void row_stats_kernel(RowStatsArgs a) {
           }
         }
       }
+    };
+    int k0 = tid;
+    if (k0 < nchunk) ld(va, k0);
+    if (u_pending) emit_u();
+    while (k0 < nchunk) {
+      if (k0 + STEP < nchunk) ld(vb, k0 + STEP);
+      proc(va, k0);
+      k0 += STEP;
+      if (k0 >= nchunk) break;
+      if (k0 + STEP < nchunk) ld(va, k0 + STEP);
+      proc(vb, k0);
+      k0 += STEP;
     }
     __syncthreads();
 
