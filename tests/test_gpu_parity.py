@@ -325,12 +325,18 @@ def test_deterministic_bitwise():
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_device_philox_equals_oracle_philox():
-    # bonus draws from a uniform p over 1024 tokens reveal ten bits of each u
-    B, gamma, V = 512, 2, 1024
-    wl = _edge_workload(V, gamma, B, "f32", seed=1)
+@pytest.mark.parametrize("dtype,V", [("f32", 1024), ("bf16", 4096)])
+def test_device_philox_equals_oracle_philox(dtype, V):
+    # bonus draws from a uniform p over V tokens reveal log2(V) bits of each u;
+    # bf16 rows take the count-histogram path, whose target rows draw their
+    # uniform inside the stream (V = 4096 gives every thread a chunk)
+    B, gamma = 512, 2
+    wl = _edge_workload(V, gamma, B, dtype, seed=1)
     wl.target[:] = 0.0
     wl.draft[:] = 0.0
+    if dtype == "bf16":
+        wl.target_bits[:] = 0
+        wl.draft_bits[:] = 0
     xs = np.zeros((B, gamma), np.int32)
     for seed, offset in [(0, 0), (12345, 7), (2**63 + 5, 2**40 + 3)]:
         got = pu.run_gpu_sample(wl, xs, tsamp=(1.0, 0, 1.0), dsamp=(1.0, 0, 1.0), seed=seed,
