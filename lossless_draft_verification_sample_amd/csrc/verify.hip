@@ -43,18 +43,20 @@ struct DrawRow {
 
 // The rows of the final draw of request b after n acceptances: the target row
 // n, and the draft row n at a rejection (n < the request's draft length g).
-__device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n, const ReqInfo& rq) {
-  const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
+// Their statistics come from the acceptance walk, which has loaded them.
+__device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n, const ReqInfo& rq,
+                                            const RowStat& ts, const RowStat& ds) {
+  const int g = a.gamma, G1 = g + 1;
   DrawRow r;
   const int64_t V = a.V;
   const size_t es = a.bf16 ? 2 : 4;
   r.trow = (const char*)a.target + ((int64_t)b * G1 + n) * V * es;
-  r.ts = a.stats[(int64_t)b * RPR + n];
+  r.ts = ts;
   r.tinv = 1.0 / (double)rq.st.temperature;
   r.tcut = (r.ts.flags & FLAG_EMPTY) ? INFINITY : r.ts.tau;
   if (n < rq.g) {
     r.drow = (const char*)a.draft + ((int64_t)b * g + n) * V * es;
-    r.ds = a.stats[(int64_t)b * RPR + G1 + n];
+    r.ds = ds;
     r.dinv = 1.0 / (double)rq.sd.temperature;
   } else {
     r.drow = nullptr;
@@ -126,7 +128,26 @@ struct Walk {
   uint32_t flags;
   double u_final;  // uniform of the final draw
   int32_t x;       // proposal of this lane (lanes < gamma)
+  RowStat ts, ds;  // statistics of target row n and draft row n (the draw's rows)
 };
+
+// Lane `src`'s RowStat (src wave-uniform), in scalar registers.
+__device__ __forceinline__ double readlane_f64(double v, int src) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ RowStat rowstat_from_lane(const RowStat& v, int src) {
+  RowStat r;
+  r.m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.m), src));
+  r.tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.tau), src));
+  r.lse = readlane_f64(v.lse, src);
+  r.flags = (uint32_t)__builtin_amdgcn_readlane((int)v.flags, src);
+  r.path = (uint32_t)__builtin_amdgcn_readlane((int)v.path, src);
+  r.px = readlane_f64(v.px, src);
+  return r;
+}
 
 // gq: the request's draft length (proposals 0..gq-1 and target rows 0..gq are
 // its own); the final-draw uniform is slot gamma whatever gq is.
@@ -137,14 +158,15 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b, int gq) {
   uint32_t rf = 0u;
   double p = 0.0, q = 0.0, u = 0.0;
   int32_t x = -1;
+  RowStat t{}, d{};
   if (lane <= g) u = a.uniforms[(int64_t)b * G1 + lane];
   if (lane <= gq) {
-    const RowStat t = st[lane];
+    t = st[lane];
     rf |= t.flags;
     p = t.px;
   }
   if (lane < gq) {
-    const RowStat d = st[G1 + lane];
+    d = st[G1 + lane];
     rf |= d.flags;
     q = d.px;
     x = a.draft_tokens[(int64_t)b * g + lane];
@@ -163,11 +185,10 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b, int gq) {
   w.flags = rf;
   if (rangem) w.flags |= FLAG_TOKEN_RANGE;
   if (w.n < gq && ((qzm >> w.n) & 1ull)) w.flags |= FLAG_Q_ZERO;
-  const uint64_t ub = (uint64_t)__double_as_longlong(u);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ub, g);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ub >> 32), g);
-  w.u_final = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  w.u_final = readlane_f64(u, g);
   w.x = x;
+  w.ts = rowstat_from_lane(t, w.n);
+  w.ds = rowstat_from_lane(d, w.n);
   return w;
 }
 
@@ -291,7 +312,7 @@ void draw_kernel(DrawArgs a) {
 
   exp_table_fill(sh.etab);
   const Walk wk = accept_walk(a, b, rq.g);
-  const DrawRow r = draw_row(a, b, wk.n, rq);
+  const DrawRow r = draw_row(a, b, wk.n, rq, wk.ts, wk.ds);
   const bool dmask = dnb > 0 && r.drow;
   if (dmask) mark_bans(sh.bmd, nsl * DRAW_SUB, dbl, dnb, dban0, tok0, a.V);
   // repetition penalty of the draw's rows: the history and the n accepted
