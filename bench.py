@@ -17,7 +17,8 @@ divided by its average duration, measured with HIP events recorded by the
 library around each of its launches on the launch stream. `cpu_baseline` times
 the float64 oracle on a bounded sample of the same workload on one host core;
 `cpu_baseline_pool` runs it over the whole batch split across up to 16 host
-processes.
+processes. `parity` compares the last timed call's tokens, accepted counts
+and flags with the one-core oracle run's, request by request.
 
 With --diagnostics every step also asks for the per-position overlaps and the
 accepted-prefix histogram; the line then carries a `diagnostics` object that
@@ -128,8 +129,10 @@ def read_ceiling(dev, nbytes, chunk_bytes, iters=50):
     return out
 
 
-def cpu_baseline(wl, xs, budget_s):
-    """The float64 oracle, as it stands, on the first requests of the workload."""
+def cpu_baseline(wl, xs, budget_s, results=None):
+    """The float64 oracle, as it stands, on the first requests of the workload.
+    When `results` is a list, the oracle's outputs of each timed slice are
+    appended to it (untimed)."""
     import oracle
     cfg = wl.cfg
     n = 1
@@ -146,18 +149,45 @@ def cpu_baseline(wl, xs, budget_s):
             u = u_all[sl]
             s = oracle.Sampler(cfg.temperature, cfg.top_k, cfg.top_p)
             t0 = time.perf_counter()
-            oracle.verify_sample(tgt, dft, xs[sl], u, s, s,
-                                 None if wl.banned is None else wl.banned[sl])
+            ref = oracle.verify_sample(tgt, dft, xs[sl], u, s, s,
+                                       None if wl.banned is None else wl.banned[sl])
         else:
             t0 = time.perf_counter()
-            oracle.verify_greedy(tgt, xs[sl])
+            ref = oracle.verify_greedy(tgt, xs[sl])
         t_total += time.perf_counter() - t0
+        if results is not None:
+            results.append(ref)
         done += take
         n = min(2 * n, 8)
     rows = done * rows_per_req
     return {"value": rows / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {cfg.B} requests ({rows} rows), float64 NumPy on one "
                       f"host core, {t_total:.1f} s; bf16->f64 upcast not timed"}
+
+
+def parity_summary(cfg, out, refs, band=1e-10):
+    """The last timed call's outputs against the oracle's on the requests the
+    one-core oracle run covered: tokens, accepted counts and flags must be
+    identical except for requests with a decision within `band` of its edge
+    (sampling only; greedy compares every request)."""
+    n = sum(len(r.num_accepted) for r in refs)
+    tok = out.tokens.cpu().numpy()[:n]
+    nacc = out.num_accepted.cpu().numpy()[:n]
+    flg = out.flags.cpu().numpy().astype(np.uint32)[:n]
+    rtok = np.concatenate([r.tokens for r in refs])
+    rnacc = np.concatenate([r.num_accepted for r in refs])
+    rflg = np.concatenate([r.flags for r in refs]).astype(np.uint32)
+    same = (tok == rtok).all(axis=1) & (nacc == rnacc) & (flg == rflg)
+    if cfg.mode == "sample":
+        margin = np.concatenate([r.margin for r in refs])
+        keep = margin > band
+        within_1e6 = int(np.concatenate([r.boundary for r in refs]).sum())
+    else:
+        keep = np.ones(n, bool)
+        within_1e6 = 0
+    return {"requests": int(n), "compared": int(keep.sum()),
+            "mismatched": int((~same & keep).sum()), "excluded_band": band,
+            "excluded": int((~keep).sum()), "decisions_within_1e-6": within_1e6}
 
 
 def _oracle_worker(conn):
@@ -480,7 +510,10 @@ def main():
         res["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(wl, xs, args.cpu_budget)
+        refs = []
+        res["cpu_baseline"] = cpu_baseline(wl, xs, args.cpu_budget, refs)
+        if not (args.mixed or args.penalty):
+            res["parity"] = parity_summary(cfg, out, refs)
         log("[bench] timing the oracle on a pool of host processes")
         res["cpu_baseline_pool"] = cpu_baseline_pool(wl, xs)
     print(json.dumps(res), flush=True)
