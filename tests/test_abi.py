@@ -54,6 +54,11 @@ def test_workspace_bytes(lib):
     assert a > 0 and a % 256 == 0
     assert ws(128, 8, 151936, 0) == a    # ban lists are read in place
     assert ws(1, 4, 1000, 0) > 0
+    # room for the row statistics (32 B per row), the uniforms (8 B per slot),
+    # the draw's sub-chunk sums (16 B per 2048 tokens per request) and the
+    # per-request arrival counters
+    B, g, V = 128, 8, 151936
+    assert a >= B * (2 * g + 1) * 32 + B * (g + 1) * 8 + B * -(-V // 2048) * 16 + B * 4
     for bad in [(0, 4, 10, 0), (1, 0, 10, 0), (1, 64, 10, 0), (1, 4, 0, 0), (1, 4, 10, -1),
                 (1, 4, 10, 2049), (2**30, 63, 10, 0)]:
         assert ws(*bad) == 0, bad
