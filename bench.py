@@ -34,6 +34,10 @@ With --penalty every request also carries a 64-token history (its first
 target row's 32 largest logits and 32 random ids) and repetition penalties
 1.2 (target) and 1.1 (draft).
 
+With --graph the line also carries `graph`: the step time when the calls are
+replayed from a captured HIP graph (launch overhead removed), next to the
+eager `value`.
+
 With --commit every step is followed by spec_verify_commit (chain KV-commit
 metadata from the step's outputs, with synthetic KV lengths and slots); the
 line then carries a `commit` object with that kernel's time and bytes.
@@ -281,6 +285,8 @@ def main():
                     help="also time the read-only calibration kernels (libsvcalib.so): "
                          "a grid-stride sweep and one row-sized chunk per workgroup over "
                          "the step's logit bytes")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -431,6 +437,35 @@ def main():
     achieved = dom_bytes / (dom_avg_ms / 1e3) / 1e9
     traffic = traffic_record(dom, cfg.name)
 
+    graph = None
+    if args.graph:
+        # one graph holds COPIES steps (one per input copy); replays are timed
+        # with events on the current stream
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(COPIES):
+                step(k)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(COPIES):
+                step(k)
+        reps = max(1, args.steps // COPIES)
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        g_ms = start.elapsed_time(stop) / (reps * COPIES)
+        graph = {"ms_per_step": g_ms, "value": rows / (g_ms / 1e3), "unit": "rows/s",
+                 "steps": reps * COPIES}
+        log(f"[bench] graph replays: {g_ms * 1e3:.1f} us per step")
+
     n_acc = out.num_accepted.cpu().numpy()
     flags = out.flags.cpu().numpy()
     res = {
@@ -462,6 +497,8 @@ def main():
         "mean_emitted_per_request": float(n_acc.mean() + 1),
         "flags_nonzero": int((flags != 0).sum()),
     }
+    if graph is not None:
+        res["graph"] = graph
     if args.penalty:
         res["config"]["repetition_penalty"] = "64-token history, 1.2 target, 1.1 draft"
     if args.mixed:
