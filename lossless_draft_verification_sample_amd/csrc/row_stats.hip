@@ -655,7 +655,7 @@ __device__ __attribute__((noinline)) uint2 greedy_row_stat(const Elem* rowp, int
     ptab = sh.hist + HT_SLOTS;
   }
   // one instantiation with run-time tests of both sets keeps this call small
-  const ArgResult r = row_argmax<Elem, RS_THREADS, 4, true, true>(rowp, V, tab, sh.fscr, sh.iscr,
+  const ArgResult r = row_argmax<Elem, RS_THREADS, 2, true, true>(rowp, V, tab, sh.fscr, sh.iscr,
                                                                   sh.uscr, ptab, theta);
   return make_uint2((uint32_t)r.arg,
                     (r.nonfinite ? FLAG_NONFINITE : 0u) | (r.arg < 0 ? FLAG_EMPTY : 0u));

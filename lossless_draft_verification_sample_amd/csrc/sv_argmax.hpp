@@ -71,13 +71,18 @@ __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, fl
   const int tail0 = head + nchunk * PER;
   if (tid < head) take(am_val<Elem>(rowp, tid), tid);
   const u32x4* body = (const u32x4*)(rowp + head);
-  for (int k0 = tid; k0 < nchunk; k0 += NT * UNROLL) {
-    u32x4 v[UNROLL];
+  // Software-pipelined stream: while one buffer of UNROLL chunks is scanned,
+  // the loads of the other are in flight.
+  constexpr int STEP = NT * UNROLL;
+  u32x4 va[UNROLL], vb[UNROLL];
+  auto ld = [&](u32x4 (&v)[UNROLL], int k0) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int k = k0 + u * NT;
       if (k < nchunk) v[u] = __builtin_nontemporal_load(body + k);
     }
+  };
+  auto scan = [&](const u32x4 (&v)[UNROLL], int k0) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int k = k0 + u * NT;
@@ -103,6 +108,17 @@ __device__ ArgResult row_argmax(const Elem* rowp, int V, const uint32_t* tab, fl
         }
       }
     }
+  };
+  int k0 = tid;
+  if (k0 < nchunk) ld(va, k0);
+  while (k0 < nchunk) {
+    if (k0 + STEP < nchunk) ld(vb, k0 + STEP);
+    scan(va, k0);
+    k0 += STEP;
+    if (k0 >= nchunk) break;
+    if (k0 + STEP < nchunk) ld(va, k0 + STEP);
+    scan(vb, k0);
+    k0 += STEP;
   }
   if (tid < V - tail0) take(am_val<Elem>(rowp, tail0 + tid), tail0 + tid);
   if (tid < head || tid < V - tail0) {
