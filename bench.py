@@ -435,7 +435,8 @@ def main():
     # target rows of greedy requests too, for their argmax)
     dom_bytes = rows * cfg.V * s
     achieved = dom_bytes / (dom_avg_ms / 1e3) / 1e9
-    traffic = traffic_record(dom, cfg.name)
+    # counter traffic is recorded for the plain call of each workload only
+    traffic = None if (args.mixed or args.penalty) else traffic_record(dom, cfg.name)
 
     graph = None
     if args.graph:
