@@ -292,9 +292,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the verifier shards over requests with no "
-              "communication, and multi-GPU runs are not part of this build (use --gpus 1).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only (use --gpus 1): the verifier shards over "
+              "requests with no communication, so N GPUs each run this measurement on "
+              "their own B/N requests.", file=sys.stderr)
         sys.exit(2)
 
     import torch

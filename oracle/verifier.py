@@ -22,7 +22,7 @@ Pages followed (cited by title and section):
   [STD]     "Speculative Token Decoupling: Asynchronous Verification via
             Flash-Decoding": Equation 3.1 (acceptance min(1, p/q)).
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * transform order: bans -> temperature -> top-k -> top-p -> renormalise;
   * top-k keeps every token whose logit is >= the k-th largest (ties kept);
   * top-p keeps token x when the tempered mass of strictly larger logits is
