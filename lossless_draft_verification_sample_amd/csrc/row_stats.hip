@@ -455,13 +455,20 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
   }
   const float m = hb_value_of_rank(rtop);
   const double md = (double)m;
-  // rescale every wave to the row maximum; prefixes before this thread
+  // rescale every wave to the row maximum; prefixes before this thread. Lane
+  // k evaluates wave k's factor once; the wave reads it back from that lane.
+  static_assert(NW <= WAVE, "one lane per wave's factor");
+  int tk = x[0].top;
+#pragma unroll
+  for (int k = 1; k < NW; ++k)
+    if (lane == k) tk = x[k].top;
+  const double sc_lane =
+      tk < HB_RANKS ? exp_neg(((double)hb_value_of_rank(tk) - md) * invT) : 0.0;
   double Z0 = 0.0, mass_before = 0.0, scale_w = 0.0;
   uint32_t cnt_before = cnt_incl - cl;
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
-    const double sc = x[k].top < HB_RANKS
-                          ? exp_neg(((double)hb_value_of_rank(x[k].top) - md) * invT) : 0.0;
+    const double sc = readlane_f64(sc_lane, k);
     const double zk = x[k].z * sc;
     Z0 += zk;
     if (k < w) {

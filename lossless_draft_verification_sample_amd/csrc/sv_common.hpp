@@ -119,6 +119,14 @@ __device__ __forceinline__ ReqInfo request_info(const ReqArgs& q, int b, int gam
   return r;
 }
 
+// Lane `src`'s double (src wave-uniform), in scalar registers.
+__device__ __forceinline__ double readlane_f64(double v, int src) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // ---------------------------------------------------------------- numbers
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

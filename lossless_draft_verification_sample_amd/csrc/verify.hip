@@ -132,12 +132,6 @@ struct Walk {
 };
 
 // Lane `src`'s RowStat (src wave-uniform), in scalar registers.
-__device__ __forceinline__ double readlane_f64(double v, int src) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
 __device__ __forceinline__ RowStat rowstat_from_lane(const RowStat& v, int src) {
   RowStat r;
   r.m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.m), src));
