@@ -585,7 +585,8 @@ __device__ __forceinline__ bool hb_epilogue(const SamplerDev s, RowShared& sh, R
     out.m = m;
   }
   out.tau = trunc ? hb_value_of_rank(rp_last) : -INFINITY;
-  out.lse = md * invT + log(Z);
+  // only thread 0 reports the row: the other waves skip the fp64 log
+  out.lse = threadIdx.x < WAVE ? md * invT + log(Z) : -INFINITY;
   return true;
 }
 
