@@ -13,15 +13,22 @@ oracle-drawn proposals of tests/golden/proposals.json.
 Prints one JSON line. `value` is verified logit rows per second
 (B*(2*gamma+1) rows per sampling call). `roofline` rates the dominant kernel
 (row_stats, or greedy_argmax) on algorithmic bytes (every logit read once)
-divided by its average duration, measured with HIP events recorded by the
-library around each of its launches on the launch stream. `cpu_baseline` times
+divided by its average duration, measured with HIP events that the benchmark
+build of the library (libspecverify_bench.so: same kernels, plus event pairs
+around each launch on the launch stream) records in a second loop. The line
+also carries the accepted-prefix histogram of the last timed call and the
+conditional acceptance rate by position derived from it. `cpu_baseline` times
 the float64 oracle on a bounded sample of the same workload on one host core;
 `cpu_baseline_pool` runs it over the whole batch split across up to 16 host
 processes. `parity` compares the last timed call's tokens, accepted counts
 and flags with the one-core oracle run's, request by request.
 
-With --diagnostics every step also asks for the per-position overlaps and the
-accepted-prefix histogram; the line then carries a `diagnostics` object that
+Before the W warm-up steps the GPU is brought to steady clocks by untimed
+calls for about --ramp-ms milliseconds (reported as `clock_ramp`); from a cold
+start the first ~150 calls run at lower clocks.
+
+With --diagnostics every step also asks for the per-position overlaps; the
+line then carries a `diagnostics` object that
 rates the overlap kernel the same way (algorithmic bytes: the row of each pair
 that is read in full, both rows when neither is truncated).
 
@@ -133,6 +140,24 @@ def read_ceiling(dev, nbytes, chunk_bytes, iters=50):
     return out
 
 
+def host_cpu():
+    """CPU model and the core counts this process sees (for the baseline lines)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(wl, xs, budget_s, results=None):
     """The float64 oracle, as it stands, on the first requests of the workload.
     When `results` is a list, the oracle's outputs of each timed slice are
@@ -166,7 +191,8 @@ def cpu_baseline(wl, xs, budget_s, results=None):
     rows = done * rows_per_req
     return {"value": rows / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {cfg.B} requests ({rows} rows), float64 NumPy on one "
-                      f"host core, {t_total:.1f} s; bf16->f64 upcast not timed"}
+                      f"host core, {t_total:.1f} s; bf16->f64 upcast not timed",
+            **host_cpu()}
 
 
 def parity_summary(cfg, out, refs, band=1e-10):
@@ -261,15 +287,18 @@ def cpu_baseline_pool(wl, xs, max_workers=16, timeout_s=300.0):
     return {"value": rows / wall, "unit": "rows/s", "cores": n, "kind": "oracle",
             "sample": f"all {cfg.B} requests ({rows} rows) split over {n} host processes, "
                       f"float64 NumPy, {wall:.2f} s wall clock from a common start (longest "
-                      f"process {max(inner):.2f} s); bf16->f64 upcast not timed"}
+                      f"process {max(inner):.2f} s); bf16->f64 upcast not timed",
+            **host_cpu()}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU reaches its steady clocks after about 150 calls (~30 ms): warm up past that
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU reaches its steady clocks after about 150 calls (~30 ms)
+    ap.add_argument("--ramp-ms", type=float, default=100.0,
+                    help="untimed calls for about this long before the warm-up steps")
     ap.add_argument("--config", default="c5")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -329,22 +358,19 @@ def main():
     bans = None if wl.banned is None else torch.from_numpy(wl.banned).to(dev)
     samp = (cfg.temperature, cfg.top_k, cfg.top_p)
     if cfg.mode == "sample":
-        ws = torch.empty(sv.spec_verify_workspace_bytes(cfg.B, cfg.gamma, cfg.V,
-                                                        0 if bans is None else bans.shape[1]),
+        ws = torch.empty(sv.spec_verify_workspace_bytes(cfg.B, cfg.gamma, cfg.V),
                          dtype=torch.uint8, device=dev)
         out = sv.SampleOut(torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev),
                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
                            torch.empty((cfg.B,), dtype=torch.int32, device=dev), None, None,
                            torch.empty((cfg.B, cfg.gamma), dtype=torch.float64, device=dev)
                            if args.diagnostics else None,
-                           torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev)
-                           if args.diagnostics else None)
+                           torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev))
     else:
         out = sv.GreedyOut(torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev),
                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
                            torch.empty((cfg.B,), dtype=torch.int32, device=dev),
-                           torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev)
-                           if args.diagnostics else None)
+                           torch.empty((cfg.gamma + 1,), dtype=torch.int32, device=dev))
 
     if args.commit:
         G1 = cfg.gamma + 1
@@ -381,21 +407,30 @@ def main():
             penalty=torch.full((cfg.B,), 1.2, dtype=torch.float32, device=dev),
             penalty_draft=torch.full((cfg.B,), 1.1, dtype=torch.float32, device=dev))
 
-    def step(k):
+    def step(k, lib=None):
         c = k % COPIES
         if cfg.mode == "sample":
             sv.spec_verify_sample(copies[c], dcopies[c], toks, samp, samp, bans,
                                   seed=cfg.philox_seed, offset=cfg.philox_offset,
-                                  requests=requests, workspace=ws, out=out)
+                                  requests=requests, workspace=ws, out=out, lib=lib)
         else:
-            sv.spec_verify_greedy(copies[c], toks, out=out)
+            sv.spec_verify_greedy(copies[c], toks, out=out, lib=lib)
         if args.commit:
-            sv.spec_verify_commit(out.tokens, out.num_accepted, kv_len, slots, out=cout)
+            sv.spec_verify_commit(out.tokens, out.num_accepted, kv_len, slots, out=cout, lib=lib)
 
+    # clock ramp: untimed calls until about ramp_ms have passed on the GPU
+    ramp_calls, t_ramp = 0, time.perf_counter()
+    while (time.perf_counter() - t_ramp) * 1e3 < args.ramp_ms:
+        for _ in range(10):
+            step(ramp_calls)
+            ramp_calls += 1
+        torch.cuda.synchronize()
+    ramp_ms = (time.perf_counter() - t_ramp) * 1e3
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    log(f"[bench] clock ramp {ramp_calls} calls in {ramp_ms:.0f} ms; warmup {args.warmup} done; "
+        f"timing {args.steps} steps")
 
     # step time: a plain loop, bracketed by events on the launch stream
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -407,13 +442,21 @@ def main():
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(stop)
     log(f"[bench] timed loop {elapsed_ms:.2f} ms")
-    # per-kernel durations: a second loop with the library's event pairs around
-    # each of its launches (those records add gaps, so this loop is not the step time)
-    sv.spec_verify_profile_start(args.steps)
-    for k in range(args.steps):
-        step(k)
+    # keep the timed loop's outputs for the parity and histogram lines (the
+    # loops below overwrite `out`)
+    timed_out = type(out)(*[None if t is None else t.clone() for t in out])
+    # per-kernel durations: a second loop through the benchmark build, which
+    # records event pairs around each of its launches (those records add gaps,
+    # so this loop is not the step time)
+    blib = sv._lib.load_bench()
+    for k in range(5):
+        step(k, blib)
     torch.cuda.synchronize()
-    prof = sv.spec_verify_profile_stop()
+    sv.bench_profile_start(args.steps)
+    for k in range(args.steps):
+        step(k, blib)
+    torch.cuda.synchronize()
+    prof = sv.bench_profile_stop()
     # per-call device time and its spread: events around every step of a
     # third loop (the records between calls add gaps, not call time)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -467,8 +510,14 @@ def main():
                  "steps": reps * COPIES}
         log(f"[bench] graph replays: {g_ms * 1e3:.1f} us per step")
 
+    out = timed_out
     n_acc = out.num_accepted.cpu().numpy()
     flags = out.flags.cpu().numpy()
+    hist = out.accept_hist.cpu().numpy().astype(np.int64)
+    # position i was reached by sum_{n >= i} h_n requests and accepted by sum_{n > i} h_n
+    reached = np.cumsum(hist[::-1])[::-1]
+    cond_acc = [float(reached[i + 1] / reached[i]) if reached[i] else None
+                for i in range(cfg.gamma)]
     res = {
         "metric": "verified logit rows/sec",
         "value": value,
@@ -496,7 +545,10 @@ def main():
                     "p90": float(np.percentile(call_us, 90))},
         "mean_accepted": float(n_acc.mean()),
         "mean_emitted_per_request": float(n_acc.mean() + 1),
+        "accept_hist": hist.tolist(),
+        "conditional_acceptance_by_position": cond_acc,
         "flags_nonzero": int((flags != 0).sum()),
+        "clock_ramp": {"calls": ramp_calls, "ms": ramp_ms},
     }
     if graph is not None:
         res["graph"] = graph
@@ -509,7 +561,7 @@ def main():
         res["roofline"]["algorithmic_bytes"] = dom_bytes
     if args.diagnostics:
         res["config"]["diagnostics"] = True
-        diag = {"accept_hist": out.accept_hist.cpu().numpy().tolist()}
+        diag = {}
         if cfg.mode == "sample":
             ov_ms, ov_n = prof["overlap"]
             ov_avg = ov_ms / max(ov_n, 1)

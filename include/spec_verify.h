@@ -84,8 +84,13 @@ typedef struct {
 #define SV_FLAG_RESIDUAL_ZERO 16u /* residual mass was 0 at a rejection; drawn from p */
 #define SV_FLAG_BAD_PARAM 32u     /* a per-request setting of sv_requests is out of range */
 
-#define SV_MAX_BANNED 2048  /* largest n_banned accepted */
-#define SV_MAX_HISTORY 4096 /* largest sv_requests.n_history accepted */
+/* Largest n_banned (and sv_requests.n_banned_draft) accepted. */
+#define SV_MAX_BANNED 2048
+/* Largest sv_requests.n_history accepted. A row penalizes at most
+ * SV_MAX_HISTORY + 63 distinct ids (its history and the proposals before it);
+ * the kernels keep them in an on-chip hash set of 4096 slots that this bound
+ * keeps at most half full. */
+#define SV_MAX_HISTORY 1984
 
 /* Per-request settings of a mixed batch ("Speculative Decoding - Turn guesses
  * into parallel work", section "Implementation roadmap and tests": continuous
@@ -136,11 +141,12 @@ typedef struct {
   const float* penalty_draft;
 } sv_requests;
 
-/* Workspace bytes needed by spec_verify_sample for these sizes (0 on bad sizes;
- * n_banned is validated but does not change the size). The workspace needs no
- * initialisation and may be reused by later calls on the same stream; calls
- * that run concurrently need separate workspaces. */
-size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t n_banned);
+/* Workspace bytes needed by spec_verify_sample for these sizes (0 when B < 1,
+ * gamma outside [1, 63], V < 1 or the sizes overflow the supported index
+ * ranges). The workspace needs no initialisation and may be reused by later
+ * calls on the same stream; calls that run concurrently need separate
+ * workspaces. */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
 
 /* Speculative-sampling verification.
  *   target_logits  [B][gamma+1][V] of dtype; row i is the target distribution
@@ -261,21 +267,6 @@ int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepte
 /* Static description of a status code. */
 const char* spec_verify_strerror(int status);
 
-/* Kernel-time accounting for benchmarks (host side, not thread-safe).
- * spec_verify_profile_start(n) creates event pairs for up to n launches of each
- * kernel; while active, every launch of the library records a HIP event pair
- * around it on the caller's stream. spec_verify_profile_stop synchronises on
- * those events, writes the summed milliseconds and launch counts of each
- * kernel (arrays of SV_NUM_KERNELS entries, indices SV_K_*), and releases them. */
-#define SV_K_ROW_STATS 0
-#define SV_K_DRAW 1
-#define SV_K_GREEDY_ARGMAX 2
-#define SV_K_GREEDY_SCAN 3
-#define SV_K_OVERLAP 4
-#define SV_K_COMMIT 5
-#define SV_NUM_KERNELS 6
-int spec_verify_profile_start(int32_t max_launches_per_kernel);
-int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     SV_FLAG_RESIDUAL_ZERO,
     SV_FLAG_TOKEN_RANGE,
     SV_MAX_BANNED,
+    SV_MAX_HISTORY,
     SV_OK,
     SvRequests,
     SvSampler,
@@ -127,6 +128,9 @@ def _requests(req, B):
         nh = int(req.history.shape[1])
         if tuple(req.history.shape) != (B, nh):
             raise ValueError("requests.history must be [B, H]")
+        if nh > SV_MAX_HISTORY:
+            raise ValueError(f"requests.history holds {nh} > SV_MAX_HISTORY = {SV_MAX_HISTORY} "
+                             "tokens per request")
     r = SvRequests(_dev_ptr(req.gamma, "requests.gamma", torch.int32),
                    _dev_ptr(req.target, "requests.target"), _dev_ptr(req.draft, "requests.draft"),
                    _dev_ptr(req.banned_draft, "requests.banned_draft", torch.int32), nbd,
@@ -136,25 +140,32 @@ def _requests(req, B):
     return ctypes.byref(r), r
 
 
-def _stream_handle(stream):
+def _stream(stream):
+    """(hipStream_t handle, torch stream) of the call. None means torch's
+    current stream; a raw handle is wrapped as an external stream. Outputs and
+    the workspace the binding allocates are allocated on that stream, so the
+    caching allocator keeps them until the call's kernels have run."""
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    elif not isinstance(stream, torch.cuda.Stream):
+        stream = (torch.cuda.default_stream() if int(stream) == 0
+                  else torch.cuda.ExternalStream(int(stream)))
+    return stream.cuda_stream, stream
 
 
 def spec_verify_strerror(status):
     return _lib.load().spec_verify_strerror(int(status)).decode()
 
 
-def spec_verify_workspace_bytes(B, gamma, V, n_banned=0):
-    return int(_lib.load().spec_verify_workspace_bytes(int(B), int(gamma), int(V), int(n_banned)))
+def spec_verify_workspace_bytes(B, gamma, V):
+    return int(_lib.load().spec_verify_workspace_bytes(int(B), int(gamma), int(V)))
 
 
 def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler=(1.0, 0, 1.0),
                        draft_sampler=(1.0, 0, 1.0), banned_ids=None, seed=0, offset=0,
                        uniforms=None, want_lse=True, want_overlap=False, want_hist=False,
-                       requests=None, workspace=None, out=None, stream=None):
+                       requests=None, workspace=None, out=None, stream=None, lib=None):
     """Speculative-sampling verification of a batch (see include/spec_verify.h).
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (bf16 or fp32),
@@ -164,12 +175,15 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
     want_overlap adds the per-position overlaps [B, gamma] (float64; one more
     read of the rows), want_hist the accepted-prefix histogram [gamma+1]
     (int32 storage of the library's uint32 counts). requests: a Requests tuple
-    of per-request settings (mixed batch) or None.
+    of per-request settings (mixed batch) or None. stream: a torch stream, a
+    raw hipStream_t handle or None (torch's current stream). lib: the loaded
+    library to call (default libspecverify.so; bench.py passes the timing
+    build).
     Returns SampleOut(tokens, num_accepted, flags, target_lse, draft_lse,
     overlap, accept_hist).
     """
     torch = _torch()
-    lib = _lib.load()
+    lib = lib or _lib.load()
     B, G1, V = target_logits.shape
     gamma = G1 - 1
     if tuple(draft_logits.shape) != (B, gamma, V):
@@ -185,20 +199,22 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
     if uniforms is not None and tuple(uniforms.shape) != (B, G1):
         raise ValueError("uniforms must be [B, gamma+1]")
     dev = target_logits.device
-    if out is None:
-        out = SampleOut(
-            torch.empty((B, G1), dtype=torch.int32, device=dev),
-            torch.empty((B,), dtype=torch.int32, device=dev),
-            torch.empty((B,), dtype=torch.int32, device=dev),
-            torch.empty((B, G1), dtype=torch.float32, device=dev) if want_lse else None,
-            torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_lse else None,
-            torch.empty((B, gamma), dtype=torch.float64, device=dev) if want_overlap else None,
-            torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None,
-        )
+    handle, strm = _stream(stream)
+    with torch.cuda.stream(strm):
+        if out is None:
+            out = SampleOut(
+                torch.empty((B, G1), dtype=torch.int32, device=dev),
+                torch.empty((B,), dtype=torch.int32, device=dev),
+                torch.empty((B,), dtype=torch.int32, device=dev),
+                torch.empty((B, G1), dtype=torch.float32, device=dev) if want_lse else None,
+                torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_lse else None,
+                torch.empty((B, gamma), dtype=torch.float64, device=dev) if want_overlap else None,
+                torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None,
+            )
+        if workspace is None:
+            need = lib.spec_verify_workspace_bytes(B, gamma, V)
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     req = _requests(requests, B)
-    need = lib.spec_verify_workspace_bytes(B, gamma, V, n_banned)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     rc = lib.spec_verify_sample(
         _dev_ptr(target_logits, "target_logits"), _dev_ptr(draft_logits, "draft_logits"), dt,
         _dev_ptr(draft_tokens, "draft_tokens", torch.int32),
@@ -213,19 +229,19 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
         _dev_ptr(out.draft_lse, "out_draft_lse", torch.float32),
         _checked(out.overlap, "out_overlap", torch.float64, (B, gamma)),
         _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)),
-        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream_handle(stream))
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), handle)
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_sample")
     return out
 
 
 def spec_verify_greedy(target_logits, draft_tokens, banned_ids=None, want_hist=False, out=None,
-                       stream=None):
+                       stream=None, lib=None):
     """Greedy verification (see include/spec_verify.h); banned_ids [B, n] int32
-    or None. Returns GreedyOut(tokens, num_accepted, flags, accept_hist)."""
+    or None; stream and lib as for spec_verify_sample.
+    Returns GreedyOut(tokens, num_accepted, flags, accept_hist)."""
     torch = _torch()
-    lib = _lib.load()
+    lib = lib or _lib.load()
     B, G1, V = target_logits.shape
     gamma = G1 - 1
     if tuple(draft_tokens.shape) != (B, gamma):
@@ -235,11 +251,13 @@ def spec_verify_greedy(target_logits, draft_tokens, banned_ids=None, want_hist=F
         raise ValueError("banned_ids must be [B, n_banned]")
     dt = _dtype_code(target_logits)
     dev = target_logits.device
+    handle, strm = _stream(stream)
     if out is None:
-        out = GreedyOut(torch.empty((B, G1), dtype=torch.int32, device=dev),
-                        torch.empty((B,), dtype=torch.int32, device=dev),
-                        torch.empty((B,), dtype=torch.int32, device=dev),
-                        torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None)
+        with torch.cuda.stream(strm):
+            out = GreedyOut(torch.empty((B, G1), dtype=torch.int32, device=dev),
+                            torch.empty((B,), dtype=torch.int32, device=dev),
+                            torch.empty((B,), dtype=torch.int32, device=dev),
+                            torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None)
     rc = lib.spec_verify_greedy(
         _dev_ptr(target_logits, "target_logits"), dt,
         _dev_ptr(draft_tokens, "draft_tokens", torch.int32),
@@ -247,24 +265,24 @@ def spec_verify_greedy(target_logits, draft_tokens, banned_ids=None, want_hist=F
         _dev_ptr(out.tokens, "out_tokens", torch.int32),
         _dev_ptr(out.num_accepted, "out_num_accepted", torch.int32),
         _dev_ptr(out.flags, "out_flags", torch.int32),
-        _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)), _stream_handle(stream))
+        _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)), handle)
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_greedy")
     return out
 
 
 def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, gamma_b=None, out=None,
-                       stream=None):
+                       stream=None, lib=None):
     """Chain KV-commit metadata of a verification round (see include/spec_verify.h).
 
     tokens [B, gamma+1] and num_accepted [B] from spec_verify_sample or
     spec_verify_greedy, kv_len [B] int32, slots [B, gamma+1] int32 or None,
     gamma_b [B] int32 proposals per request or None.
     Returns CommitOut(new_kv_len, anchor, n_free, free_slots); free_slots is
-    None when slots is None.
+    None when slots is None. stream and lib as for spec_verify_sample.
     """
     torch = _torch()
-    lib = _lib.load()
+    lib = lib or _lib.load()
     B, G1 = tokens.shape
     gamma = G1 - 1
     if tuple(num_accepted.shape) != (B,) or tuple(kv_len.shape) != (B,):
@@ -272,12 +290,14 @@ def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, gamma_b=None, o
     if slots is not None and tuple(slots.shape) != (B, G1):
         raise ValueError("slots must be [B, gamma+1]")
     dev = tokens.device
+    handle, strm = _stream(stream)
     if out is None:
-        out = CommitOut(torch.empty((B,), dtype=torch.int32, device=dev),
-                        torch.empty((B,), dtype=torch.int32, device=dev),
-                        torch.empty((B,), dtype=torch.int32, device=dev),
-                        torch.empty((B, gamma), dtype=torch.int32, device=dev)
-                        if slots is not None else None)
+        with torch.cuda.stream(strm):
+            out = CommitOut(torch.empty((B,), dtype=torch.int32, device=dev),
+                            torch.empty((B,), dtype=torch.int32, device=dev),
+                            torch.empty((B,), dtype=torch.int32, device=dev),
+                            torch.empty((B, gamma), dtype=torch.int32, device=dev)
+                            if slots is not None else None)
     rc = lib.spec_verify_commit(
         _dev_ptr(tokens, "tokens", torch.int32), _dev_ptr(num_accepted, "num_accepted", torch.int32),
         _dev_ptr(kv_len, "kv_len", torch.int32), _dev_ptr(slots, "slots", torch.int32),
@@ -285,25 +305,27 @@ def spec_verify_commit(tokens, num_accepted, kv_len, slots=None, gamma_b=None, o
         _checked(out.new_kv_len, "new_kv_len", torch.int32, (B,)),
         _checked(out.anchor, "anchor", torch.int32, (B,)),
         _checked(out.n_free, "n_free", torch.int32, (B,)),
-        _checked(out.free_slots, "free_slots", torch.int32, (B, gamma)), _stream_handle(stream))
+        _checked(out.free_slots, "free_slots", torch.int32, (B, gamma)), handle)
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_commit")
     return out
 
 
-def spec_verify_profile_start(max_launches_per_kernel):
-    rc = _lib.load().spec_verify_profile_start(int(max_launches_per_kernel))
+def bench_profile_start(max_launches_per_kernel):
+    """Starts per-kernel event timing in the benchmark build (_lib.load_bench());
+    only calls made with lib=_lib.load_bench() are timed."""
+    rc = _lib.load_bench().sv_bench_profile_start(int(max_launches_per_kernel))
     if rc != SV_OK:
-        raise SpecVerifyError(rc, "spec_verify_profile_start")
+        raise SpecVerifyError(rc, "sv_bench_profile_start")
 
 
-def spec_verify_profile_stop():
-    """Returns {kernel name: (total_ms, launches)} since spec_verify_profile_start."""
+def bench_profile_stop():
+    """Returns {kernel name: (total_ms, launches)} since bench_profile_start."""
     import ctypes
     ms = (ctypes.c_double * _lib.SV_NUM_KERNELS)()
     n = (ctypes.c_int32 * _lib.SV_NUM_KERNELS)()
-    rc = _lib.load().spec_verify_profile_stop(ctypes.cast(ms, ctypes.c_void_p),
-                                              ctypes.cast(n, ctypes.c_void_p))
+    rc = _lib.load_bench().sv_bench_profile_stop(ctypes.cast(ms, ctypes.c_void_p),
+                                                 ctypes.cast(n, ctypes.c_void_p))
     if rc != SV_OK:
-        raise SpecVerifyError(rc, "spec_verify_profile_stop")
+        raise SpecVerifyError(rc, "sv_bench_profile_stop")
     return {name: (ms[k], n[k]) for k, name in enumerate(_lib.KERNEL_NAMES)}

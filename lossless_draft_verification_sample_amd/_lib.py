@@ -1,7 +1,9 @@
 """ctypes declarations of the C interface in include/spec_verify.h.
 
 Loading fails loudly when the HIP library has not been built; there is no
-fallback implementation.
+fallback implementation. load_bench() loads the benchmark build of the same
+sources (libspecverify_bench.so), which adds per-kernel event timing
+(csrc/sv_bench_timing.h); only bench.py uses it.
 """
 
 import ctypes
@@ -9,6 +11,8 @@ import os
 
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+BENCH_LIB_NAME = "libspecverify_bench.so"
+BENCH_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), BENCH_LIB_NAME)
 
 SV_F32 = 0
 SV_BF16 = 1
@@ -28,8 +32,9 @@ SV_FLAG_RESIDUAL_ZERO = 16
 SV_FLAG_BAD_PARAM = 32
 
 SV_MAX_BANNED = 2048
-SV_MAX_HISTORY = 4096
+SV_MAX_HISTORY = 1984
 
+# kernel indices of sv_bench_profile_stop (csrc/sv_bench_timing.h)
 SV_K_ROW_STATS = 0
 SV_K_DRAW = 1
 SV_K_GREEDY_ARGMAX = 2
@@ -60,7 +65,7 @@ _i32 = _c.c_int32
 _u64 = _c.c_uint64
 
 SIGNATURES = {
-    "spec_verify_workspace_bytes": (_c.c_size_t, [_i32, _i32, _i32, _i32]),
+    "spec_verify_workspace_bytes": (_c.c_size_t, [_i32, _i32, _i32]),
     "spec_verify_sample": (_c.c_int, [
         _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
         _c.POINTER(SvRequests), _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -70,26 +75,40 @@ SIGNATURES = {
     "spec_verify_commit": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp,
                                       _vp]),
     "spec_verify_strerror": (_c.c_char_p, [_c.c_int]),
-    "spec_verify_profile_start": (_c.c_int, [_i32]),
-    "spec_verify_profile_stop": (_c.c_int, [_vp, _vp]),
+}
+BENCH_SIGNATURES = {
+    "sv_bench_profile_start": (_c.c_int, [_i32]),
+    "sv_bench_profile_stop": (_c.c_int, [_vp, _vp]),
 }
 
 _LIB = None
+_BENCH_LIB = None
+
+
+def _open(path, name, sigs):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{name} is not built ({path}); run "
+            "`python -m lossless_draft_verification_sample_amd.build` or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    for fname, (res, args) in sigs.items():
+        fn = getattr(lib, fname)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
 
 
 def load(path=LIB_PATH):
     """The loaded library with argument types set (cached)."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    if not os.path.exists(path):
-        raise RuntimeError(
-            f"{LIB_NAME} is not built ({path}); run "
-            "`python -m lossless_draft_verification_sample_amd.build` or __graft_entry__.build()")
-    lib = ctypes.CDLL(path)
-    for name, (res, args) in SIGNATURES.items():
-        fn = getattr(lib, name)
-        fn.restype = res
-        fn.argtypes = args
-    _LIB = lib
-    return lib
+    if _LIB is None:
+        _LIB = _open(path, LIB_NAME, SIGNATURES)
+    return _LIB
+
+
+def load_bench(path=BENCH_LIB_PATH):
+    """The benchmark build (same entry points plus per-kernel event timing)."""
+    global _BENCH_LIB
+    if _BENCH_LIB is None:
+        _BENCH_LIB = _open(path, BENCH_LIB_NAME, {**SIGNATURES, **BENCH_SIGNATURES})
+    return _BENCH_LIB

@@ -1,11 +1,19 @@
-"""Build libspecverify.so (the HIP library behind include/spec_verify.h) and
-libsvcalib.so (an HBM read-bandwidth calibration kernel) for gfx950.
+"""Build the HIP libraries of the package for gfx950, in-tree.
 
-    python -m lossless_draft_verification_sample_amd.build
+    python -m lossless_draft_verification_sample_amd.build [-v]
 
-Compiles in-tree with hipcc; the shared object lands next to this file.
+- libspecverify.so: the verifier behind include/spec_verify.h.
+- libspecverify_bench.so: the same kernels and entry points, plus HIP event
+  pairs around every launch and the two calls that read them
+  (csrc/sv_bench_timing.h). Only bench.py loads it, for per-kernel times.
+- libsvcalib.so: an HBM read-bandwidth calibration kernel (bench.py
+  --read-ceiling); not on the verification path.
+
+Every source is compiled to an object (in parallel) under _build/, then the
+objects are linked; the shared objects land next to this file.
 """
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -13,8 +21,11 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
+OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libspecverify.so"
-SOURCES = ["row_stats.hip", "verify.hip", "overlap.hip", "greedy.hip", "commit.hip", "api.cpp"]
+BENCH_LIB_NAME = "libspecverify_bench.so"
+KERNEL_SOURCES = ["row_stats.hip", "verify.hip", "overlap.hip", "greedy.hip", "commit.hip"]
+API_SOURCE = "api.cpp"
 # HBM read-bandwidth calibration (bench.py --read-ceiling); not on the path
 CALIB_LIB_NAME = "libsvcalib.so"
 CALIB_SOURCES = ["calib/read_ceiling.hip"]
@@ -25,7 +36,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     # IEEE float32 division: the repetition penalty divides logits
     "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -34,6 +44,7 @@ HIPCC_FLAGS = [
     "-Wall",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+NOISE = "packed-fp32-ops"
 
 
 def hipcc():
@@ -43,26 +54,47 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose=False, out_dir=PKG_DIR):
-    out = _compile(LIB_NAME, SOURCES, verbose, out_dir)
-    _compile(CALIB_LIB_NAME, CALIB_SOURCES, verbose, out_dir)
-    return out
-
-
-def _compile(lib_name, sources, verbose, out_dir):
-    out = os.path.join(out_dir, lib_name)
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in sources]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "packed-fp32-ops"
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if NOISE not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
+
+
+def _object(src, tag, extra, verbose):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    base = os.path.splitext(os.path.basename(src))[0]
+    obj = os.path.join(OBJ_DIR, f"{base}{tag}.o")
+    _run([hipcc(), *HIPCC_FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)
+    return obj
+
+
+def _link(lib_name, objs, verbose, out_dir):
+    out = os.path.join(out_dir, lib_name)
+    tmp = out + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False, out_dir=PKG_DIR):
+    """Compiles every source and links the three libraries; returns the path of
+    libspecverify.so."""
+    jobs = [(s, "", []) for s in KERNEL_SOURCES + CALIB_SOURCES]
+    jobs += [(API_SOURCE, "", []), (API_SOURCE, "_bench", ["-DSV_BENCH_TIMING"])]
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda j: _object(*j, verbose), jobs))
+    kern = objs[: len(KERNEL_SOURCES)]
+    calib = objs[len(KERNEL_SOURCES): len(KERNEL_SOURCES) + len(CALIB_SOURCES)]
+    api, api_bench = objs[-2], objs[-1]
+    out = _link(LIB_NAME, kern + [api], verbose, out_dir)
+    _link(BENCH_LIB_NAME, kern + [api_bench], verbose, out_dir)
+    _link(CALIB_LIB_NAME, calib, verbose, out_dir)
     return out
 
 

@@ -1,6 +1,10 @@
 // Host side of the C interface declared in include/spec_verify.h: argument
 // validation (before anything touches the device), workspace carving and the
 // kernel launch sequence on the caller's stream.
+//
+// Built twice: as the product library, and with SV_BENCH_TIMING as the
+// benchmark library, which also records HIP event pairs around every launch
+// (sv_bench_timing.h).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -10,7 +14,14 @@
 #include <vector>
 
 #include "../../include/spec_verify.h"
+#include "sv_bans.hpp"
+#include "sv_bench_timing.h"
 #include "sv_launch.hpp"
+
+// The penalized ids of a row (history plus up to 63 proposals) and a ban list
+// must each fit the on-chip hash sets at most half full.
+static_assert(SV_MAX_HISTORY + 63 <= (int)sv::HT_MAX_IDS, "penalty set bound");
+static_assert(SV_MAX_BANNED <= (int)sv::HT_MAX_IDS, "ban set bound");
 
 namespace {
 
@@ -24,9 +35,8 @@ struct Layout {
   int ov_spp, ov_parts;
 };
 
-bool layout(int32_t B, int32_t gamma, int32_t V, int32_t n_banned, Layout* L) {
-  if (B < 1 || gamma < 1 || gamma > 63 || V < 1 || n_banned < 0 || n_banned > SV_MAX_BANNED)
-    return false;
+bool layout(int32_t B, int32_t gamma, int32_t V, Layout* L) {
+  if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return false;
   const int64_t rows = (int64_t)B * (2 * (int64_t)gamma + 1);
   if (rows >= INT32_MAX) return false;
   const int64_t nsub = ((int64_t)V + sv::DRAW_SUB - 1) / sv::DRAW_SUB;
@@ -88,6 +98,7 @@ sv::SamplerDev to_dev(const sv_sampler& s) {
 
 // ---------------------------------------------------------------- profiling
 
+#ifdef SV_BENCH_TIMING
 struct Prof {
   bool on = false;
   int cap = 0;
@@ -96,6 +107,7 @@ struct Prof {
 };
 Prof g_prof;
 
+// Records an event pair around one launch while a profile is active.
 struct ProfScope {
   int k;
   hipStream_t s;
@@ -112,14 +124,20 @@ struct ProfScope {
     }
   }
 };
+#else
+// The product library records nothing.
+struct ProfScope {
+  ProfScope(int, hipStream_t) {}
+};
+#endif
 
 }  // namespace
 
 extern "C" {
 
-size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t n_banned) {
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
   Layout L;
-  if (!layout(B, gamma, V, n_banned, &L)) return 0;
+  if (!layout(B, gamma, V, &L)) return 0;
   return L.total;
 }
 
@@ -172,7 +190,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)target_logits % es) || ((uintptr_t)draft_logits % es)) return SV_EINVAL;
   Layout L;
-  if (!layout(B, gamma, V, n_banned, &L)) return SV_ESIZE;
+  if (!layout(B, gamma, V, &L)) return SV_ESIZE;
   if (!workspace || ((uintptr_t)workspace % WS_ALIGN) || workspace_bytes < L.total)
     return SV_EWORKSPACE;
 
@@ -313,7 +331,8 @@ int spec_verify_commit(const int32_t* out_tokens, const int32_t* out_num_accepte
   return SV_OK;
 }
 
-int spec_verify_profile_start(int32_t max_launches_per_kernel) {
+#ifdef SV_BENCH_TIMING
+int sv_bench_profile_start(int32_t max_launches_per_kernel) {
   if (g_prof.on || max_launches_per_kernel < 1) return SV_EINVAL;
   for (int k = 0; k < SV_NUM_KERNELS; ++k) {
     g_prof.ev[k].assign(2 * (size_t)max_launches_per_kernel, nullptr);
@@ -326,7 +345,7 @@ int spec_verify_profile_start(int32_t max_launches_per_kernel) {
   return SV_OK;
 }
 
-int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
+int sv_bench_profile_stop(double* total_ms, int32_t* launches) {
   if (!g_prof.on) return SV_EINVAL;
   int rc = SV_OK;
   for (int k = 0; k < SV_NUM_KERNELS; ++k) {
@@ -347,5 +366,7 @@ int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
   g_prof.on = false;
   return rc;
 }
+
+#endif  // SV_BENCH_TIMING
 
 }  // extern "C"

@@ -67,8 +67,11 @@ __global__ __launch_bounds__(WAVE) void greedy_scan_kernel(GreedyArgs a) {
   int n = g;
   for (int i = 0; i < g; ++i) {
     const int32_t x = xs[i];
-    if (x < 0 || x >= a.V) flags |= FLAG_TOKEN_RANGE;
-    if (n == g && x != (out[i] & 0x7FFFFFFF) - 1) n = i;
+    const bool range = x < 0 || x >= a.V;
+    if (range) flags |= FLAG_TOKEN_RANGE;
+    // a proposal outside the vocabulary never matches, not even the -1 of a
+    // row without an admissible id
+    if (n == g && (range || x != (out[i] & 0x7FFFFFFF) - 1)) n = i;
   }
   for (int i = 0; i < G1; ++i) {
     const int32_t e = out[i];

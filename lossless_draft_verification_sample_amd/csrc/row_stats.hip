@@ -71,7 +71,9 @@ constexpr uint32_t HB_BINS = HB_NEG + HB_WIN + 1u;
 constexpr int HB_RANKS = 2 * HB_WIN + 1;      // value-ordered ranks: +window, zero, -window
 constexpr uint32_t TINY_MAX = 64;             // tiny values tracked exactly per row
 
-static_assert(HT_SLOTS >= 2 * 2048 && HT_SLOTS <= HB_BINS, "ban hash set size");
+// The ban set and the penalty set each hold at most HT_MAX_IDS ids (the host
+// bounds both lists), and both fit in the histogram storage before the stream.
+static_assert(HT_MAX_IDS >= 2048 && 2 * HT_SLOTS <= HB_BINS, "hash set sizes");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -619,16 +621,7 @@ __device__ __forceinline__ uint32_t pen_build(uint32_t* ptab, const uint32_t* ba
     if (id < 0 || id >= V) continue;
     if (bantab && ht_has(bantab, id)) continue;   // banned wins
     if (id == x) *xpen = 1u;
-    uint32_t slot = ht_slot(id);
-    while (true) {
-      const uint32_t old = atomicCAS(&ptab[slot], HT_EMPTY, (uint32_t)id);
-      if (old == HT_EMPTY) {
-        own |= 1u << k;
-        break;
-      }
-      if (old == (uint32_t)id) break;
-      slot = (slot + 1u) & (HT_SLOTS - 1u);
-    }
+    if (ht_insert(ptab, id)) own |= 1u << k;
   }
   return own;
 }

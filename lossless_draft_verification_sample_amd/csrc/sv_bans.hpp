@@ -1,5 +1,11 @@
-// LDS hash set of a request's banned ids (linear probing, at most half full),
-// shared by the kernels that test single ids against a raw ban list.
+// LDS hash set of token ids (linear probing), shared by the kernels that test
+// single ids against a raw ban list or a row's repetition-penalized ids.
+//
+// Every set holds at most HT_MAX_IDS distinct ids, half of its slots: the host
+// bounds the ban lists (SV_MAX_BANNED) and the penalized ids of a row (the
+// history, SV_MAX_HISTORY, plus at most 63 earlier proposals) accordingly, so
+// a probe sequence always meets an empty slot. The probe loops are also capped
+// at HT_SLOTS steps, so no input can keep them spinning.
 #pragma once
 
 #include "sv_common.hpp"
@@ -8,9 +14,23 @@ namespace sv {
 
 constexpr uint32_t HT_SLOTS = 4096;
 constexpr uint32_t HT_EMPTY = 0xFFFFFFFFu;
+constexpr uint32_t HT_MAX_IDS = HT_SLOTS / 2;
 
 __device__ __forceinline__ uint32_t ht_slot(int32_t id) {
   return ((uint32_t)id * 0x9E3779B1u) >> 20;   // multiplicative hash, 12 bits
+}
+
+// Inserts `id` into the set; true when this call added it (false when it was
+// already there).
+__device__ __forceinline__ bool ht_insert(uint32_t* tab, int32_t id) {
+  uint32_t slot = ht_slot(id);
+  for (uint32_t probe = 0; probe < HT_SLOTS; ++probe) {
+    const uint32_t old = atomicCAS(&tab[slot], HT_EMPTY, (uint32_t)id);
+    if (old == HT_EMPTY) return true;
+    if (old == (uint32_t)id) return false;
+    slot = (slot + 1u) & (HT_SLOTS - 1u);
+  }
+  return false;   // a full set: unreachable within HT_MAX_IDS ids
 }
 
 // Inserts the valid ids of a raw ban list into the LDS hash set `tab` (all
@@ -26,28 +46,20 @@ __device__ __forceinline__ uint32_t ht_build(uint32_t* tab, const int32_t* bl, i
     const int32_t id = j == (int)threadIdx.x ? first : bl[j];
     if (id < 0 || id >= V) continue;
     if (id == x) *xban = 1u;
-    uint32_t slot = ht_slot(id);
-    while (true) {
-      const uint32_t old = atomicCAS(&tab[slot], HT_EMPTY, (uint32_t)id);
-      if (old == HT_EMPTY) {
-        own |= 1u << k;
-        break;
-      }
-      if (old == (uint32_t)id) break;
-      slot = (slot + 1u) & (HT_SLOTS - 1u);
-    }
+    if (ht_insert(tab, id)) own |= 1u << k;
   }
   return own;
 }
 
 __device__ __forceinline__ bool ht_has(const uint32_t* tab, int32_t id) {
   uint32_t slot = ht_slot(id);
-  while (true) {
+  for (uint32_t probe = 0; probe < HT_SLOTS; ++probe) {
     const uint32_t v = tab[slot];
     if (v == (uint32_t)id) return true;
     if (v == HT_EMPTY) return false;
     slot = (slot + 1u) & (HT_SLOTS - 1u);
   }
+  return false;
 }
 
 }  // namespace sv

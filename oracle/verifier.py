@@ -402,7 +402,9 @@ def verify_greedy(target, draft_tokens, banned=None):
             f |= FLAG_TOKEN_RANGE
         n = gamma
         for i in range(gamma):
-            if xs[i] != am[b, i]:
+            # a proposal outside [0, V) is no token of the row: it never
+            # matches, not even the -1 "argmax" of a row with no admissible id
+            if not 0 <= xs[i] < V or xs[i] != am[b, i]:
                 n = i
                 break
             tokens[b, i] = xs[i]
@@ -498,7 +500,7 @@ def verify_batch(target, draft, draft_tokens, uniforms, target_samplers, draft_s
                 f |= FLAG_TOKEN_RANGE
             n = gb
             for i in range(gb):
-                if xs[i] != am[i]:
+                if not 0 <= xs[i] < V or xs[i] != am[i]:
                     n = i
                     break
                 tokens[b, i] = xs[i]

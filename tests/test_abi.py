@@ -50,17 +50,15 @@ def test_strerror(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.spec_verify_workspace_bytes
-    a = ws(128, 8, 151936, 64)
+    a = ws(128, 8, 151936)
     assert a > 0 and a % 256 == 0
-    assert ws(128, 8, 151936, 0) == a    # ban lists are read in place
-    assert ws(1, 4, 1000, 0) > 0
+    assert ws(1, 4, 1000) > 0
     # room for the row statistics (32 B per row), the uniforms (8 B per slot),
     # the draw's sub-chunk sums (16 B per 2048 tokens per request) and the
     # per-request arrival counters
     B, g, V = 128, 8, 151936
     assert a >= B * (2 * g + 1) * 32 + B * (g + 1) * 8 + B * -(-V // 2048) * 16 + B * 4
-    for bad in [(0, 4, 10, 0), (1, 0, 10, 0), (1, 64, 10, 0), (1, 4, 0, 0), (1, 4, 10, -1),
-                (1, 4, 10, 2049), (2**30, 63, 10, 0)]:
+    for bad in [(0, 4, 10), (1, 0, 10), (1, 64, 10), (1, 4, 0), (2**30, 63, 10)]:
         assert ws(*bad) == 0, bad
 
 
@@ -87,7 +85,7 @@ def test_sample_argument_errors(lib):
     S = L.SvSampler
     # everything valid except the workspace: rejected before launching
     assert _sample(lib) == L.SV_EWORKSPACE
-    need = lib.spec_verify_workspace_bytes(2, 3, 100, 0)
+    need = lib.spec_verify_workspace_bytes(2, 3, 100)
     assert _sample(lib, ws=FAKE, ws_bytes=need - 1) == L.SV_EWORKSPACE
     assert _sample(lib, ws=FAKE + 8, ws_bytes=need) == L.SV_EWORKSPACE   # misaligned
     cases = {
@@ -111,6 +109,34 @@ def test_sample_argument_errors(lib):
     assert _sample(lib, requests=ctypes.byref(bad_req)) == L.SV_EINVAL
     big = L.SvRequests(None, None, None, FAKE, 2049)
     assert _sample(lib, requests=ctypes.byref(big)) == L.SV_EINVAL
+
+
+def test_history_bound(lib):
+    """n_history above SV_MAX_HISTORY is rejected before any launch, and the
+    bound keeps every row's penalized ids (history plus up to 63 earlier
+    proposals) within half of the kernels' 4096-slot on-chip hash set."""
+    import ctypes
+    from lossless_draft_verification_sample_amd import _lib as L
+    hdr = open(HEADER).read()
+    hist_max = int(re.search(r"#define SV_MAX_HISTORY (\d+)", hdr).group(1))
+    bans_max = int(re.search(r"#define SV_MAX_BANNED (\d+)", hdr).group(1))
+    assert L.SV_MAX_HISTORY == hist_max and L.SV_MAX_BANNED == bans_max
+    bans = open(os.path.join(ROOT, "lossless_draft_verification_sample_amd", "csrc",
+                             "sv_bans.hpp")).read()
+    slots = int(re.search(r"HT_SLOTS = (\d+)", bans).group(1))
+    max_gamma = 63
+    assert hist_max + max_gamma <= slots // 2
+    assert bans_max <= slots // 2
+    need = lib.spec_verify_workspace_bytes(2, 3, 100)
+    ok = dict(ws=FAKE, ws_bytes=need)
+    # the largest list passes validation (it then fails only on the fake device
+    # pointers, which a CPU test cannot launch with, so check the rejection side)
+    over = L.SvRequests(None, None, None, None, 0, FAKE, hist_max + 1, None, None)
+    assert _sample(lib, requests=ctypes.byref(over), **ok) == L.SV_EINVAL
+    neg = L.SvRequests(None, None, None, None, 0, FAKE, -1, None, None)
+    assert _sample(lib, requests=ctypes.byref(neg), **ok) == L.SV_EINVAL
+    nolist = L.SvRequests(None, None, None, None, 0, None, 5, None, None)
+    assert _sample(lib, requests=ctypes.byref(nolist), **ok) == L.SV_EINVAL
 
 
 def test_greedy_argument_errors(lib):
@@ -147,10 +173,17 @@ def test_commit_argument_errors(lib):
     assert call(B=2**30, g=63) == L.SV_ESIZE
 
 
-def test_profile_stop_without_start(lib):
+def test_timing_lives_in_the_bench_build_only(lib):
+    """The product library has no event timing; the benchmark build exports the
+    same entry points plus the two timing calls, which reject misuse."""
     from lossless_draft_verification_sample_amd import _lib as L
-    assert lib.spec_verify_profile_stop(None, None) == L.SV_EINVAL
-    assert lib.spec_verify_profile_start(0) == L.SV_EINVAL
+    assert not hasattr(lib, "sv_bench_profile_start")
+    assert not hasattr(lib, "sv_bench_profile_stop")
+    bench = L.load_bench()
+    for n in _declared_functions():
+        assert hasattr(bench, n), n
+    assert bench.sv_bench_profile_stop(None, None) == L.SV_EINVAL
+    assert bench.sv_bench_profile_start(0) == L.SV_EINVAL
 
 
 def test_product_does_not_import_oracle():

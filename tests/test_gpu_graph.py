@@ -52,7 +52,7 @@ def test_sample_call_replays_in_a_graph():
     toks = torch.from_numpy(xs).to(dev)
     bans = torch.from_numpy(wl.banned).to(dev)
     samp = pu.sampler_of(cfg)
-    ws = torch.empty(sv.spec_verify_workspace_bytes(cfg.B, cfg.gamma, cfg.V, bans.shape[1]),
+    ws = torch.empty(sv.spec_verify_workspace_bytes(cfg.B, cfg.gamma, cfg.V),
                      dtype=torch.uint8, device=dev)
 
     def new_out():

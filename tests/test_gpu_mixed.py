@@ -290,3 +290,40 @@ def test_overlap_with_penalties():
             if min(pd.topp_margin, qd.topp_margin) <= pu.EXACT_BAND:
                 continue
             assert abs(got["overlap"][b, i] - oracle.overlap(pd.p, qd.p)) <= 1e-9, (b, i)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20011), ("f32", 7001)])
+def test_penalty_at_the_history_limit(dtype, V):
+    """The longest history the interface accepts (SV_MAX_HISTORY ids, all
+    distinct) plus 63 distinct proposals: every row's penalized set is as large
+    as it can be (2047 ids at the bonus row). A sampled request with top-p, a
+    greedy request and a sampled request with top-k; the draft rows of the
+    sampled ones are penalized too."""
+    import lossless_draft_verification_sample_amd as sv
+    g = 63
+    H = sv.SV_MAX_HISTORY
+    wl = pu.make("c5", B=3, gamma=g, V=V, dtype=dtype, seed=99 + V % 7)
+    rng = np.random.default_rng(V)
+    ids = rng.permutation(V).astype(np.int32)
+    xs = np.stack([ids[b * g:(b + 1) * g] for b in range(3)])
+    rest = ids[3 * g:]
+    hist = np.stack([rng.choice(rest, H, replace=False) for _ in range(3)]).astype(np.int32)
+    # request 0 mostly proposes its penalized target's argmax, so that its walk
+    # runs deep into the block
+    for i in range(g):
+        pen_set = hist[0].tolist() + xs[0, :i].tolist()
+        am = oracle.greedy_argmax(wl.target[0, i].astype(np.float64), (), pen_set, 1.3, dtype)
+        if am not in xs[0, :i].tolist() and am not in hist[0].tolist():
+            xs[0, i] = am
+    ts = [(0.8, 0, 0.9), (0.0, 0, 1.0), (1.0, 40, 1.0)]
+    ds = [(0.8, 0, 0.9), (1.0, 0, 1.0), (1.0, 40, 1.0)]
+    pen_t = np.array([1.3, 1.5, 1.2], np.float32)
+    pen_d = np.array([1.1, 1.0, 1.4], np.float32)
+    banned = rng.integers(-1, V, (3, 16)).astype(np.int32)
+    got = _run_pen(wl, xs, ts, ds, None, banned, None, hist, pen_t, pen_d)
+    u = pu.philox_uniforms(4, 2, 3, g)
+    ref = oracle.verify_batch(wl.target.astype(np.float64), wl.draft.astype(np.float64), xs, u,
+                              [oracle.Sampler(*s) for s in ts], [oracle.Sampler(*s) for s in ds],
+                              banned, None, None, hist, pen_t, pen_d, dtype)
+    _compare(got, ref, f"history limit {dtype}")
+    assert not np.any(got["flags"] & oracle.FLAG_BAD_PARAM)

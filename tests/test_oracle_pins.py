@@ -387,6 +387,34 @@ def test_greedy_brute_force_ties_and_signed_zero():
             assert bool(g.flags[b] & 1) == bool(np.any((xs[b] < 0) | (xs[b] >= V)))
 
 
+def test_greedy_out_of_range_proposal_never_matches():
+    """A proposal outside [0, V) is not a token: greedy verification rejects it
+    even where the row has no admissible id (its argmax is then -1, and the
+    -1 of a padding proposal must not count as a match). Checked for
+    verify_greedy and for the greedy requests of verify_batch."""
+    V, gamma = 6, 2
+    nan_row = np.full(V, np.nan)
+    target = np.zeros((2, gamma + 1, V))
+    target[0, 0] = nan_row                       # request 0: row 0 has no admissible id
+    target[1, 0] = nan_row
+    target[1, 0, 3] = 1.0                        # request 1: only id 3 is a number
+    banned = np.array([[-1, -1], [3, -1]])       # ... but 3 is banned: no admissible id
+    xs = np.array([[-1, 2], [-1, 0]], dtype=np.int32)
+    g = oracle.verify_greedy(target, xs, banned)
+    for b in range(2):
+        assert g.argmax[b, 0] == -1
+        assert g.num_accepted[b] == 0
+        assert g.tokens[b].tolist() == [-1, -1, -1]
+        assert g.flags[b] & oracle.FLAG_TOKEN_RANGE and g.flags[b] & oracle.FLAG_EMPTY
+    assert g.flags[0] & oracle.FLAG_NONFINITE
+    greedy = [oracle.Sampler(0.0, 0, 1.0)] * 2
+    mb = oracle.verify_batch(target, np.zeros((2, gamma, V)), xs, np.full((2, gamma + 1), 0.5),
+                             greedy, greedy, banned)
+    assert mb.num_accepted.tolist() == [0, 0]
+    assert mb.tokens.tolist() == g.tokens.tolist()
+    assert mb.flags.tolist() == g.flags.tolist()
+
+
 def test_flags_and_edge_cases():
     V, gamma = 10, 2
     z = np.zeros((1, gamma + 1, V))
