@@ -75,6 +75,8 @@ typedef struct {
 #define SV_EWORKSPACE (-3) /* workspace NULL or smaller than spec_verify_workspace_bytes */
 #define SV_ESIZE (-4)      /* sizes overflow the supported index ranges */
 #define SV_EHIP (-5)       /* a HIP launch or runtime call failed */
+#define SV_ESCRATCH (-6)   /* spec_verify_sample_noalloc: the sizes need more workspace
+                              than SV_NOALLOC_SCRATCH_BYTES */
 
 /* Per-request flag bits written to out_flags. */
 #define SV_FLAG_TOKEN_RANGE 1u    /* some draft token lies outside [0, V) */
@@ -207,6 +209,30 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
                        uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
                        double* out_overlap, uint32_t* out_accept_hist,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify_sample without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, outputs and errors are those of
+ * spec_verify_sample; the workspace is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held until
+ * the process ends. The call allocates nothing. Sizes whose
+ * spec_verify_workspace_bytes exceed SV_NOALLOC_SCRATCH_BYTES return
+ * SV_ESCRATCH (c5-sized batches, B = 128, gamma = 8, V = 151936, need about
+ * 0.3 MB). The first call on a device resolves that device's array address
+ * (SV_EHIP if it cannot). Every call on one GPU shares its array: calls that
+ * may overlap on one GPU (different streams, or different host threads)
+ * race and must be serialised by the caller; calls in order on one stream are
+ * safe. Nothing needs clearing: every call initialises what it reads. */
+#define SV_NOALLOC_SCRATCH_BYTES (8u << 20)
+int spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits,
+                               sv_dtype dtype, const int32_t* draft_tokens,
+                               const int32_t* banned_ids, int32_t n_banned, int32_t B,
+                               int32_t gamma, int32_t V, sv_sampler target, sv_sampler draft,
+                               const sv_requests* requests, uint64_t seed, uint64_t offset,
+                               const double* uniforms, int32_t* out_tokens,
+                               int32_t* out_num_accepted, uint32_t* out_flags,
+                               float* out_target_lse, float* out_draft_lse, double* out_overlap,
+                               uint32_t* out_accept_hist, void* stream);
 
 /* Greedy verification ("Drafters and Speculative Decoding", section "Greedy
  * verification"): proposal i is kept while it equals the argmax of target row i

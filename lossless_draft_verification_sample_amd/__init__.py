@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     SV_BF16,
     SV_EDTYPE,
     SV_EHIP,
+    SV_ESCRATCH,
     SV_EINVAL,
     SV_ESIZE,
     SV_EWORKSPACE,
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     SV_FLAG_TOKEN_RANGE,
     SV_MAX_BANNED,
     SV_MAX_HISTORY,
+    SV_NOALLOC_SCRATCH_BYTES,
     SV_OK,
     SvRequests,
     SvSampler,
@@ -162,10 +164,25 @@ def spec_verify_workspace_bytes(B, gamma, V):
     return int(_lib.load().spec_verify_workspace_bytes(int(B), int(gamma), int(V)))
 
 
+def spec_verify_sample_noalloc(target_logits, draft_logits, draft_tokens,
+                               target_sampler=(1.0, 0, 1.0), draft_sampler=(1.0, 0, 1.0),
+                               banned_ids=None, seed=0, offset=0, uniforms=None, want_lse=True,
+                               want_overlap=False, want_hist=False, requests=None, out=None,
+                               stream=None, lib=None):
+    """spec_verify_sample on the library's static per-GPU scratch instead of a
+    workspace (see include/spec_verify.h). Pass `out` to avoid every
+    allocation in this binding as well."""
+    return spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler,
+                              draft_sampler, banned_ids, seed, offset, uniforms, want_lse,
+                              want_overlap, want_hist, requests, None, out, stream, lib,
+                              _noalloc=True)
+
+
 def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler=(1.0, 0, 1.0),
                        draft_sampler=(1.0, 0, 1.0), banned_ids=None, seed=0, offset=0,
                        uniforms=None, want_lse=True, want_overlap=False, want_hist=False,
-                       requests=None, workspace=None, out=None, stream=None, lib=None):
+                       requests=None, workspace=None, out=None, stream=None, lib=None,
+                       _noalloc=False):
     """Speculative-sampling verification of a batch (see include/spec_verify.h).
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (bf16 or fp32),
@@ -211,11 +228,14 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
                 torch.empty((B, gamma), dtype=torch.float64, device=dev) if want_overlap else None,
                 torch.empty((G1,), dtype=torch.int32, device=dev) if want_hist else None,
             )
-        if workspace is None:
+        if workspace is None and not _noalloc:
             need = lib.spec_verify_workspace_bytes(B, gamma, V)
             workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     req = _requests(requests, B)
-    rc = lib.spec_verify_sample(
+    fn = lib.spec_verify_sample_noalloc if _noalloc else lib.spec_verify_sample
+    ws_args = () if _noalloc else (_dev_ptr(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size())
+    rc = fn(
         _dev_ptr(target_logits, "target_logits"), _dev_ptr(draft_logits, "draft_logits"), dt,
         _dev_ptr(draft_tokens, "draft_tokens", torch.int32),
         _dev_ptr(banned_ids, "banned_ids", torch.int32), n_banned, B, gamma, V,
@@ -228,10 +248,9 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, target_sampler
         _dev_ptr(out.target_lse, "out_target_lse", torch.float32),
         _dev_ptr(out.draft_lse, "out_draft_lse", torch.float32),
         _checked(out.overlap, "out_overlap", torch.float64, (B, gamma)),
-        _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)),
-        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), handle)
+        _checked(out.accept_hist, "out_accept_hist", torch.int32, (G1,)), *ws_args, handle)
     if rc != SV_OK:
-        raise SpecVerifyError(rc, "spec_verify_sample")
+        raise SpecVerifyError(rc, fn.__name__)
     return out
 
 

@@ -23,6 +23,8 @@ SV_EDTYPE = -2
 SV_EWORKSPACE = -3
 SV_ESIZE = -4
 SV_EHIP = -5
+SV_ESCRATCH = -6
+SV_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 SV_FLAG_TOKEN_RANGE = 1
 SV_FLAG_Q_ZERO = 2
@@ -70,6 +72,9 @@ SIGNATURES = {
         _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
         _c.POINTER(SvRequests), _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
         _c.c_size_t, _vp]),
+    "spec_verify_sample_noalloc": (_c.c_int, [
+        _vp, _vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, SvSampler, SvSampler,
+        _c.POINTER(SvRequests), _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_greedy": (_c.c_int, [_vp, _c.c_int, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                       _vp, _vp, _vp]),
     "spec_verify_commit": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp,

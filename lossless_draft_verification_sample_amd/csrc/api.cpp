@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/spec_verify.h"
@@ -131,37 +132,44 @@ struct ProfScope {
 };
 #endif
 
-}  // namespace
+// ---------------------------------------------------------------- static scratch
 
-extern "C" {
+// Workspace of spec_verify_sample_noalloc, for callers that cannot allocate
+// device memory. Each device holds its own copy until the process ends. In
+// host code this name is only a stand-in for the symbol: the device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
 
-size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
-  Layout L;
-  if (!layout(B, gamma, V, &L)) return 0;
-  return L.total;
-}
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[MAX_DEVICES] = {nullptr};
 
-const char* spec_verify_strerror(int status) {
-  switch (status) {
-    case SV_OK: return "success";
-    case SV_EINVAL: return "invalid argument (null pointer, size or sampler setting)";
-    case SV_EDTYPE: return "unsupported dtype (expected SV_F32 or SV_BF16)";
-    case SV_EWORKSPACE: return "workspace missing or smaller than spec_verify_workspace_bytes()";
-    case SV_ESIZE: return "sizes exceed the supported index ranges";
-    case SV_EHIP: return "HIP launch or runtime error";
-    default: return "unknown status";
+// Device address of the current device's scratch array (resolved on the first
+// call on that device, with that device current).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SV_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_EHIP;
+    g_scratch_dev[dev] = p;
   }
+  *out = g_scratch_dev[dev];
+  return SV_OK;
 }
 
-int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype dtype,
-                       const int32_t* draft_tokens, const int32_t* banned_ids,
-                       int32_t n_banned, int32_t B, int32_t gamma, int32_t V,
-                       sv_sampler target, sv_sampler draft, const sv_requests* requests,
-                       uint64_t seed, uint64_t offset,
-                       const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
-                       uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
-                       double* out_overlap, uint32_t* out_accept_hist,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+// The sampling call. With use_scratch the workspace is this device's static
+// scratch array (spec_verify_sample_noalloc) instead of the caller's.
+int sample_impl(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                const int32_t* draft_tokens, const int32_t* banned_ids, int32_t n_banned,
+                int32_t B, int32_t gamma, int32_t V, sv_sampler target, sv_sampler draft,
+                const sv_requests* requests, uint64_t seed, uint64_t offset,
+                const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
+                uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
+                double* out_overlap, uint32_t* out_accept_hist, void* workspace,
+                size_t workspace_bytes, bool use_scratch, void* stream) {
   if (!target_logits || !draft_logits || !draft_tokens || !out_tokens || !out_num_accepted)
     return SV_EINVAL;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
@@ -191,6 +199,12 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
   if (((uintptr_t)target_logits % es) || ((uintptr_t)draft_logits % es)) return SV_EINVAL;
   Layout L;
   if (!layout(B, gamma, V, &L)) return SV_ESIZE;
+  if (use_scratch) {
+    if (L.total > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ESCRATCH;
+    const int rc = scratch_ptr(&workspace);
+    if (rc != SV_OK) return rc;
+    workspace_bytes = SV_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || ((uintptr_t)workspace % WS_ALIGN) || workspace_bytes < L.total)
     return SV_EWORKSPACE;
 
@@ -285,6 +299,60 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
     if (sv::launch_overlap(a, bf16, B * gamma, st)) return SV_EHIP;
   }
   return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
+  Layout L;
+  if (!layout(B, gamma, V, &L)) return 0;
+  return L.total;
+}
+
+const char* spec_verify_strerror(int status) {
+  switch (status) {
+    case SV_OK: return "success";
+    case SV_EINVAL: return "invalid argument (null pointer, size or sampler setting)";
+    case SV_EDTYPE: return "unsupported dtype (expected SV_F32 or SV_BF16)";
+    case SV_EWORKSPACE: return "workspace missing or smaller than spec_verify_workspace_bytes()";
+    case SV_ESIZE: return "sizes exceed the supported index ranges";
+    case SV_EHIP: return "HIP launch or runtime error";
+    case SV_ESCRATCH:
+      return "sizes need more workspace than spec_verify_sample_noalloc's static scratch holds";
+    default: return "unknown status";
+  }
+}
+
+int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                       const int32_t* draft_tokens, const int32_t* banned_ids,
+                       int32_t n_banned, int32_t B, int32_t gamma, int32_t V,
+                       sv_sampler target, sv_sampler draft, const sv_requests* requests,
+                       uint64_t seed, uint64_t offset,
+                       const double* uniforms, int32_t* out_tokens, int32_t* out_num_accepted,
+                       uint32_t* out_flags, float* out_target_lse, float* out_draft_lse,
+                       double* out_overlap, uint32_t* out_accept_hist,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return sample_impl(target_logits, draft_logits, dtype, draft_tokens, banned_ids, n_banned, B,
+                     gamma, V, target, draft, requests, seed, offset, uniforms, out_tokens,
+                     out_num_accepted, out_flags, out_target_lse, out_draft_lse, out_overlap,
+                     out_accept_hist, workspace, workspace_bytes, false, stream);
+}
+
+int spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits,
+                               sv_dtype dtype, const int32_t* draft_tokens,
+                               const int32_t* banned_ids, int32_t n_banned, int32_t B,
+                               int32_t gamma, int32_t V, sv_sampler target, sv_sampler draft,
+                               const sv_requests* requests, uint64_t seed, uint64_t offset,
+                               const double* uniforms, int32_t* out_tokens,
+                               int32_t* out_num_accepted, uint32_t* out_flags,
+                               float* out_target_lse, float* out_draft_lse, double* out_overlap,
+                               uint32_t* out_accept_hist, void* stream) {
+  return sample_impl(target_logits, draft_logits, dtype, draft_tokens, banned_ids, n_banned, B,
+                     gamma, V, target, draft, requests, seed, offset, uniforms, out_tokens,
+                     out_num_accepted, out_flags, out_target_lse, out_draft_lse, out_overlap,
+                     out_accept_hist, nullptr, 0, true, stream);
 }
 
 int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t* draft_tokens,

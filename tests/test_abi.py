@@ -43,7 +43,7 @@ def test_binding_names_match_header():
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.spec_verify_strerror(code)
     assert b"unknown" in lib.spec_verify_strerror(42)
 
@@ -137,6 +137,24 @@ def test_history_bound(lib):
     assert _sample(lib, requests=ctypes.byref(neg), **ok) == L.SV_EINVAL
     nolist = L.SvRequests(None, None, None, None, 0, None, 5, None, None)
     assert _sample(lib, requests=ctypes.byref(nolist), **ok) == L.SV_EINVAL
+
+
+def test_noalloc_rejects_sizes_beyond_the_scratch(lib):
+    """spec_verify_sample_noalloc validates like spec_verify_sample and rejects
+    sizes whose workspace exceeds its static scratch, before touching a device."""
+    from lossless_draft_verification_sample_amd import _lib as L
+    S = L.SvSampler(1.0, 0, 1.0)
+    na = lib.spec_verify_sample_noalloc
+
+    def call(B, gamma, V, target=FAKE):
+        return na(target, FAKE, L.SV_BF16, FAKE, None, 0, B, gamma, V, S, S, None, 0, 0, None,
+                  FAKE, FAKE, None, None, None, None, None, None)
+    assert lib.spec_verify_workspace_bytes(8192, 8, 1 << 20) > L.SV_NOALLOC_SCRATCH_BYTES
+    assert call(8192, 8, 1 << 20) == L.SV_ESCRATCH
+    assert call(8192, 8, 1 << 20, target=None) == L.SV_EINVAL   # argument checks come first
+    assert call(0, 8, 1000) == L.SV_EINVAL
+    assert lib.spec_verify_workspace_bytes(128, 8, 151936) <= L.SV_NOALLOC_SCRATCH_BYTES
+    assert b"scratch" in lib.spec_verify_strerror(L.SV_ESCRATCH)
 
 
 def test_greedy_argument_errors(lib):
