@@ -183,10 +183,10 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
  *                    sum_x min(p_i(x), q_i(x)) = 1 - TV(p_i, q_i) of target row
  *                    i and draft row i after every sampler transform; with x_i
  *                    drawn from q_i it is the probability that proposal i is
- *                    accepted once the walk reaches it ("Drafters and
- *                    Speculative Decoding", sections "Confidence and
- *                    verification admission" and "Accepted length is not
- *                    speed"). 0 when either row is empty; unspecified for a
+ *                    accepted once the walk reaches it ("Speculative
+ *                    Decoding - Turn guesses into parallel work", sections
+ *                    "Confidence and verification admission" and "Accepted
+ *                    length is not speed"). 0 when either row is empty; unspecified for a
  *                    request flagged SV_FLAG_NONFINITE. Computing it reads the
  *                    rows 0..gamma-1 once more (only the kept groups of the
  *                    other row when one of the two is truncated).
@@ -258,10 +258,11 @@ int spec_verify_greedy(const void* target_logits, sv_dtype dtype, const int32_t*
                        int32_t* out_num_accepted, uint32_t* out_flags,
                        uint32_t* out_accept_hist, void* stream);
 
-/* Chain KV-commit metadata of one verification round ("Drafters and
- * Speculative Decoding: Useful Tokens, Correct State", sections "Committed
- * tokens versus cached states" and "Committing state after rejection"), from
- * the outputs of spec_verify_sample or spec_verify_greedy, on the same stream.
+/* Chain KV-commit metadata of one verification round ("Speculative Decoding -
+ * Turn guesses into parallel work", section "Committed tokens versus cached
+ * states"; "Drafters and Speculative Decoding: Useful Tokens, Correct State",
+ * section "Committing state after rejection"), from the outputs of
+ * spec_verify_sample or spec_verify_greedy, on the same stream.
  * gamma_b [B] (device) gives each request's number of proposals as in
  * sv_requests (NULL: all gamma); below, gamma stands for gamma_b[b].
  * Convention: before the round request b has kv_len[b] = K materialised target

@@ -1,6 +1,7 @@
-// Chain KV-commit metadata after one verification round ("Drafters and
-// Speculative Decoding: Useful Tokens, Correct State", sections "Committed
-// tokens versus cached states" and "Committing state after rejection").
+// Chain KV-commit metadata after one verification round ("Speculative
+// Decoding - Turn guesses into parallel work", section "Committed tokens versus
+// cached states"; "Drafters and Speculative Decoding: Useful Tokens, Correct
+// State", section "Committing state after rejection").
 //
 // Convention: before the round request b has kv_len[b] = K materialised target
 // KV rows and its last committed token (the anchor) is pending. The target pass

@@ -1,12 +1,13 @@
 // Per-position overlap of the target and draft distributions of a request:
 // alpha_i = sum_x min(p_i(x), q_i(x)) = 1 - TV(p_i, q_i), for i < gamma.
 //
-// "Drafters and Speculative Decoding: Useful Tokens, Correct State", section
+// "Speculative Decoding - Turn guesses into parallel work", section
 // "Confidence and verification admission": this overlap is the soft label of a
-// confidence head; with x drawn from q_i and the acceptance rule of section
-// "Sampling needs a correction rule" it is the probability that proposal i is
-// accepted once the walk reaches it ("Accepted length is not speed": the
-// conditional acceptance c_i).
+// confidence head; with x drawn from q_i and the acceptance rule of "Drafters
+// and Speculative Decoding: Useful Tokens, Correct State", section "Sampling
+// needs a correction rule", it is the probability that proposal i is accepted
+// once the walk reaches it (first page, section "Accepted length is not
+// speed": the conditional acceptance c_i).
 //
 // p_i and q_i are the sampler-transformed rows the walk compares (bans,
 // temperature, top-k, top-p), so a token contributes only when it is kept in

@@ -4,11 +4,12 @@ TEST INFRASTRUCTURE, like the rest of this package: only tests/,
 __graft_entry__.smoke() and bench.py's cpu_baseline leg may use it.
 
 Pages followed (cited by title and section):
-  [DRAFT] "Drafters and Speculative Decoding: Useful Tokens, Correct State",
+  [ATLAS] "Speculative Decoding - Turn guesses into parallel work",
           "Committed tokens versus cached states" (the logical token list and
           the processed KV length differ; a sampled correction or bonus is
-          committed before its KV row exists; the convention must be stated)
-          and "Committing state after rejection" (the running example: rows
+          committed before its KV row exists; the convention must be stated).
+  [DRAFT] "Drafters and Speculative Decoding: Useful Tokens, Correct State",
+          "Committing state after rejection" (the running example: rows
           through the accepted prefix are kept, the rejected suffix becomes
           invalid, the correction stays a pending anchor).
 

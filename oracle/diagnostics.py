@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE, like the rest of this package: only tests/,
 __graft_entry__.smoke() and bench.py's cpu_baseline leg may use it.
 
 Pages followed (cited by title and section):
-  [DRAFT] "Drafters and Speculative Decoding: Useful Tokens, Correct State":
+  [ATLAS] "Speculative Decoding - Turn guesses into parallel work":
           "Confidence and verification admission" (the soft label of a
           confidence head is the overlap 1 - TV(p_k, q_k) of the target and
           draft distributions at position k), "Read the benchmark contract"
@@ -12,7 +12,8 @@ Pages followed (cited by title and section):
           "Accepted length is not speed" (c_i, the acceptance probability at
           position i given that the earlier positions survived; survival
           a_j = c_0 ... c_j).
-  [DRAFT] "Sampling needs a correction rule": the worked three-token example,
+  [DRAFT] "Drafters and Speculative Decoding: Useful Tokens, Correct State",
+          "Sampling needs a correction rule": the worked three-token example,
           whose rejection mass 0.40 fixes the overlap 0.60.
 
 Parity status:
@@ -41,9 +42,9 @@ def overlap(p, q):
     """alpha = sum_x min(p(x), q(x)) = 1 - TV(p, q).
 
     With x drawn from q and accepted with probability min(1, p(x)/q(x)), the
-    acceptance probability is sum_x q(x) min(1, p(x)/q(x)) = alpha ([DRAFT]
-    "Confidence and verification admission"; "Sampling needs a correction
-    rule"). Summed with math.fsum (correctly rounded).
+    acceptance probability is sum_x q(x) min(1, p(x)/q(x)) = alpha ([ATLAS]
+    "Confidence and verification admission"; [DRAFT] "Sampling needs a
+    correction rule"). Summed with math.fsum (correctly rounded).
     """
     p = np.asarray(p, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
@@ -77,7 +78,7 @@ def position_overlaps(target, draft, target_sampler, draft_sampler, banned=None)
 
 def accepted_prefix_histogram(num_accepted, gamma):
     """counts[n] = number of requests whose walk accepted exactly n proposals,
-    n = 0..gamma ([DRAFT] "Read the benchmark contract")."""
+    n = 0..gamma ([ATLAS] "Read the benchmark contract")."""
     counts = np.zeros(gamma + 1, dtype=np.int64)
     for n in np.asarray(num_accepted).tolist():
         counts[int(n)] += 1
@@ -100,7 +101,7 @@ def prefix_length_law(alphas):
     """Law of the accepted length n of one request whose proposals are drawn
     from q_i, given the conditional acceptance probabilities c_i = alpha_i:
     P(n = k) = c_0 ... c_{k-1} (1 - c_k) for k < gamma and c_0 ... c_{gamma-1}
-    for k = gamma ([DRAFT] "Accepted length is not speed": survival is the
+    for k = gamma ([ATLAS] "Accepted length is not speed": survival is the
     product of the conditional acceptances)."""
     alphas = [float(a) for a in alphas]
     gamma = len(alphas)
