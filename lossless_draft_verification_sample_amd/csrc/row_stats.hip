@@ -110,6 +110,12 @@ struct RowShared {
   float fscr[RS_THREADS / WAVE];
   uint32_t uscr[RS_THREADS / WAVE];
   int32_t iscr[RS_THREADS / WAVE];
+  // generic path: one 8-bit digit level of the radix selection
+  uint32_t rcnt[256];
+  unsigned long long rmh[256], rml[256];
+  uint32_t rsel_d, rsel_c;
+  unsigned long long rsel_h, rsel_l;
+  double rsel_target;
 };
 
 // Exact classification of one bf16 logit that fell outside the counted window.
@@ -228,9 +234,39 @@ __device__ __forceinline__ float gval(uint32_t k) {
   return f32_from_key(k);
 }
 
+// A mass m in [0, 1] in fixed point: m = (h + l * 2^-40) * 2^-40 up to 2^-80.
+// Sums of h and of l are exact 64-bit integer sums (no carry between them is
+// needed while fewer than 2^24 masses are added), so they do not depend on
+// the order of the additions.
+struct Fix {
+  unsigned long long h, l;
+};
+__device__ __forceinline__ Fix fix_of(double m) {
+  const double a = m * 0x1.0p40;
+  const double hf = floor(a);
+  Fix f;
+  f.h = (unsigned long long)hf;
+  f.l = (unsigned long long)((a - hf) * 0x1.0p40);
+  return f;
+}
+__device__ __forceinline__ Fix fix_add(Fix a, Fix b) {
+  a.h += b.h;
+  a.l += b.l;
+  return a;
+}
+__device__ __forceinline__ double fix_val(Fix f) {
+  return (double)f.h * 0x1.0p-40 + (double)f.l * 0x1.0p-80;
+}
+// Rows with fewer elements than this take the radix selection (exact
+// fixed-point sums); longer ones the bisection.
+constexpr int RADIX_MAX_V = 1 << 24;
+
+// Not inlined: its registers stay out of the count-histogram path's
+// allocation (every bf16 row takes that path; only fp32 rows and rare bf16
+// rows come here).
 template <typename Elem>
-__device__ __forceinline__ void row_generic(const Elem* rowp, int V, const SamplerDev s, const GenericCtx& g,
-                            RowShared& sh, RowStat& out) {
+__device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const SamplerDev s,
+                                            const GenericCtx g, RowShared& sh, RowStat out) {
   const double c2 = 1.4426950408889634 / (double)s.temperature;  // log2(e) / T
   // pass 1: max, min, count and the exp-sum against per-lane integer references
   float mx = -INFINITY, mn = INFINITY;
@@ -263,7 +299,7 @@ __device__ __forceinline__ void row_generic(const Elem* rowp, int V, const Sampl
     out.lse = -INFINITY;
     out.flags |= FLAG_EMPTY;
     out.path = 1u;
-    return;
+    return out;
   }
   double Z = block_sum<RS_THREADS>(
       ref > -INFINITY ? ldexp(acc, (int)fmax(ref - rmax, -2000.0)) : 0.0, sh.dscr);
@@ -287,7 +323,148 @@ __device__ __forceinline__ void row_generic(const Elem* rowp, int V, const Sampl
   };
   float tau = -INFINITY;
   bool trunc = false;
-  if (s.top_k > 0 && (uint32_t)s.top_k < cnt) {
+  if (V < RADIX_MAX_V && ((s.top_k > 0 && (uint32_t)s.top_k < cnt) || s.top_p < 1.0f)) {
+    // Radix selection over the order-preserving keys, most significant 8-bit
+    // digit first: one pass over the row per digit (2 for bf16 keys, 4 for
+    // fp32). Each pass counts, per digit value, the admissible elements whose
+    // higher digits equal the part of the threshold fixed so far (and the
+    // fixed-point sum of their masses exp(z/T) relative to 2^rmax); wave 0 then
+    // picks the digit where the running total from the top reaches what is
+    // needed. Top-k: the k-th largest key; top-p (after top-k, over keys at or
+    // above its cut): the largest key whose mass at or above it reaches
+    // top_p * Z. Counts and fixed-point sums are exact, so the result does not
+    // depend on the order of the LDS additions.
+    constexpr int KB = sizeof(Elem) == 2 ? 16 : 32;
+    auto level = [&](int shift, uint32_t prefix, uint32_t floor_key, bool cnt_on) {
+      if (threadIdx.x < 256) {
+        sh.rcnt[threadIdx.x] = 0u;
+        sh.rmh[threadIdx.x] = 0ull;
+        sh.rml[threadIdx.x] = 0ull;
+      }
+      __syncthreads();
+      for_each_elem<Elem>(rowp, V, [&](float z, int id) {
+        if (!g.admissible(z, id)) return;
+        z = g.value(z, id);
+        const uint32_t key = gkey<Elem>(z);
+        if (key < floor_key) return;
+        if (shift + 8 < KB && (key >> (shift + 8)) != prefix) return;
+        const uint32_t d = (key >> shift) & 255u;
+        if (cnt_on) atomicAdd(&sh.rcnt[d], 1u);
+        const Fix f = fix_of(exp2((double)z * c2 - rmax));
+        atomicAdd(&sh.rmh[d], f.h);
+        atomicAdd(&sh.rml[d], f.l);
+      });
+      __syncthreads();
+    };
+    // Wave 0 scans the digits from the top (lane l takes 255 - 4l - j,
+    // j = 0..3) for the first one where the running count reaches `need`
+    // (count mode) or above + the running mass reaches `target` (mass mode;
+    // a negative target, given at the first level only, means top_p times that
+    // level's total mass, i.e. the whole set's); if rounding leaves every digit
+    // short, the lowest digit with elements. It writes the digit, the count and
+    // mass of the level's elements above it, and the target it used.
+    auto pick = [&](bool mass_mode, uint32_t need, Fix above, double target, float top_p) {
+      if (threadIdx.x < WAVE) {
+        const int l = threadIdx.x;
+        uint32_t c[4];
+        Fix m[4];
+        uint32_t lc = 0u;
+        Fix lm = {0ull, 0ull};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 255 - 4 * l - j;
+          c[j] = sh.rcnt[d];
+          m[j].h = sh.rmh[d];
+          m[j].l = sh.rml[d];
+          lc += c[j];
+          lm = fix_add(lm, m[j]);
+        }
+        const uint32_t ic = wave_incl_scan(lc);
+        const unsigned long long ih = wave_incl_scan(lm.h), il = wave_incl_scan(lm.l);
+        if (target < 0.0) {
+          Fix tot;
+          tot.h = (unsigned long long)__shfl(ih, WAVE - 1, WAVE);
+          tot.l = (unsigned long long)__shfl(il, WAVE - 1, WAVE);
+          target = (double)top_p * fix_val(fix_add(above, tot));
+        }
+        uint32_t rc = ic - lc;
+        Fix rm;
+        rm.h = ih - lm.h;
+        rm.l = il - lm.l;
+        int sel = -1, last = -1;
+        uint32_t selc = 0u, lastc = 0u;
+        Fix selm = {0ull, 0ull}, lastm = {0ull, 0ull};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool nz = c[j] != 0u || (m[j].h | m[j].l) != 0ull;
+          if (nz) {
+            const bool reached = mass_mode ? fix_val(fix_add(fix_add(above, rm), m[j])) >= target
+                                           : rc + c[j] >= need;
+            if (reached && sel < 0) {
+              sel = 255 - 4 * l - j;
+              selc = rc;
+              selm = rm;
+            }
+            last = 255 - 4 * l - j;
+            lastc = rc;
+            lastm = rm;
+          }
+          rc += c[j];
+          rm = fix_add(rm, m[j]);
+        }
+        const uint64_t bs = __ballot(sel >= 0), bl = __ballot(last >= 0);
+        const int who = bs ? __ffsll((unsigned long long)bs) - 1 : (bl ? 63 - __clzll((long long)bl) : 0);
+        if (l == 0) sh.rsel_target = target;
+        if (l == who) {
+          const bool found = sel >= 0;
+          sh.rsel_d = (uint32_t)(found ? sel : (last >= 0 ? last : 0));
+          sh.rsel_c = found ? selc : lastc;
+          sh.rsel_h = found ? selm.h : lastm.h;
+          sh.rsel_l = found ? selm.l : lastm.l;
+        }
+      }
+      __syncthreads();
+    };
+    uint32_t floor_key = 0u;
+    if (s.top_k > 0 && (uint32_t)s.top_k < cnt) {
+      uint32_t need = (uint32_t)s.top_k, prefix = 0u;
+      Fix above = {0ull, 0ull}, zk = {0ull, 0ull};
+      for (int shift = KB - 8; shift >= 0; shift -= 8) {
+        level(shift, prefix, 0u, true);
+        pick(false, need, above, 0.0, 1.0f);
+        const uint32_t d = sh.rsel_d;
+        need -= sh.rsel_c;
+        above = fix_add(above, Fix{sh.rsel_h, sh.rsel_l});
+        if (shift == 0) zk = fix_add(above, Fix{sh.rmh[d], sh.rml[d]});
+        prefix = (prefix << 8) | d;
+        __syncthreads();   // the digit's bins are read before the next level clears them
+      }
+      floor_key = prefix;
+      tau = gval<Elem>(prefix);
+      trunc = true;
+      Z = fix_val(zk);
+    }
+    if (s.top_p < 1.0f) {
+      uint32_t prefix = 0u;
+      Fix above = {0ull, 0ull}, zp = {0ull, 0ull};
+      // top_p times the kept set's mass after top-k; otherwise times the
+      // first level's total, which the first pick computes
+      double target = trunc ? (double)s.top_p * Z : -1.0;
+      for (int shift = KB - 8; shift >= 0; shift -= 8) {
+        level(shift, prefix, floor_key, false);
+        pick(true, 0u, above, target, s.top_p);
+        target = sh.rsel_target;
+        const uint32_t d = sh.rsel_d;
+        above = fix_add(above, Fix{sh.rsel_h, sh.rsel_l});
+        if (shift == 0) zp = fix_add(above, Fix{sh.rmh[d], sh.rml[d]});
+        prefix = (prefix << 8) | d;
+        __syncthreads();
+      }
+      tau = gval<Elem>(prefix);
+      trunc = true;
+      Z = fix_val(zp);
+    }
+  } else if (s.top_k > 0 && (uint32_t)s.top_k < cnt) {
     // largest key t with count(z >= value(t)) >= k
     uint32_t lo = gkey<Elem>(mn), hi = gkey<Elem>(mx) + 1u;
     while (hi - lo > 1u) {
@@ -301,7 +478,7 @@ __device__ __forceinline__ void row_generic(const Elem* rowp, int V, const Sampl
     trunc = true;
     Z = mass_ge(tau);
   }
-  if (s.top_p < 1.0f) {
+  if (V >= RADIX_MAX_V && s.top_p < 1.0f) {
     // largest key t with mass(z >= value(t)) >= top_p * Z (within the top-k set)
     const double target = (double)s.top_p * Z;
     uint32_t lo = gkey<Elem>(trunc ? fmaxf(tau, mn) : mn), hi = gkey<Elem>(mx) + 1u;
@@ -324,6 +501,7 @@ __device__ __forceinline__ void row_generic(const Elem* rowp, int V, const Sampl
   out.tau = trunc ? tau : -INFINITY;
   out.lse = rmax * 0.6931471805599453 + log(Z);
   out.path = 1u;
+  return out;
 }
 
 // ------------------------------------------------------------------ histogram epilogue
@@ -940,7 +1118,7 @@ void row_stats_kernel(RowStatsArgs a) {
       g.ptab = sh.hist + HT_SLOTS;
     }
     out.flags &= ~FLAG_EMPTY;
-    row_generic<Elem>(rowp, V, s, g, sh, out);
+    out = row_generic<Elem>(rowp, V, s, g, sh, out);
   }
 
   if (u_pending) emit_u();

@@ -20,6 +20,7 @@ own workloads need models and prompt sets, so these synthetic rows stand in):
   c5   B=128, gamma=8, V=151936, bf16, target ~ N(0, 3^2) plus Zipf boosts,
        draft = target + N(0, 1), T=0.8, top-p 0.9, 64 distinct banned ids per
        request applied to p and q.
+  c5f32  c5's recipe and seed with float32 logits (not rounded to bf16).
 Values are drawn in float32 from NumPy's PCG64 (default_rng(seed)), draft rows
 add their noise to the unrounded target row, and bf16 rows are rounded to
 nearest-even from float32.
@@ -62,6 +63,9 @@ CONFIGS = {
                  match_prob=0.7, seed=1004),
     "c5": Config("c5", "sample", 128, 8, 151936, "bf16", 3.0, 1.0, boost="zipf",
                  temperature=0.8, top_p=0.9, n_banned=64, seed=1005),
+    # c5's recipe with float32 logits (not rounded to bf16): the generic path
+    "c5f32": Config("c5f32", "sample", 128, 8, 151936, "f32", 3.0, 1.0, boost="zipf",
+                    temperature=0.8, top_p=0.9, n_banned=64, seed=1005),
 }
 
 

@@ -1,5 +1,6 @@
-"""Whole-batch parity at full size: every request of the c2, c3a, c3b and c5
-workloads, at several Philox offsets, against the float64 oracle.
+"""Whole-batch parity at full size: every request of the c2, c3a, c3b, c5 and
+c5f32 (c5 with float32 logits) workloads, at several Philox offsets, against
+the float64 oracle.
 
 "Speculative Decoding - Turn guesses into parallel work", section
 "Implementation roadmap and tests", asks for more than a few matching outputs.
@@ -23,7 +24,8 @@ from tests.oracle_pool import OraclePool
 
 pytestmark = pytest.mark.gpu
 
-OFFSETS = {"c2": (0, 1, 2, 3, 4, 5, 6, 7), "c3a": (0, 1, 2), "c3b": (0, 1, 2), "c5": (0, 1, 2)}
+OFFSETS = {"c2": (0, 1, 2, 3, 4, 5, 6, 7), "c3a": (0, 1, 2), "c3b": (0, 1, 2), "c5": (0, 1, 2),
+           "c5f32": (0, 1)}
 
 
 @pytest.fixture(scope="module", autouse=True)

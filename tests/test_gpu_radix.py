@@ -1,0 +1,78 @@
+"""The generic path's top-k and top-p cuts (radix selection over the
+order-preserving keys, one pass per 8-bit digit) against the oracle, at the
+full c5 vocabulary: fp32 rows (32-bit keys, four digits) and bf16 rows that
+leave the counted window (16-bit keys, two digits); every sampler shape
+(top-p alone, top-k alone, both, top-k = 1), exact ties at the cut, and rows
+whose kept values are all negative. Same bar as the other parity tests:
+tokens, accepted counts and flags bit-exact outside the 1e-10 decision band,
+lse within 1e-5."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLERS = [(0.8, 0, 0.9), (0.7, 50, 1.0), (1.0, 40, 0.95), (1.3, 1, 1.0), (0.5, 0, 0.5),
+            (1.0, 3000, 0.999)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import lossless_draft_verification_sample_amd._lib as L
+    L.load()
+
+
+def _check(wl, samp, where, seed=3, offset=9):
+    cfg = wl.cfg
+    xs = pu.oracle_proposals(wl, samp)
+    got = pu.run_gpu_sample(wl, xs, tsamp=samp, dsamp=samp, seed=seed, offset=offset)
+    u = pu.philox_uniforms(seed, offset, cfg.B, cfg.gamma)
+    ref = pu.run_oracle_sample(wl, xs, u, range(cfg.B), tsamp=samp, dsamp=samp)
+    nb = pu.compare_sample(got, ref, range(cfg.B), where=where)
+    assert nb <= 1, where
+
+
+@pytest.mark.parametrize("samp", SAMPLERS)
+def test_fp32_full_vocabulary(samp):
+    wl = pu.make("c5f32", B=3, gamma=3, seed=400)
+    _check(wl, samp, f"fp32 {samp}")
+
+
+@pytest.mark.parametrize("samp", [(1.0, 1000, 1.0), (1.0, 0, 0.7), (1.0, 700, 0.9)])
+def test_fp32_ties_at_the_cut(samp):
+    # 40 distinct values, each shared by thousands of tokens: the cuts fall
+    # inside runs of equal keys
+    wl = pu.make("c5f32", B=2, gamma=2, seed=401)
+    rng = np.random.default_rng(5)
+    levels = np.sort(rng.normal(0, 2, 40)).astype(np.float32)
+    wl.target = levels[rng.integers(0, 40, wl.target.shape)]
+    wl.draft = levels[rng.integers(0, 40, wl.draft.shape)]
+    _check(wl, samp, f"fp32 ties {samp}")
+
+
+@pytest.mark.parametrize("samp", [(0.8, 0, 0.9), (1.0, 25, 1.0)])
+def test_fp32_all_negative_rows(samp):
+    wl = pu.make("c5f32", B=2, gamma=2, seed=402)
+    wl.target = (wl.target - np.float32(80.0)).astype(np.float32)
+    wl.draft = (wl.draft - np.float32(80.0)).astype(np.float32)
+    _check(wl, samp, f"fp32 negative {samp}")
+
+
+@pytest.mark.parametrize("samp", SAMPLERS)
+def test_bf16_rows_on_the_generic_path(samp):
+    # one logit of 700 in every row leaves the counted window (|z| < 512)
+    from lossless_draft_verification_sample_amd import synth
+    wl = pu.make("c5", B=3, gamma=3, seed=403)
+    t, d = wl.target.copy(), wl.draft.copy()
+    t[:, :, 777] = -700.0
+    d[:, :, 778] = -700.0
+    wl.target_bits = synth.f32_to_bf16_bits(t)
+    wl.draft_bits = synth.f32_to_bf16_bits(d)
+    wl.target = synth.bf16_bits_to_f32(wl.target_bits)
+    wl.draft = synth.bf16_bits_to_f32(wl.draft_bits)
+    _check(wl, samp, f"bf16 generic {samp}")
