@@ -871,6 +871,24 @@ void row_stats_kernel(RowStatsArgs a) {
   const Elem* rowp = is_target
                          ? (const Elem*)a.target + ((int64_t)b * G1 + i) * (int64_t)a.V
                          : (const Elem*)a.draft + ((int64_t)b * a.gamma + (i - G1)) * (int64_t)a.V;
+  const int V = a.V;
+  const int pi = is_target ? i : i - G1;
+  // draft rows take the draft ban list when there is one
+  const bool dbans = MIXED && !is_target && a.req.banned_d;
+  const int nb_all = dbans ? a.req.n_banned_d : (a.banned ? a.n_banned : 0);
+  const int32_t* bl_all = nb_all == 0 ? nullptr
+                          : dbans ? a.req.banned_d + (int64_t)b * a.req.n_banned_d
+                                  : a.banned + (int64_t)b * a.n_banned;
+  // repetition penalty of the row: its history and the proposals before it
+  const int H = (MIXED && a.req.history) ? a.req.n_history : 0;
+  const int32_t* hist = H ? a.req.history + (int64_t)b * a.req.n_history : nullptr;
+  const int32_t* props = a.draft_tokens + (int64_t)b * a.gamma;
+  // The row's first ban and penalty entries and its proposal token are loaded
+  // before the request's settings are known (every index here is in range),
+  // so that in a mixed batch these loads do not wait for the settings.
+  const int32_t ban0_all = tid < nb_all ? bl_all[tid] : -1;
+  const int32_t pen0_all = (MIXED && tid < H + pi) ? pen_id(hist, H, props, tid) : -1;
+  const int32_t xprop_all = pi < a.gamma ? props[pi] : -1;
   ReqInfo rq;
   if constexpr (MIXED) {
     rq = request_info(a.req, b, a.gamma, a.st, a.sd);
@@ -882,35 +900,24 @@ void row_stats_kernel(RowStatsArgs a) {
     rq.bad = false;
   }
   const SamplerDev s = is_target ? rq.st : rq.sd;
-  const int V = a.V;
-  const int pi = is_target ? i : i - G1;
   // rows the request does not use: beyond its draft length, the draft rows of
   // a greedy request, every row of a request with settings out of range
   const bool used = !MIXED || (!rq.bad && pi <= rq.g && (is_target ? true : !rq.greedy && pi < rq.g));
   const bool greedy_row = MIXED && used && rq.greedy;   // a target row: its argmax
-  // draft rows take the draft ban list when there is one
-  const bool dbans = MIXED && !is_target && a.req.banned_d;
-  const int nb = !used ? 0 : dbans ? a.req.n_banned_d : (a.banned ? a.n_banned : 0);
-  const int32_t* bl = nb == 0 ? nullptr
-                      : dbans ? a.req.banned_d + (int64_t)b * a.req.n_banned_d
-                              : a.banned + (int64_t)b * a.n_banned;
+  const int nb = used ? nb_all : 0;
+  const int32_t* bl = nb == 0 ? nullptr : bl_all;
+  const int32_t ban0 = used ? ban0_all : -1;
   // the proposal this row scores (none for the bonus row) and its logit
-  const int32_t xprop = (used && pi < (MIXED ? rq.g : a.gamma))
-                             ? a.draft_tokens[(int64_t)b * a.gamma + pi] : -1;
+  const int32_t xprop = (used && pi < (MIXED ? rq.g : a.gamma)) ? xprop_all : -1;
   const bool xvalid = xprop >= 0 && xprop < V;
   const float zx = (tid == 0 && xvalid) ? elem_value<Elem>(rowp[xprop]) : 0.0f;
-  const int32_t ban0 = tid < nb ? bl[tid] : -1;
   if (tid == 0) {
     sh.xban = 0u;
     sh.xpen = 0u;
   }
-  // repetition penalty of the row: its history and the proposals before it
   const float theta = is_target ? rq.pt : rq.pd;
-  const int H = (MIXED && a.req.history) ? a.req.n_history : 0;
   const int npen = (MIXED && used && theta != 1.0f) ? H + pi : 0;
-  const int32_t* hist = H ? a.req.history + (int64_t)b * a.req.n_history : nullptr;
-  const int32_t* props = a.draft_tokens + (int64_t)b * a.gamma;
-  const int32_t pen0 = tid < npen ? pen_id(hist, H, props, tid) : -1;   // loaded early
+  const int32_t pen0 = tid < npen ? pen0_all : -1;
   // Target row i also draws uniform slot i of its request for the acceptance
   // walk (slot gamma: the final draw). Lane 0 of the last wave computes it,
   // in the bf16 stream while its first loads are in flight.

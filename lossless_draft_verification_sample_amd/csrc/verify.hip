@@ -153,17 +153,25 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b, int gq) {
   double p = 0.0, q = 0.0, u = 0.0;
   int32_t x = -1;
   RowStat t{}, d{};
-  if (lane <= g) u = a.uniforms[(int64_t)b * G1 + lane];
-  if (lane <= gq) {
+  // loads for every position of the call (all in range), so that they need
+  // not wait for a mixed batch's per-request draft length; then masked by it
+  if (lane <= g) {
+    u = a.uniforms[(int64_t)b * G1 + lane];
     t = st[lane];
+  }
+  if (lane < g) {
+    d = st[G1 + lane];
+    x = a.draft_tokens[(int64_t)b * g + lane];
+  }
+  if (lane <= gq) {
     rf |= t.flags;
     p = t.px;
   }
   if (lane < gq) {
-    d = st[G1 + lane];
     rf |= d.flags;
     q = d.px;
-    x = a.draft_tokens[(int64_t)b * g + lane];
+  } else {
+    x = -1;
   }
   rf &= FLAG_NONFINITE | FLAG_EMPTY;
 #pragma unroll
