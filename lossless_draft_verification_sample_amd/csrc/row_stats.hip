@@ -173,10 +173,14 @@ __device__ __forceinline__ float elem_value<float>(float e) {
   return e;
 }
 
-// Calls f(z, id) for every element of the row, 16-byte vector loads in the body.
+// Calls f(z, id) for every element of the row: 16-byte vector loads in the
+// body, software-pipelined (each thread's next GEN_U chunks are in flight
+// while the current ones are processed).
+constexpr int GEN_U = 2;
 template <typename Elem, typename F>
 __device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
   constexpr int PER = 16 / sizeof(Elem);
+  constexpr int STEP = RS_THREADS * GEN_U;
   const int tid = threadIdx.x;
   const uintptr_t addr = (uintptr_t)rowp;
   int head = (int)(((16u - (addr & 15u)) & 15u) / sizeof(Elem));
@@ -186,19 +190,46 @@ __device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
   if (tid < head) f(elem_value<Elem>(rowp[tid]), tid);
   if (tid < V - tail0) f(elem_value<Elem>(rowp[tail0 + tid]), tail0 + tid);
   const u32x4* body = (const u32x4*)(rowp + head);
-  for (int k = tid; k < nchunk; k += RS_THREADS) {
-    const u32x4 v = body[k];
-    const int id0 = head + k * PER;
-    if constexpr (sizeof(Elem) == 2) {
+  u32x4 va[GEN_U], vb[GEN_U];
+  auto ld = [&](u32x4(&v)[GEN_U], int k0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f(bf16_to_f32(v[j] & 0xFFFFu), id0 + 2 * j);
-        f(bf16_to_f32(v[j] >> 16), id0 + 2 * j + 1);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f(__uint_as_float(v[j]), id0 + j);
+    for (int u = 0; u < GEN_U; ++u) {
+      const int k = k0 + u * RS_THREADS;
+      if (k < nchunk) v[u] = body[k];
     }
+  };
+  auto run = [&](const u32x4(&v)[GEN_U], int k0) {
+#pragma unroll
+    for (int u = 0; u < GEN_U; ++u) {
+      const int k = k0 + u * RS_THREADS;
+      if (k >= nchunk) continue;
+      const int id0 = head + k * PER;
+      if constexpr (sizeof(Elem) == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = v[u][j];
+          f(bf16_to_f32(w & 0xFFFFu), id0 + 2 * j);
+          f(bf16_to_f32(w >> 16), id0 + 2 * j + 1);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = v[u][j];
+          f(__uint_as_float(w), id0 + j);
+        }
+      }
+    }
+  };
+  int k0 = tid;
+  if (k0 < nchunk) ld(va, k0);
+  while (k0 < nchunk) {
+    if (k0 + STEP < nchunk) ld(vb, k0 + STEP);
+    run(va, k0);
+    k0 += STEP;
+    if (k0 >= nchunk) break;
+    if (k0 + STEP < nchunk) ld(va, k0 + STEP);
+    run(vb, k0);
+    k0 += STEP;
   }
 }
 
@@ -232,6 +263,31 @@ __device__ __forceinline__ float gval(uint32_t k) {
     return f32_from_key((k32 & 0x80000000u) ? k32 : (k32 | 0xFFFFu));
   }
   return f32_from_key(k);
+}
+
+// 2^x in fp64 for x <= about 0 (masses relative to the row's reference), to
+// about an ulp: x = k + r with k = rint(x) and r exact (|r| <= 1/2); r ln 2 in
+// double-double through an fma with ln 2 split into a head and a tail; e^t - 1
+// from its degree-13 Taylor polynomial (|t| <= 0.35, remainder below 1e-17).
+__device__ __forceinline__ double exp2_neg(double x) {
+  x = fmax(x, -1100.0);                       // 2^-1100 is 0 in fp64
+  const double k = rint(x);
+  const double r = x - k;
+  const double t = fma(r, 0x1.62e42fefa39efp-1, r * 0x1.abc9e3b39803fp-56);
+  double q = fma(t, 1.0 / 6227020800.0, 1.0 / 479001600.0);
+  q = fma(q, t, 1.0 / 39916800.0);
+  q = fma(q, t, 1.0 / 3628800.0);
+  q = fma(q, t, 1.0 / 362880.0);
+  q = fma(q, t, 1.0 / 40320.0);
+  q = fma(q, t, 1.0 / 5040.0);
+  q = fma(q, t, 1.0 / 720.0);
+  q = fma(q, t, 1.0 / 120.0);
+  q = fma(q, t, 1.0 / 24.0);
+  q = fma(q, t, 1.0 / 6.0);
+  q = fma(q, t, 0.5);
+  q = fma(q, t, 1.0);
+  q *= t;                                     // e^t - 1
+  return ldexp(1.0 + q, (int)k);
 }
 
 // A mass m in [0, 1] in fixed point: m = (h + l * 2^-40) * 2^-40 up to 2^-80.
@@ -268,7 +324,11 @@ template <typename Elem>
 __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const SamplerDev s,
                                             const GenericCtx g, RowShared& sh, RowStat out) {
   const double c2 = 1.4426950408889634 / (double)s.temperature;  // log2(e) / T
-  // pass 1: max, min, count and the exp-sum against per-lane integer references
+  // A truncating sampler takes its cuts and the kept set's mass from the radix
+  // selection below, so the first pass needs no exp.
+  const bool radix_cut = V < RADIX_MAX_V && (s.top_k > 0 || s.top_p < 1.0f);
+  // pass 1: max, min, count and (without a radix cut) the exp-sum against
+  // per-lane integer references
   float mx = -INFINITY, mn = INFINITY;
   uint32_t cnt = 0, bad = 0;
   double ref = -INFINITY, acc = 0.0;
@@ -279,19 +339,23 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
     ++cnt;
     mn = fminf(mn, z);
     if (z > mx) mx = z;
+    if (radix_cut) return;
     const double e = (double)z * c2;
     if (e > ref) {
       const double nr = ceil(e);
       if (ref > -INFINITY) acc = ldexp(acc, (int)fmax(ref - nr, -2000.0));
       ref = nr;
     }
-    acc += exp2(e - ref);
+    acc += exp2_neg(e - ref);
   });
   mx = block_max<RS_THREADS>(mx, sh.fscr);
   mn = block_min<RS_THREADS>(mn, sh.fscr);
   cnt = block_sum<RS_THREADS>(cnt, sh.uscr);
   bad = block_max<RS_THREADS>(bad, sh.uscr);
-  const double rmax = block_max<RS_THREADS>(ref, sh.dscr);
+  // the reference exponent: ceil of the largest z / T in log2 units (what the
+  // per-lane references give)
+  const double rmax = radix_cut ? (mx > -INFINITY ? ceil((double)mx * c2) : -INFINITY)
+                                : block_max<RS_THREADS>(ref, sh.dscr);
   out.flags |= bad ? FLAG_NONFINITE : 0u;
   if (cnt == 0u) {
     out.m = -INFINITY;
@@ -301,15 +365,17 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
     out.path = 1u;
     return out;
   }
-  double Z = block_sum<RS_THREADS>(
-      ref > -INFINITY ? ldexp(acc, (int)fmax(ref - rmax, -2000.0)) : 0.0, sh.dscr);
+  double Z = radix_cut ? 0.0
+                       : block_sum<RS_THREADS>(
+                             ref > -INFINITY ? ldexp(acc, (int)fmax(ref - rmax, -2000.0)) : 0.0,
+                             sh.dscr);
   // mass (relative to 2^rmax) and count of the admissible values >= thr
   auto mass_ge = [&](float thr) -> double {
     double a = 0.0;
     for_each_elem<Elem>(rowp, V, [&](float z, int id) {
       if (!g.admissible(z, id)) return;
       z = g.value(z, id);
-      if (z >= thr) a += exp2((double)z * c2 - rmax);
+      if (z >= thr) a += exp2_neg((double)z * c2 - rmax);
     });
     return block_sum<RS_THREADS>(a, sh.dscr);
   };
@@ -343,14 +409,21 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
       }
       __syncthreads();
       for_each_elem<Elem>(rowp, V, [&](float z, int id) {
-        if (!g.admissible(z, id)) return;
-        z = g.value(z, id);
+        // without a penalty the key is known before the ban lookup, which
+        // only the elements of the current prefix then pay
+        if (g.ptab) {
+          if (!g.admissible(z, id)) return;
+          z = g.value(z, id);
+        } else if (!(z > -INFINITY && z < INFINITY)) {
+          return;
+        }
         const uint32_t key = gkey<Elem>(z);
         if (key < floor_key) return;
         if (shift + 8 < KB && (key >> (shift + 8)) != prefix) return;
+        if (!g.ptab && g.tab && ht_has(g.tab, id)) return;
         const uint32_t d = (key >> shift) & 255u;
         if (cnt_on) atomicAdd(&sh.rcnt[d], 1u);
-        const Fix f = fix_of(exp2((double)z * c2 - rmax));
+        const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
         atomicAdd(&sh.rmh[d], f.h);
         atomicAdd(&sh.rml[d], f.l);
       });
@@ -497,6 +570,9 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
     trunc = true;
     Z = zlo;
   }
+  // a radix-cut sampler that keeps everything (top-k at least the count,
+  // top-p 1): the first pass skipped the exp-sum
+  if (radix_cut && !trunc) Z = mass_ge(-INFINITY);
   out.m = mx;
   out.tau = trunc ? tau : -INFINITY;
   out.lse = rmax * 0.6931471805599453 + log(Z);
