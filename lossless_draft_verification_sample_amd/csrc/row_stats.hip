@@ -239,6 +239,13 @@ struct GenericCtx {
   const uint32_t* ptab;   // LDS hash set of the penalized ids, or nullptr
   float theta;            // their repetition penalty
   bool bf16;              // penalized values are rounded to bf16
+  // the raw ban list, its first entry for this thread, and which of this
+  // thread's entries (list index threadIdx.x + k * RS_THREADS, bit k) entered
+  // the set: every distinct valid id has exactly one owner
+  const int32_t* bl;
+  int nb;
+  int32_t ban0;
+  uint32_t own;
   __device__ __forceinline__ bool admissible(float z, int id) const {
     // finite and not banned; NaN fails both comparisons
     if (!(z > -INFINITY && z < INFINITY)) return false;
@@ -327,6 +334,20 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
   // A truncating sampler takes its cuts and the kept set's mass from the radix
   // selection below, so the first pass needs no exp.
   const bool radix_cut = V < RADIX_MAX_V && (s.top_k > 0 || s.top_p < 1.0f);
+  // Bans of a radix cut without a repetition penalty: the passes take every
+  // finite element and then remove the banned ones, each distinct id once by
+  // its owner thread, from the integer counts and fixed-point masses (exact),
+  // instead of a set lookup per element.
+  constexpr int BPT = (int)HT_MAX_IDS / RS_THREADS;   // list entries per thread
+  static_assert(BPT * RS_THREADS >= (int)HT_MAX_IDS, "ban entries per thread");
+  const bool sub_bans = radix_cut && g.tab && !g.ptab;
+  float zb[BPT];
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    zb[k] = __builtin_nanf("");
+    if (sub_bans && ((g.own >> k) & 1u))
+      zb[k] = elem_value<Elem>(rowp[k == 0 ? g.ban0 : g.bl[threadIdx.x + k * RS_THREADS]]);
+  }
   // pass 1: max, min, count and (without a radix cut) the exp-sum against
   // per-lane integer references
   float mx = -INFINITY, mn = INFINITY;
@@ -334,7 +355,7 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
   double ref = -INFINITY, acc = 0.0;
   for_each_elem<Elem>(rowp, V, [&](float z, int id) {
     if (z != z || z == INFINITY) bad = 1u;
-    if (!g.admissible(z, id)) return;
+    if (sub_bans ? !(z > -INFINITY && z < INFINITY) : !g.admissible(z, id)) return;
     z = g.value(z, id);
     ++cnt;
     mn = fminf(mn, z);
@@ -352,6 +373,26 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
   mn = block_min<RS_THREADS>(mn, sh.fscr);
   cnt = block_sum<RS_THREADS>(cnt, sh.uscr);
   bad = block_max<RS_THREADS>(bad, sh.uscr);
+  if (sub_bans) {
+    uint32_t bc = 0u;
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      if (zb[k] > -INFINITY && zb[k] < INFINITY) {
+        ++bc;
+        bm = fmaxf(bm, zb[k]);
+      }
+    }
+    cnt -= block_sum<RS_THREADS>(bc, sh.uscr);
+    if (block_max<RS_THREADS>(bm, sh.fscr) >= mx) {
+      // a banned token holds the maximum: one more pass, with lookups
+      float m2 = -INFINITY;
+      for_each_elem<Elem>(rowp, V, [&](float z, int id) {
+        if (g.admissible(z, id) && z > m2) m2 = z;
+      });
+      mx = block_max<RS_THREADS>(m2, sh.fscr);
+    }
+  }
   // the reference exponent: ceil of the largest z / T in log2 units (what the
   // per-lane references give)
   const double rmax = radix_cut ? (mx > -INFINITY ? ceil((double)mx * c2) : -INFINITY)
@@ -409,8 +450,9 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
       }
       __syncthreads();
       for_each_elem<Elem>(rowp, V, [&](float z, int id) {
-        // without a penalty the key is known before the ban lookup, which
-        // only the elements of the current prefix then pay
+        // with a penalty the set lookups come first (they change values);
+        // without one every finite element counts here and the banned ones
+        // are taken back out after the loop
         if (g.ptab) {
           if (!g.admissible(z, id)) return;
           z = g.value(z, id);
@@ -420,13 +462,29 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
         const uint32_t key = gkey<Elem>(z);
         if (key < floor_key) return;
         if (shift + 8 < KB && (key >> (shift + 8)) != prefix) return;
-        if (!g.ptab && g.tab && ht_has(g.tab, id)) return;
         const uint32_t d = (key >> shift) & 255u;
         if (cnt_on) atomicAdd(&sh.rcnt[d], 1u);
         const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
         atomicAdd(&sh.rmh[d], f.h);
         atomicAdd(&sh.rml[d], f.l);
       });
+      if (sub_bans) {
+        // the banned elements this level counted, taken back out (the bins
+        // wrap through zero at worst, and end exact)
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+          const float z = zb[k];
+          if (!(z > -INFINITY && z < INFINITY)) continue;
+          const uint32_t key = gkey<Elem>(z);
+          if (key < floor_key) continue;
+          if (shift + 8 < KB && (key >> (shift + 8)) != prefix) continue;
+          const uint32_t d = (key >> shift) & 255u;
+          if (cnt_on) atomicSub(&sh.rcnt[d], 1u);
+          const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
+          atomicAdd(&sh.rmh[d], 0ull - f.h);
+          atomicAdd(&sh.rml[d], 0ull - f.l);
+        }
+      }
       __syncthreads();
     };
     // Wave 0 scans the digits from the top (lane l takes 255 - 4l - j,
@@ -936,7 +994,7 @@ __device__ __forceinline__ void row_finish(const RowStatsArgs& a, int row, const
 // MIXED: per-request draft lengths, samplers (greedy requests included) and
 // draft ban lists; the plain variant carries none of that logic.
 template <typename Elem, bool MIXED>
-__global__ __launch_bounds__(RS_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(RS_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(Elem) == 2 ? 6 : 4)))
 void row_stats_kernel(RowStatsArgs a) {
   __shared__ RowShared sh;
   const int tid = threadIdx.x;
@@ -1185,13 +1243,13 @@ void row_stats_kernel(RowStatsArgs a) {
   if (generic) {
     __syncthreads();
     // the ban set moves into the (now free) histogram storage
-    GenericCtx g{nullptr, nullptr, theta, sizeof(Elem) == 2};
+    GenericCtx g{nullptr, nullptr, theta, sizeof(Elem) == 2, bl, nb, ban0, 0u};
     if (nb > 0 || (MIXED && npen > 0)) {
       for (uint32_t k = tid; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
       __syncthreads();
     }
     if (nb > 0) {
-      (void)ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
+      g.own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
       __syncthreads();
       g.tab = sh.hist;
     }
