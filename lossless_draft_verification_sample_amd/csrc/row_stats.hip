@@ -29,14 +29,17 @@
 // magnitude >= 2^9, more tiny values than the list holds, or a truncation cut
 // that falls among the tiny values is handed to the generic path.
 //
-// fp32 rows (generic path). One streaming pass keeps, per lane, the running
-// maximum and the fp64 sum of exp2(z*log2e/T - ref) against an integer
-// reference ref that only ever increases, so rescaling is an exact power of
-// two; the per-lane sums are combined exactly at the end. Thresholds, when
-// asked for, come from a bisection over the order-preserving integer keys of
-// the values (16-bit keys for bf16 rows, 32-bit for fp32), one pass over the
-// row per step. Bans are looked up in the LDS hash set. Exact in the same
-// sense as the histogram path, only slower for truncated rows.
+// fp32 rows (generic path). A first streaming pass finds the maximum and the
+// count. An untruncated row also sums, per lane, exp2(z*log2e/T - ref) against
+// an integer reference ref that only ever increases, so rescaling is an exact
+// power of two, and the per-lane sums are combined exactly at the end. A
+// truncated row takes its cuts from a radix selection over the
+// order-preserving integer keys of the values (8-bit digits: four passes for
+// fp32 keys, two for the 16-bit keys of bf16 rows), whose per-digit counts and
+// fixed-point mass sums are exact integers; the kept set's mass comes from
+// the same sums. Bans are removed from those sums exactly, or looked up in
+// the LDS hash set when a repetition penalty changes values. Exact in the
+// same sense as the histogram path, only slower.
 //
 // Each row also evaluates the probability of its proposal token (target row
 // i < gamma: p_i(x_i); draft row i: q_i(x_i)), which is all the acceptance walk
