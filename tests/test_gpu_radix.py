@@ -76,3 +76,30 @@ def test_bf16_rows_on_the_generic_path(samp):
     wl.target = synth.bf16_bits_to_f32(wl.target_bits)
     wl.draft = synth.bf16_bits_to_f32(wl.draft_bits)
     _check(wl, samp, f"bf16 generic {samp}")
+
+
+@pytest.mark.parametrize("samp", [(0.8, 0, 0.9), (1.0, 30, 1.0), (1.0, 200, 0.8)])
+def test_fp32_bans_holding_the_maximum(samp):
+    # every row's two largest logits are banned (the generic path then
+    # recomputes the admissible maximum), next to duplicate and out-of-range
+    # ids and a banned NaN; the counts and masses of the banned values are
+    # taken out of the radix sums exactly
+    wl = pu.make("c5f32", B=3, gamma=3, V=40009, seed=404)
+    rng = np.random.default_rng(9)
+    t, d = wl.target.copy(), wl.draft.copy()
+    # the same two tokens top every row of a request, so that one ban list
+    # covers them; in the last request a NaN sits at a third banned token
+    for b in range(wl.cfg.B):
+        top2 = rng.choice(wl.cfg.V, 2, replace=False)
+        t[b, :, top2[0]] = 30.0
+        t[b, :, top2[1]] = 29.5
+        d[b, :, top2[0]] = 28.0
+        d[b, :, top2[1]] = 27.5
+        nan_id = (int(top2[0]) + 17) % wl.cfg.V
+        if b == 2:   # a flagged request: only its flags are compared
+            t[b, 0, nan_id] = np.nan
+        bans = wl.banned[b].copy()
+        bans[:6] = [top2[0], top2[1], top2[0], -1, wl.cfg.V + 3, nan_id]
+        wl.banned[b] = bans
+    wl.target, wl.draft = t.astype(np.float32), d.astype(np.float32)
+    _check(wl, samp, f"fp32 banned maximum {samp}")
