@@ -242,13 +242,9 @@ struct GenericCtx {
   const uint32_t* ptab;   // LDS hash set of the penalized ids, or nullptr
   float theta;            // their repetition penalty
   bool bf16;              // penalized values are rounded to bf16
-  // the raw ban list, its first entry for this thread, and which of this
-  // thread's entries (list index threadIdx.x + k * RS_THREADS, bit k) entered
-  // the set: every distinct valid id has exactly one owner
-  const int32_t* bl;
-  int nb;
-  int32_t ban0;
-  uint32_t own;
+  // The banned values are listed in LDS behind the ban set (gen_banned_values)
+  // for the radix cut to take out of its sums.
+  bool sub_bans;
   __device__ __forceinline__ bool admissible(float z, int id) const {
     // finite and not banned; NaN fails both comparisons
     if (!(z > -INFINITY && z < INFINITY)) return false;
@@ -327,6 +323,17 @@ __device__ __forceinline__ double fix_val(Fix f) {
 // fixed-point sums); longer ones the bisection.
 constexpr int RADIX_MAX_V = 1 << 24;
 
+// The banned values a radix cut takes out of its sums: entry k of thread t
+// (list index t + k * RS_THREADS) at k * RS_THREADS + t, NaN when that entry
+// is not the one owner of a valid id. They sit behind the ban set, in the
+// histogram storage that only a repetition penalty's set would use.
+constexpr int GEN_BPT = (int)HT_MAX_IDS / RS_THREADS;   // list entries per thread
+static_assert(GEN_BPT * RS_THREADS >= (int)HT_MAX_IDS, "ban entries per thread");
+static_assert(GEN_BPT * RS_THREADS <= (int)HT_SLOTS, "banned values fit behind the set");
+__device__ __forceinline__ float* gen_banned_values(uint32_t* hist) {
+  return (float*)(hist + HT_SLOTS);
+}
+
 // Not inlined: its registers stay out of the count-histogram path's
 // allocation (every bf16 row takes that path; only fp32 rows and rare bf16
 // rows come here).
@@ -341,16 +348,8 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
   // finite element and then remove the banned ones, each distinct id once by
   // its owner thread, from the integer counts and fixed-point masses (exact),
   // instead of a set lookup per element.
-  constexpr int BPT = (int)HT_MAX_IDS / RS_THREADS;   // list entries per thread
-  static_assert(BPT * RS_THREADS >= (int)HT_MAX_IDS, "ban entries per thread");
-  const bool sub_bans = radix_cut && g.tab && !g.ptab;
-  float zb[BPT];
-#pragma unroll
-  for (int k = 0; k < BPT; ++k) {
-    zb[k] = __builtin_nanf("");
-    if (sub_bans && ((g.own >> k) & 1u))
-      zb[k] = elem_value<Elem>(rowp[k == 0 ? g.ban0 : g.bl[threadIdx.x + k * RS_THREADS]]);
-  }
+  const bool sub_bans = g.sub_bans;
+  const float* zb = gen_banned_values(sh.hist) + threadIdx.x;   // this thread's entries, stride RS_THREADS
   // pass 1: max, min, count and (without a radix cut) the exp-sum against
   // per-lane integer references
   float mx = -INFINITY, mn = INFINITY;
@@ -380,10 +379,11 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
     uint32_t bc = 0u;
     float bm = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      if (zb[k] > -INFINITY && zb[k] < INFINITY) {
+    for (int k = 0; k < GEN_BPT; ++k) {
+      const float z = zb[k * RS_THREADS];
+      if (z > -INFINITY && z < INFINITY) {
         ++bc;
-        bm = fmaxf(bm, zb[k]);
+        bm = fmaxf(bm, z);
       }
     }
     cnt -= block_sum<RS_THREADS>(bc, sh.uscr);
@@ -475,8 +475,8 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
         // the banned elements this level counted, taken back out (the bins
         // wrap through zero at worst, and end exact)
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-          const float z = zb[k];
+        for (int k = 0; k < GEN_BPT; ++k) {
+          const float z = zb[k * RS_THREADS];
           if (!(z > -INFINITY && z < INFINITY)) continue;
           const uint32_t key = gkey<Elem>(z);
           if (key < floor_key) continue;
@@ -1246,15 +1246,28 @@ void row_stats_kernel(RowStatsArgs a) {
   if (generic) {
     __syncthreads();
     // the ban set moves into the (now free) histogram storage
-    GenericCtx g{nullptr, nullptr, theta, sizeof(Elem) == 2, bl, nb, ban0, 0u};
+    GenericCtx g{nullptr, nullptr, theta, sizeof(Elem) == 2, false};
     if (nb > 0 || (MIXED && npen > 0)) {
       for (uint32_t k = tid; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = HT_EMPTY;
       __syncthreads();
     }
     if (nb > 0) {
-      g.own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
+      const uint32_t own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
       __syncthreads();
       g.tab = sh.hist;
+      // A radix cut without a repetition penalty takes the banned values out
+      // of its exact sums: each owner lists its values (a thread reads only
+      // its own entries later, so no barrier is needed).
+      if (!(MIXED && npen > 0) && V < RADIX_MAX_V && (s.top_k > 0 || s.top_p < 1.0f)) {
+        float* zl = gen_banned_values(sh.hist);
+#pragma unroll
+        for (int k = 0; k < GEN_BPT; ++k) {
+          float z = __builtin_nanf("");
+          if ((own >> k) & 1u) z = elem_value<Elem>(rowp[k == 0 ? ban0 : bl[tid + k * RS_THREADS]]);
+          zl[k * RS_THREADS + tid] = z;
+        }
+        g.sub_bans = true;
+      }
     }
     if (MIXED && npen > 0) {
       (void)pen_build(sh.hist + HT_SLOTS, g.tab, hist, H, props, npen, V, pen0, xprop, &sh.xpen);
