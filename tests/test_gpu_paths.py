@@ -1,6 +1,7 @@
 """Parity of code paths and limits of the HIP verifier beyond the benchmark
 recipes: unaligned rows and many draw parts, vocabularies past the old LDS
-bitmap size, the largest draft length, full ban lists, the zero-residual
+bitmap size and past the radix selection's 2^24 elements, the largest draft
+length, full ban lists, the zero-residual
 fallback and explicit uniforms at the ends of (0, 1]. Same bar as
 test_gpu_parity: bit-exact outside the 1e-10 decision band, lse within 1e-5."""
 
@@ -43,7 +44,8 @@ def test_unaligned_rows_many_draw_parts(samp):
 
 
 def test_vocabulary_beyond_bitmap_size_fp32_bans():
-    # fp32 rows take the generic path; bans are looked up in the LDS hash set
+    # fp32 rows take the generic path; a radix cut takes the 700 banned ids
+    # (duplicates included) out of its exact sums
     V, B, gamma = 300007, 1, 2
     wl = pu.make("c3a", B=B, gamma=gamma, V=V, dtype="f32", boost="none", seed=72)
     rng = np.random.default_rng(72)
@@ -53,6 +55,28 @@ def test_vocabulary_beyond_bitmap_size_fp32_bans():
     samp = (0.9, 0, 0.95)
     xs = pu.oracle_proposals(wl, draft_sampler=samp)
     _check(wl, xs, samp, banned=banned, where="V=300007 fp32")
+
+
+@pytest.mark.parametrize("dtype,samp", [("f32", (0.8, 0, 0.9)), ("f32", (1.0, 50, 1.0)),
+                                        ("bf16", (0.9, 0, 0.95))])
+def test_vocabulary_beyond_the_radix_limit(dtype, samp):
+    # 2^24 + 3 tokens: the generic path's cuts come from a bisection over the
+    # order-preserving keys (the radix selection's fixed-point sums stop at
+    # 2^24 elements); bf16 rows get there through one logit of -700, outside
+    # the counted window. One request, one proposal; 67 MB per fp32 row.
+    from lossless_draft_verification_sample_amd import synth
+    V = (1 << 24) + 3
+    wl = pu.make("c5f32" if dtype == "f32" else "c5", B=1, gamma=1, V=V, seed=79)
+    if dtype == "bf16":
+        t, d = wl.target.copy(), wl.draft.copy()
+        t[:, :, 12345] = -700.0
+        d[:, :, 12346] = -700.0
+        wl.target_bits = synth.f32_to_bf16_bits(t)
+        wl.draft_bits = synth.f32_to_bf16_bits(d)
+        wl.target = synth.bf16_bits_to_f32(wl.target_bits)
+        wl.draft = synth.bf16_bits_to_f32(wl.draft_bits)
+    xs = pu.oracle_proposals(wl, draft_sampler=samp)
+    _check(wl, xs, samp, seed=3, offset=1, where=f"V=2^24+3 {dtype} {samp}")
 
 
 def test_largest_gamma():
