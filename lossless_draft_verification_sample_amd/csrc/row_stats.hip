@@ -256,7 +256,8 @@ struct GenericCtx {
   }
 };
 
-// Order-preserving keys for the bisection: 16 bits for bf16 rows, 32 for fp32.
+// Order-preserving keys for the radix selection and the bisection: 16 bits
+// for bf16 rows, 32 for fp32.
 template <typename Elem>
 __device__ __forceinline__ uint32_t gkey(float v) {
   return sizeof(Elem) == 2 ? (f32_key(v) >> 16) : f32_key(v);
@@ -294,6 +295,26 @@ __device__ __forceinline__ double exp2_neg(double x) {
   q = fma(q, t, 1.0);
   q *= t;                                     // e^t - 1
   return ldexp(1.0 + q, (int)k);
+}
+
+// The same 2^x through a 256-entry table of 2^(j/256) (P. T. P. Tang, "Table-
+// driven implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989): x = m + j/256 + r with t = rint(256 x)
+// and r = x - t/256 exact (|r| <= 1/512); 2^r = e^u with u = r ln 2 in
+// double-double, e^u - 1 from its degree-4 Taylor polynomial (|u| < 0.0014,
+// remainder below 4e-17 relative).
+__device__ __forceinline__ double exp2_tab(double x, const double* tab) {
+  x = fmax(x, -1100.0);
+  const double t = rint(x * 256.0);
+  const double r = fma(t, -1.0 / 256.0, x);
+  const double u = fma(r, 0x1.62e42fefa39efp-1, r * 0x1.abc9e3b39803fp-56);
+  double q = fma(u, 1.0 / 24.0, 1.0 / 6.0);
+  q = fma(q, u, 0.5);
+  q = fma(q, u, 1.0);
+  q *= u;                                     // e^u - 1
+  const int ti = (int)t;
+  const double tj = tab[ti & 255];
+  return ldexp(fma(tj, q, tj), ti >> 8);
 }
 
 // A mass m in [0, 1] in fixed point: m = (h + l * 2^-40) * 2^-40 up to 2^-80.
@@ -445,12 +466,34 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
     // top_p * Z. Counts and fixed-point sums are exact, so the result does not
     // depend on the order of the LDS additions.
     constexpr int KB = sizeof(Elem) == 2 ? 16 : 32;
+    // Without a penalty set, the histogram storage around the banned values
+    // is free during the levels (the ban set is not looked up there): it
+    // holds MC copies of the count and mass bins, lane l adding to copy
+    // l % MC, merged before each pick (a wave's lanes crowd into the few
+    // digits that normal logits' exponents select, and LDS atomics to one
+    // address serialise), and the exp table.
+    constexpr int MC = 4;
+    static_assert(2 * 256 * MC * 2 <= (int)HT_SLOTS &&
+                  HT_SLOTS + GEN_BPT * RS_THREADS + 2 * 256 + 256 * MC <= HB_BINS,
+                  "level storage");
+    const bool spread = !g.ptab;
+    unsigned long long* cmh = (unsigned long long*)sh.hist;   // [256][MC]
+    unsigned long long* cml = cmh + 256 * MC;                  // [256][MC]
+    double* etab = (double*)(sh.hist + HT_SLOTS + GEN_BPT * RS_THREADS);
+    uint32_t* ccnt = sh.hist + HT_SLOTS + GEN_BPT * RS_THREADS + 2 * 256;   // [256][MC]
+    if (spread && threadIdx.x < 256) etab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 256.0));
     auto level = [&](int shift, uint32_t prefix, uint32_t floor_key, bool cnt_on) {
       if (threadIdx.x < 256) {
         sh.rcnt[threadIdx.x] = 0u;
         sh.rmh[threadIdx.x] = 0ull;
         sh.rml[threadIdx.x] = 0ull;
       }
+      if (spread)
+        for (int k = threadIdx.x; k < 256 * MC; k += RS_THREADS) {
+          cmh[k] = 0ull;
+          cml[k] = 0ull;
+          ccnt[k] = 0u;
+        }
       __syncthreads();
       for_each_elem<Elem>(rowp, V, [&](float z, int id) {
         // with a penalty the set lookups come first (they change values);
@@ -466,10 +509,18 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
         if (key < floor_key) return;
         if (shift + 8 < KB && (key >> (shift + 8)) != prefix) return;
         const uint32_t d = (key >> shift) & 255u;
-        if (cnt_on) atomicAdd(&sh.rcnt[d], 1u);
-        const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
-        atomicAdd(&sh.rmh[d], f.h);
-        atomicAdd(&sh.rml[d], f.l);
+        if (spread) {
+          const uint32_t c = d * MC + (threadIdx.x & (MC - 1));
+          if (cnt_on) atomicAdd(&ccnt[c], 1u);
+          const Fix f = fix_of(exp2_tab((double)z * c2 - rmax, etab));
+          atomicAdd(&cmh[c], f.h);
+          atomicAdd(&cml[c], f.l);
+        } else {
+          if (cnt_on) atomicAdd(&sh.rcnt[d], 1u);
+          const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
+          atomicAdd(&sh.rmh[d], f.h);
+          atomicAdd(&sh.rml[d], f.l);
+        }
       });
       if (sub_bans) {
         // the banned elements this level counted, taken back out (the bins
@@ -483,12 +534,28 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
           if (shift + 8 < KB && (key >> (shift + 8)) != prefix) continue;
           const uint32_t d = (key >> shift) & 255u;
           if (cnt_on) atomicSub(&sh.rcnt[d], 1u);
-          const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
+          const Fix f = fix_of(exp2_tab((double)z * c2 - rmax, etab));
           atomicAdd(&sh.rmh[d], 0ull - f.h);
           atomicAdd(&sh.rml[d], 0ull - f.l);
         }
       }
       __syncthreads();
+      if (spread) {
+        if (threadIdx.x < 256) {
+          unsigned long long h = sh.rmh[threadIdx.x], l = sh.rml[threadIdx.x];
+          uint32_t n = sh.rcnt[threadIdx.x];
+#pragma unroll
+          for (int c = 0; c < MC; ++c) {
+            h += cmh[threadIdx.x * MC + c];
+            l += cml[threadIdx.x * MC + c];
+            n += ccnt[threadIdx.x * MC + c];
+          }
+          sh.rmh[threadIdx.x] = h;
+          sh.rml[threadIdx.x] = l;
+          sh.rcnt[threadIdx.x] = n;
+        }
+        __syncthreads();
+      }
     };
     // Wave 0 scans the digits from the top (lane l takes 255 - 4l - j,
     // j = 0..3) for the first one where the running count reaches `need`
