@@ -205,8 +205,6 @@ struct DrawShared {
   uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
   uint32_t bmd[DRAW_SPW_MAX * DRAW_SUB / 32];   // draft-only bans (mixed batches)
   uint32_t bmp[DRAW_SPW_MAX * DRAW_SUB / 32];   // repetition-penalized ids (mixed batches)
-  double w[DRAW_SPW_MAX];
-  double p[DRAW_SPW_MAX];
   double scr[2 * DR_NW];
   int32_t iscr[2 * DR_NW];
   int32_t last;
@@ -281,7 +279,7 @@ __device__ __forceinline__ void mask_group(Group<Elem>& g, uint32_t bits) {
 // that logic. The bf16 MIXED variant is held to 128 VGPRs (four waves per
 // SIMD, so all workgroups of a launch stay resident; one spill).
 template <typename Elem, bool MIXED>
-__global__ __launch_bounds__(DR_THREADS, (MIXED && sizeof(Elem) == 2) ? 4 : 1)
+__global__ __launch_bounds__(DR_THREADS, sizeof(Elem) == 2 ? (MIXED ? 4 : 1) : 2)
 void draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
@@ -394,12 +392,20 @@ void draw_kernel(DrawArgs a) {
         if (km[k]) group_sums<Elem>(r, tg[k], dg[k], km[k], sh.etab, sw, sp);
     }
   };
+  // A sub-chunk's sums go out as soon as its wave has them. Publication
+  // without a release fence: agent-scope atomic stores, which the hardware
+  // writes through to the device-coherent level; every writer waits for its
+  // stores to complete before the barrier that precedes the arrival ticket,
+  // so they are visible device-wide before the ticket is taken. The reader
+  // uses agent-scope atomic loads. (A release on the ticket would also write
+  // back the whole L2, once per workgroup, for nothing.)
   auto publish = [&](int sl, double sw, double sp) {
     sw = wave_total(sw);
     sp = wave_total(sp);
     if (lane == 0) {
-      sh.w[sl] = sw;
-      sh.p[sl] = sp;
+      double* dst = &a.sums[(int64_t)b * a.nsub + sub0 + sl].w;
+      __hip_atomic_store(dst, sw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
   // The wave's sub-chunks, specialised by how the draft row is read: 0 =
@@ -553,19 +559,7 @@ void draw_kernel(DrawArgs a) {
     run(std::integral_constant<int, 1>{});
   else
     run(std::integral_constant<int, 2>{});
-  __syncthreads();
-  if (tid < nsl) {
-    // Publication without a release fence: the sums are agent-scope atomic
-    // stores, which the hardware writes through to the device-coherent level,
-    // and each writer waits for its stores to complete before the barrier, so
-    // they are visible device-wide before thread 0 bumps the arrival counter.
-    // The reader uses agent-scope atomic loads. (A release on the counter would
-    // also write back the whole L2, once per workgroup, for nothing.)
-    double* dst = &a.sums[(int64_t)b * a.nsub + sub0 + tid].w;
-    __hip_atomic_store(dst, sh.w[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, sh.p[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-  }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's sums have landed
   // the last workgroup of the request to arrive performs the selection
   __syncthreads();
   if (tid == 0)
@@ -614,7 +608,8 @@ void draw_kernel(DrawArgs a) {
       int sel = -1;
       double selb = 0.0;
       for (int c = k0; c < k1; ++c) {
-        const double v = ld(use_p ? &cs[c].p : &cs[c].w);
+        // a run of one sub-chunk: its value is the run's sum, already loaded
+        const double v = per == 1 ? loc : ld(use_p ? &cs[c].p : &cs[c].w);
         if (v > 0.0) {
           sel = c;                  // the last sub-chunk with weight unless one reaches t
           selb = run;
