@@ -471,18 +471,27 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
     // holds MC copies of the count and mass bins, lane l adding to copy
     // l % MC, merged before each pick (a wave's lanes crowd into the few
     // digits that normal logits' exponents select, and LDS atomics to one
-    // address serialise), and the exp table.
+    // address serialise), the exp table, and a list of the values that share
+    // the first two digits of an fp32 key (see `lmode` below).
     constexpr int MC = 4;
-    static_assert(2 * 256 * MC * 2 <= (int)HT_SLOTS &&
-                  HT_SLOTS + GEN_BPT * RS_THREADS + 2 * 256 + 256 * MC <= HB_BINS,
+    constexpr uint32_t LOFF = HT_SLOTS + GEN_BPT * RS_THREADS + 2 * 256 + 256 * MC;
+    constexpr uint32_t LCAP = HB_BINS - LOFF - 1u;
+    static_assert(2 * 256 * MC * 2 <= (int)HT_SLOTS && LOFF + 1u + 256u <= HB_BINS,
                   "level storage");
     const bool spread = !g.ptab;
     unsigned long long* cmh = (unsigned long long*)sh.hist;   // [256][MC]
     unsigned long long* cml = cmh + 256 * MC;                  // [256][MC]
     double* etab = (double*)(sh.hist + HT_SLOTS + GEN_BPT * RS_THREADS);
     uint32_t* ccnt = sh.hist + HT_SLOTS + GEN_BPT * RS_THREADS + 2 * 256;   // [256][MC]
+    uint32_t* lcnt = sh.hist + LOFF;
+    float* lst = (float*)(sh.hist + LOFF + 1u);
     if (spread && threadIdx.x < 256) etab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 256.0));
-    auto level = [&](int shift, uint32_t prefix, uint32_t floor_key, bool cnt_on) {
+    // lmode 1: the pass also lists the values it counts (those whose key
+    // matches the prefix), up to LCAP of them; lmode 2: the level runs over
+    // that list instead of the row. The list holds every element the next
+    // level can count, with the same values, so the counts and exact sums
+    // are those a pass over the row would give.
+    auto level = [&](int shift, uint32_t prefix, uint32_t floor_key, bool cnt_on, int lmode) {
       if (threadIdx.x < 256) {
         sh.rcnt[threadIdx.x] = 0u;
         sh.rmh[threadIdx.x] = 0ull;
@@ -494,8 +503,9 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
           cml[k] = 0ull;
           ccnt[k] = 0u;
         }
+      if (lmode == 1 && threadIdx.x == 0) *lcnt = 0u;
       __syncthreads();
-      for_each_elem<Elem>(rowp, V, [&](float z, int id) {
+      auto body = [&](float z, int id) {
         // with a penalty the set lookups come first (they change values);
         // without one every finite element counts here and the banned ones
         // are taken back out after the loop
@@ -515,13 +525,23 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
           const Fix f = fix_of(exp2_tab((double)z * c2 - rmax, etab));
           atomicAdd(&cmh[c], f.h);
           atomicAdd(&cml[c], f.l);
+          if (lmode == 1) {
+            const uint32_t k = atomicAdd(lcnt, 1u);
+            if (k < LCAP) lst[k] = z;
+          }
         } else {
           if (cnt_on) atomicAdd(&sh.rcnt[d], 1u);
           const Fix f = fix_of(exp2_neg((double)z * c2 - rmax));
           atomicAdd(&sh.rmh[d], f.h);
           atomicAdd(&sh.rml[d], f.l);
         }
-      });
+      };
+      if (lmode == 2) {
+        const uint32_t n = *lcnt;
+        for (uint32_t k = threadIdx.x; k < n; k += RS_THREADS) body(lst[k], 0);
+      } else {
+        for_each_elem<Elem>(rowp, V, body);
+      }
       if (sub_bans) {
         // the banned elements this level counted, taken back out (the bins
         // wrap through zero at worst, and end exact)
@@ -626,12 +646,22 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
       }
       __syncthreads();
     };
+    // fp32 keys without a penalty set: the third pass lists the values that
+    // share its 16-bit prefix (at a cut among normal logits, about a hundred
+    // of c5's 151,936), and the last level reads that list instead of the row
+    // when it held them all. The list is read after the barriers that end the
+    // third level and its pick, so every thread sees the same count.
+    auto lmode_of = [&](int shift) -> int {
+      if (KB != 32 || !spread) return 0;
+      if (shift == 8) return 1;
+      return (shift == 0 && *lcnt <= LCAP) ? 2 : 0;
+    };
     uint32_t floor_key = 0u;
     if (s.top_k > 0 && (uint32_t)s.top_k < cnt) {
       uint32_t need = (uint32_t)s.top_k, prefix = 0u;
       Fix above = {0ull, 0ull}, zk = {0ull, 0ull};
       for (int shift = KB - 8; shift >= 0; shift -= 8) {
-        level(shift, prefix, 0u, true);
+        level(shift, prefix, 0u, true, lmode_of(shift));
         pick(false, need, above, 0.0, 1.0f);
         const uint32_t d = sh.rsel_d;
         need -= sh.rsel_c;
@@ -652,7 +682,7 @@ __device__ __noinline__ RowStat row_generic(const Elem* rowp, int V, const Sampl
       // first level's total, which the first pick computes
       double target = trunc ? (double)s.top_p * Z : -1.0;
       for (int shift = KB - 8; shift >= 0; shift -= 8) {
-        level(shift, prefix, floor_key, false);
+        level(shift, prefix, floor_key, false, lmode_of(shift));
         pick(true, 0u, above, target, s.top_p);
         target = sh.rsel_target;
         const uint32_t d = sh.rsel_d;

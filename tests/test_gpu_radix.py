@@ -103,3 +103,30 @@ def test_fp32_bans_holding_the_maximum(samp):
         wl.banned[b] = bans
     wl.target, wl.draft = t.astype(np.float32), d.astype(np.float32)
     _check(wl, samp, f"fp32 banned maximum {samp}")
+
+
+@pytest.mark.parametrize("m", [300, 516, 517, 2000])
+@pytest.mark.parametrize("pmode", ["top-k", "top-k then top-p"])
+def test_fp32_cut_inside_a_prefix_cluster(m, pmode):
+    # m distinct values that share their first 16 key bits (all in
+    # [8, 8.0625)) above a background that stays below 6, and ten values
+    # above them: the top-k cut falls inside the cluster, so the last digit
+    # level sees exactly m candidates, the most the third pass can list for
+    # it being 516 (larger clusters take a fourth pass over the row)
+    wl = pu.make("c5f32", B=2, gamma=2, V=30011, seed=405)
+    rng = np.random.default_rng(11 + m)
+    V = wl.cfg.V
+    t = np.clip(rng.normal(0, 1, wl.target.shape), -6, 5.9).astype(np.float32)
+    d = np.clip(rng.normal(0, 1, wl.draft.shape), -6, 5.9).astype(np.float32)
+    base = np.float32(8.0).view(np.uint32)
+    for arr in (t, d):
+        for b in range(arr.shape[0]):
+            for i in range(arr.shape[1]):
+                pos = rng.choice(V, m + 10, replace=False)
+                bits = base + rng.choice(1 << 16, m, replace=False).astype(np.uint32)
+                arr[b, i, pos[:m]] = bits.view(np.float32)
+                arr[b, i, pos[m:]] = 12.0 + np.arange(10, dtype=np.float32)
+    wl.target, wl.draft = t, d
+    k = 10 + m // 2
+    samp = (1.0, k, 1.0) if pmode == "top-k" else (1.0, k, 0.97)
+    _check(wl, samp, f"fp32 prefix cluster m={m} {samp}")
