@@ -1209,13 +1209,18 @@ void row_stats_kernel(RowStatsArgs a) {
         if (k < nchunk) v[u] = __builtin_nontemporal_load(body + k);
       }
     };
-    // A row with no ban or penalty set to build issues its first buffer of
-    // stream loads now, so that it arrives during the histogram fill. (With
-    // sets to build, measured slower: their gathers would queue behind it.)
-    const bool early = nb == 0 && npen == 0;
+    // A ban list of at most one wave's length, in a row without a penalty
+    // set, needs no hash set: during the stream, the first wave finds each
+    // distinct id's first copy with lane shuffles and takes its logit
+    // (gathered above) out of the counts.
+    const bool wave_bans = nb > 0 && nb <= WAVE && npen == 0;
+    // A row with no set to build issues its first buffer of stream loads now,
+    // so that it arrives during the histogram fill. (With sets to build,
+    // measured slower: their gathers would queue behind it.)
+    const bool early = (nb == 0 || wave_bans) && npen == 0;
     if (early && tid < nchunk) ld(va, tid);
     // the first HT_SLOTS bins hold the ban hash set until the stream starts
-    const uint32_t fill = nb > 0 ? HT_EMPTY : 0u;
+    const uint32_t fill = (nb > 0 && !wave_bans) ? HT_EMPTY : 0u;
     const uint32_t pfill = npen > 0 ? HT_EMPTY : 0u;
     // 16-byte stores: the two set regions end on 16-byte boundaries
     static_assert(HT_SLOTS % 4 == 0 && 2 * HT_SLOTS <= HB_BINS &&
@@ -1231,7 +1236,7 @@ void row_stats_kernel(RowStatsArgs a) {
     __syncthreads();
 
     uint32_t own = 0u, own_p = 0u;
-    if (nb > 0) {
+    if (nb > 0 && !wave_bans) {
       own = ht_build(sh.hist, bl, nb, V, ban0, xprop, &sh.xban);
       __syncthreads();
     }
@@ -1241,7 +1246,18 @@ void row_stats_kernel(RowStatsArgs a) {
                         pen0, xprop, &sh.xpen);
       __syncthreads();
     }
-    if (nb > 0 || (MIXED && npen > 0)) {
+    // subtracts the counts of a banned bf16 logit (each distinct id once)
+    auto unban = [&](uint32_t bits) {
+      const uint32_t ae = bits & 0x7FFFu;
+      const uint32_t t = ae - HB_BASE;
+      if (t < HB_WIN)
+        atomicSub(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
+      else if (ae == 0u)
+        atomicSub(&sh.zero_cnt, 1u);
+      else if (ae < HB_BASE)
+        sh.special = 1u;   // a banned tiny value: the generic path sorts it out
+    };
+    if ((nb > 0 && !wave_bans) || (MIXED && npen > 0)) {
       for (uint32_t k = tid; k < 2 * HT_SLOTS; k += RS_THREADS) sh.hist[k] = 0u;
       __syncthreads();
       // Each distinct banned id leaves the counts once (its owner subtracts
@@ -1253,15 +1269,7 @@ void row_stats_kernel(RowStatsArgs a) {
       int kb = 0;
       for (int j = tid; j < nb; j += RS_THREADS, ++kb) {
         if (!((own >> kb) & 1u)) continue;
-        const uint32_t bits = kb == 0 ? ban_bits : (uint32_t)rp[bl[j]];
-        const uint32_t ae = bits & 0x7FFFu;
-        const uint32_t t = ae - HB_BASE;
-        if (t < HB_WIN)
-          atomicSub(&sh.hist[t + ((bits >> 15) ? HB_NEG : 0u)], 1u);
-        else if (ae == 0u)
-          atomicSub(&sh.zero_cnt, 1u);
-        else if (ae < HB_BASE)
-          sh.special = 1u;   // a banned tiny value: the generic path sorts it out
+        unban(kb == 0 ? ban_bits : (uint32_t)rp[bl[j]]);
       }
       if constexpr (MIXED) {
         // values outside the counted window on either side of a move send
@@ -1307,18 +1315,39 @@ void row_stats_kernel(RowStatsArgs a) {
         }
       }
     };
+    // The first wave's short ban list, taken out once its first stream
+    // buffer is counted: the gathered logits have long arrived by then, and
+    // the wave waits for them while its next buffer is in flight (used only
+    // after the stream, the gather would be issued there, a round trip at the
+    // end of the row).
+    bool bans_due = wave_bans && tid < WAVE;
+    auto take_bans = [&]() {
+      // lane l holds list entry l (-1 past the list); it owns its id when no
+      // lower lane holds the same valid id
+      const bool valid = ban0 >= 0 && ban0 < V;
+      bool dup = false;
+      for (int i = 0; i < WAVE; ++i) {
+        const int32_t o = __shfl(ban0, i, WAVE);
+        dup |= i < tid && o == ban0;
+      }
+      if (__ballot(valid && ban0 == xprop) && tid == 0) sh.xban = 1u;
+      if (valid && !dup) unban(ban_bits);
+      bans_due = false;
+    };
     int k0 = tid;
     if (!early && k0 < nchunk) ld(va, k0);
     if (u_pending) emit_u();
     while (k0 < nchunk) {
       if (k0 + STEP < nchunk) ld(vb, k0 + STEP);
       proc(va, k0);
+      if (bans_due) take_bans();
       k0 += STEP;
       if (k0 >= nchunk) break;
       if (k0 + STEP < nchunk) ld(va, k0 + STEP);
       proc(vb, k0);
       k0 += STEP;
     }
+    if (bans_due) take_bans();
     __syncthreads();
 
     if (tid == 0) {

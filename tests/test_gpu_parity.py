@@ -219,6 +219,38 @@ def test_bans_padding_duplicates_and_invalid_proposals(dtype):
     assert got["flags"][5] & oracle.FLAG_Q_ZERO
 
 
+@pytest.mark.parametrize("nb", [1, 63, 64, 65])
+def test_short_ban_lists_at_full_vocabulary(nb):
+    # bf16 rows of c5's vocabulary with ban lists of up to one wave (taken out
+    # of the counts after the stream, de-duplicated across a wave's lanes)
+    # and one longer (the LDS hash set): each list bans the largest logit of
+    # its request's first target row and that request's first proposal, and
+    # holds duplicates, padding and ids outside [0, V)
+    wl = pu.make("c5", B=4, gamma=3, seed=410 + nb)
+    rng = np.random.default_rng(nb)
+    V = wl.cfg.V
+    banned = rng.integers(0, V, (wl.cfg.B, nb)).astype(np.int32)
+    s = (0.8, 0, 0.9)
+    xs = pu.oracle_proposals(wl, s)
+    for b in range(wl.cfg.B):
+        top = int(np.argmax(wl.target[b, 0]))
+        banned[b, 0] = top
+        if nb > 1:
+            banned[b, 1] = xs[b, 0]
+        if nb > 4:
+            banned[b, 2] = top             # a duplicate
+            banned[b, 3] = -1              # padding
+            banned[b, 4] = V + b           # outside [0, V)
+    wl.banned = banned
+    u = pu.philox_uniforms(5, 1, wl.cfg.B, wl.cfg.gamma)
+    got = pu.run_gpu_sample(wl, xs, tsamp=s, dsamp=s, banned=banned, seed=5, offset=1)
+    ref = pu.run_oracle_sample(wl, xs, u, range(wl.cfg.B), tsamp=s, dsamp=s, banned=banned)
+    pu.compare_sample(got, ref, range(wl.cfg.B), where=f"short bans {nb}")
+    if nb > 1:   # the banned first proposal has q = 0: rejected at once
+        assert all(got["flags"][b] & oracle.FLAG_Q_ZERO and got["num_accepted"][b] == 0
+                   for b in range(wl.cfg.B))
+
+
 def test_all_banned_and_masked_rows():
     V, gamma, B = 64, 2, 3
     wl = _edge_workload(V, gamma, B, "bf16", seed=11)
