@@ -32,23 +32,40 @@ size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
   size_t stats, unif, sums, tickets, ov_partial, ov_tickets, total;
-  int nsub, spw, nwg;
+  int nsub;
   int ov_spp, ov_parts;
 };
+
+// Draw workgroups per request (nwg), each over spw consecutive sub-chunks.
+// A draw that may weigh every token of its row (a target sampler that keeps
+// everything, or a mixed batch, whose samplers only the device sees) is fp64
+// work on every token: one sub-chunk per wave, so that every wave takes part.
+// Otherwise (a plain batch whose target sampler truncates) a draw weighs a few
+// thousand tokens at most and extra workgroups only add their setup: about
+// DRAW_TARGET_WGS in total, each over at most DRAW_SPW_MAX sub-chunks.
+void draw_split(int64_t nsub, int64_t B, bool dense, int64_t* spw, int64_t* nwg) {
+  if (dense) {
+    *spw = nsub < sv::DRAW_WAVES ? nsub : sv::DRAW_WAVES;
+  } else {
+    int64_t n = (sv::DRAW_TARGET_WGS + B - 1) / B;
+    if (n > nsub) n = nsub;
+    *spw = (nsub + n - 1) / n;
+    if (*spw > sv::DRAW_SPW_MAX) *spw = sv::DRAW_SPW_MAX;
+  }
+  *nwg = (nsub + *spw - 1) / *spw;
+}
 
 bool layout(int32_t B, int32_t gamma, int32_t V, Layout* L) {
   if (B < 1 || gamma < 1 || gamma > 63 || V < 1) return false;
   const int64_t rows = (int64_t)B * (2 * (int64_t)gamma + 1);
   if (rows >= INT32_MAX) return false;
   const int64_t nsub = ((int64_t)V + sv::DRAW_SUB - 1) / sv::DRAW_SUB;
-  // draw workgroups: about DRAW_TARGET_WGS in total, each over at most
-  // DRAW_SPW_MAX sub-chunks of one request
-  int64_t nwg = (sv::DRAW_TARGET_WGS + B - 1) / B;
-  if (nwg > nsub) nwg = nsub;
-  int64_t spw = (nsub + nwg - 1) / nwg;
-  if (spw > sv::DRAW_SPW_MAX) spw = sv::DRAW_SPW_MAX;
-  nwg = (nsub + spw - 1) / spw;
-  if ((int64_t)B * nwg >= INT32_MAX) return false;
+  // the draw grid of either split must fit
+  for (const bool dense : {false, true}) {
+    int64_t spw, nwg;
+    draw_split(nsub, B, dense, &spw, &nwg);
+    if ((int64_t)B * nwg >= INT32_MAX) return false;
+  }
   // overlap workgroups: about OV_TARGET_WGS in total, each over at most
   // OV_SPW_MAX sub-chunks of one (request, position) pair
   const int64_t pairs = (int64_t)B * gamma;
@@ -60,8 +77,6 @@ bool layout(int32_t B, int32_t gamma, int32_t V, Layout* L) {
   parts = (nsub + spp - 1) / spp;
   if (pairs * parts >= INT32_MAX) return false;
   L->nsub = (int)nsub;
-  L->spw = (int)spw;
-  L->nwg = (int)nwg;
   L->ov_spp = (int)spp;
   L->ov_parts = (int)parts;
   size_t off = 0;
@@ -255,8 +270,13 @@ int sample_impl(const void* target_logits, const void* draft_logits, sv_dtype dt
     a.gamma = gamma;
     a.V = V;
     a.nsub = L.nsub;
-    a.spw = L.spw;
-    a.nwg = L.nwg;
+    const bool mixed = req.gammas || req.ts || req.ds || req.banned_d || req.pen_t ||
+                       req.pen_d || req.history;
+    const bool dense = mixed || (target.top_k == 0 && target.top_p >= 1.0f);
+    int64_t spw, nwg;
+    draw_split(L.nsub, B, dense, &spw, &nwg);
+    a.spw = (int)spw;
+    a.nwg = (int)nwg;
     a.st = to_dev(target);
     a.sd = to_dev(draft);
     a.req = req;

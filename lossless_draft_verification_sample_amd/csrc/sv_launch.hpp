@@ -14,6 +14,7 @@ namespace sv {
 constexpr int DRAW_SUB = 2048;
 constexpr int DRAW_SPW_MAX = 16;
 constexpr int DRAW_TARGET_WGS = 1024;   // about four draw workgroups per CU
+constexpr int DRAW_WAVES = 4;           // waves per draw workgroup
 
 // Per-position overlap: every (request, position) pair is split into `parts`
 // workgroups of at most OV_SPW_MAX sub-chunks, about OV_TARGET_WGS in total.

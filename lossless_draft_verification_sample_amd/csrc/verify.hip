@@ -30,6 +30,7 @@ namespace sv {
 
 constexpr int DR_THREADS = 256;
 constexpr int DR_NW = DR_THREADS / WAVE;
+static_assert(DR_NW == DRAW_WAVES, "the host sizes dense draw splits by this");
 constexpr int GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
 static_assert(DRAW_SUB == DR_THREADS * GRP, "one group of GRP logits per thread per sub-chunk");
 
