@@ -65,18 +65,22 @@ __device__ __forceinline__ DrawRow draw_row(const DrawArgs& a, int b, int n, con
   return r;
 }
 
-// Draw weight of one token whose target logit zt is kept: p(x), and
-// w(x) = max(0, p - q) at a rejection (w = p for the bonus draw).
-__device__ __forceinline__ void tok_weight(const DrawRow& r, float zt, float zd, const double* tab,
-                                           double& w, double& p) {
-  p = exp_tab(fma((double)zt, r.tinv, -r.ts.lse), tab);
-  w = p;
-  if (r.drow) {
-    // zd belongs to a token that is not banned (its target logit is kept)
-    const double q = is_kept(zd, r.ds, false) ? exp_tab(fma((double)zd, r.dinv, -r.ds.lse), tab)
-                                              : 0.0;
-    w = p > q ? p - q : 0.0;
-  }
+// p(x) of a token whose target logit zt is kept.
+__device__ __forceinline__ double tok_p(const DrawRow& r, float zt, const double* tab) {
+  return exp_tab(fma((double)zt, r.tinv, -r.ts.lse), tab);
+}
+
+// Draw weight of one token whose target logit zt is kept: w(x) = max(0, p - q)
+// at a rejection, p for the bonus draw. (Skipping the exps where the draft's
+// log-probability is at least the target's saves nothing: some lane of the
+// wave needs them.)
+__device__ __forceinline__ double tok_w(const DrawRow& r, float zt, float zd, const double* tab) {
+  const double p = exp_tab(fma((double)zt, r.tinv, -r.ts.lse), tab);
+  if (!r.drow) return p;
+  // zd belongs to a token that is not banned (its target logit is kept)
+  const double q = is_kept(zd, r.ds, false) ? exp_tab(fma((double)zd, r.dinv, -r.ds.lse), tab)
+                                            : 0.0;
+  return p > q ? p - q : 0.0;
 }
 
 // Bit e set when token e of the group is kept in the target row; only those
@@ -91,20 +95,15 @@ __device__ __forceinline__ uint32_t kept_mask(const DrawRow& r, const Group<Elem
   return m;
 }
 
-// Sums of w and p over the kept tokens of a group.
+// Sum of w over the kept tokens of a group.
 template <typename Elem>
-__device__ __forceinline__ void group_sums(const DrawRow& r, const Group<Elem>& tg,
-                                           const Group<Elem>& dg, uint32_t km, const double* tab,
-                                           double& sw, double& sp) {
+__device__ __forceinline__ double group_wsum(const DrawRow& r, const Group<Elem>& tg,
+                                             const Group<Elem>& dg, uint32_t km, const double* tab) {
+  double sw = 0.0;
 #pragma unroll
-  for (int e = 0; e < GRP; ++e) {
-    if ((km >> e) & 1u) {
-      double w, p;
-      tok_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab, w, p);
-      sw += w;
-      sp += p;
-    }
-  }
+  for (int e = 0; e < GRP; ++e)
+    if ((km >> e) & 1u) sw += tok_w(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab);
+  return sw;
 }
 
 // Per-token draw weights of a group: w, or p when `use_p` (0 outside the mask).
@@ -115,11 +114,9 @@ __device__ __forceinline__ void group_values(const DrawRow& r, const Group<Elem>
 #pragma unroll
   for (int e = 0; e < GRP; ++e) {
     v[e] = 0.0;
-    if ((km >> e) & 1u) {
-      double w, p;
-      tok_weight(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab, w, p);
-      v[e] = use_p ? p : w;
-    }
+    if ((km >> e) & 1u)
+      v[e] = use_p ? tok_p(r, group_val<Elem>(tg, e), tab)
+                   : tok_w(r, group_val<Elem>(tg, e), r.drow ? group_val<Elem>(dg, e) : 0.0f, tab);
   }
 }
 
@@ -355,9 +352,9 @@ void draw_kernel(DrawArgs a) {
     }
     return cnt;
   };
-  // sums of those kept tokens from registers, added to sw and sp
+  // the weight sum of those kept tokens from registers, added to sw
   auto sub_sums = [&](int sbase, const Group<Elem>(&tg)[GPL], const Group<Elem>(&dg)[GPL],
-                      const uint32_t(&km)[GPL], uint32_t cnt, double& sw, double& sp) {
+                      const uint32_t(&km)[GPL], uint32_t cnt, double& sw) {
     const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
     const uint32_t total = lane63(incl);
     if (total == 0u) return;
@@ -381,33 +378,29 @@ void draw_kernel(DrawArgs a) {
       wave_sync_lds();
       if ((uint32_t)lane < total) {
         const KeptTok t = sh.kt[wv][lane];
-        double w, p;
-        tok_weight(r, t.zt, t.zd, sh.etab, w, p);
-        sw += w;
-        sp += p;
+        sw += tok_w(r, t.zt, t.zd, sh.etab);
       }
       wave_sync_lds();
     } else {
 #pragma unroll
       for (int k = 0; k < GPL; ++k)
-        if (km[k]) group_sums<Elem>(r, tg[k], dg[k], km[k], sh.etab, sw, sp);
+        if (km[k]) sw += group_wsum<Elem>(r, tg[k], dg[k], km[k], sh.etab);
     }
   };
-  // A sub-chunk's sums go out as soon as its wave has them. Publication
+  // A sub-chunk's weight sum goes out as soon as its wave has it (the p sums,
+  // needed only when the residual has no mass, are left to the selection).
+  // Publication
   // without a release fence: agent-scope atomic stores, which the hardware
   // writes through to the device-coherent level; every writer waits for its
   // stores to complete before the barrier that precedes the arrival ticket,
   // so they are visible device-wide before the ticket is taken. The reader
   // uses agent-scope atomic loads. (A release on the ticket would also write
   // back the whole L2, once per workgroup, for nothing.)
-  auto publish = [&](int sl, double sw, double sp) {
+  auto publish = [&](int sl, double sw) {
     sw = wave_total(sw);
-    sp = wave_total(sp);
-    if (lane == 0) {
-      double* dst = &a.sums[(int64_t)b * a.nsub + sub0 + sl].w;
-      __hip_atomic_store(dst, sw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(dst + 1, sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (lane == 0)
+      __hip_atomic_store(&a.sums[(int64_t)b * a.nsub + sub0 + sl].w, sw, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   };
   // The wave's sub-chunks, specialised by how the draft row is read: 0 =
   // queued reads at a truncated target, 1 = none (bonus draw), 2 = streamed.
@@ -462,24 +455,16 @@ void draw_kernel(DrawArgs a) {
             qd[u] = pen_apply(qd[u], rq.pd, sizeof(Elem) == 2);
         }
       }
-      double qw[QU], qp[QU];
+      double qw[QU];
 #pragma unroll
-      for (int u = 0; u < QU; ++u) {
-        qw[u] = 0.0;
-        qp[u] = 0.0;
-        if (qx[u] >= 0) tok_weight(r, qt[u], qd[u], sh.etab, qw[u], qp[u]);
-      }
+      for (int u = 0; u < QU; ++u) qw[u] = qx[u] >= 0 ? tok_w(r, qt[u], qd[u], sh.etab) : 0.0;
       for (int sl = pend_lo; sl <= pend_hi; sl += DR_NW) {
         const int lo = tok0 + sl * DRAW_SUB;
-        double sw = 0.0, sp = 0.0;
+        double sw = 0.0;
 #pragma unroll
-        for (int u = 0; u < QU; ++u) {
-          if (qx[u] >= lo && qx[u] < lo + DRAW_SUB) {
-            sw += qw[u];
-            sp += qp[u];
-          }
-        }
-        publish(sl, sw, sp);
+        for (int u = 0; u < QU; ++u)
+          if (qx[u] >= lo && qx[u] < lo + DRAW_SUB) sw += qw[u];
+        publish(sl, sw);
       }
       wave_sync_lds();
       qlen = 0;
@@ -506,9 +491,9 @@ void draw_kernel(DrawArgs a) {
       uint32_t km[GPL];
       const uint32_t cnt = sub_mask(sbase, tg, km);
       if constexpr (MODE != 0) {
-        double sw = 0.0, sp = 0.0;
-        sub_sums(sbase, tg, dg, km, cnt, sw, sp);
-        publish(sl, sw, sp);
+        double sw = 0.0;
+        sub_sums(sbase, tg, dg, km, cnt, sw);
+        publish(sl, sw);
       } else {
         const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
         const int total = (int)lane63(incl);
@@ -524,11 +509,11 @@ void draw_kernel(DrawArgs a) {
             if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, x0 - tok0));
             if (dpen) penalize_group<Elem>(dg[k], bm_group(sh.bmp, x0 - tok0), rq.pd);
           }
-          double sw = 0.0, sp = 0.0;
+          double sw = 0.0;
 #pragma unroll
           for (int k = 0; k < GPL; ++k)
-            if (km[k]) group_sums<Elem>(r, tg[k], dg[k], km[k], sh.etab, sw, sp);
-          publish(sl, sw, sp);
+            if (km[k]) sw += group_wsum<Elem>(r, tg[k], dg[k], km[k], sh.etab);
+          publish(sl, sw);
           continue;
         }
         int pos = qlen + (int)(incl - cnt);
@@ -573,24 +558,63 @@ void draw_kernel(DrawArgs a) {
   uint32_t flags = wk.flags;
   ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
   auto ld = [](double* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  // every thread sums a contiguous run of sub-chunks (w and p), read once;
-  // one block scan gives the prefixes before each run and both totals
+  // Per-token values of sub-chunk s0, one group of GRP tokens per thread: w,
+  // or p when use_p (0 outside the target's kept set). The sub-chunk's bitmaps
+  // are built here, with barriers: every thread calls this.
+  auto sub_values = [&](int s0, bool use_p, double(&v)[GRP]) {
+    const int x0 = s0 + tid * GRP;
+    Group<Elem> tg, dg;
+    if (x0 < a.V) {
+      load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
+      if (r.drow && !use_p) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
+    }
+    if (dmask && !use_p) {
+      mark_bans(sh.bmd, DRAW_SUB, dbl, dnb, dban0, s0, a.V);
+      if (x0 < a.V) mask_group<Elem>(dg, bm_group(sh.bmd, x0 - s0));
+    }
+    if (tpen || (dpen && !use_p)) {
+      mark_pen(sh.bmp, DRAW_SUB, hist, H, props, n, s0, a.V);
+      if (x0 < a.V) {
+        if (tpen) penalize_group<Elem>(tg, bm_group(sh.bmp, x0 - s0), rq.pt);
+        if (dpen && !use_p) penalize_group<Elem>(dg, bm_group(sh.bmp, x0 - s0), rq.pd);
+      }
+    }
+    if (nb > 0) mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
+    const uint32_t km = x0 < a.V ? kept_mask<Elem>(r, tg, nb > 0 ? bm_group(sh.bm, x0 - s0) : 0u) : 0u;
+    group_values<Elem>(r, tg, dg, km, sh.etab, use_p, v);
+  };
+  // every thread sums a contiguous run of sub-chunks, read once; one block
+  // scan gives the prefix before each run and the total
   const int per = (a.nsub + DR_THREADS - 1) / DR_THREADS;
   const int k0 = tid * per, k1 = min(k0 + per, a.nsub);
-  double lw = 0.0, lp = 0.0;
-  for (int c = k0; c < k1; ++c) {
-    lw += ld(&cs[c].w);
-    lp += ld(&cs[c].p);
-  }
-  double bw, bp, tw, tp;
-  block_excl_scan2<DR_THREADS>(lw, lp, sh.scr, bw, bp, tw, tp);
-  // fall back to p when the residual has no mass
+  double loc = 0.0, before, S, unused0, unused1;
+  for (int c = k0; c < k1; ++c) loc += ld(&cs[c].w);
+  block_excl_scan2<DR_THREADS>(loc, 0.0, sh.scr, before, unused0, S, unused1);
+  // Fall back to p when the residual has no mass (p and q then agree on every
+  // token). The stream summed only the residual, so the p sums of the
+  // sub-chunks are made here, one sub-chunk at a time.
   bool use_p = false;
-  double S = tw;
-  if (!(tw > 0.0) && n < g) {
+  if (!(S > 0.0) && n < g) {
     flags |= FLAG_RESIDUAL_ZERO;
     use_p = true;
-    S = tp;
+    // an empty target row keeps nothing: every p sum is 0
+    const int nsum = (r.ts.flags & FLAG_EMPTY) ? 0 : a.nsub;
+    for (int c = 0; c < nsum; ++c) {
+      double v[GRP];
+      sub_values(c * DRAW_SUB, true, v);
+      double ls = 0.0;
+#pragma unroll
+      for (int e = 0; e < GRP; ++e) ls += v[e];
+      double pb, tot;
+      block_excl_scan2<DR_THREADS>(ls, 0.0, sh.scr, pb, unused0, tot, unused1);
+      if (tid == 0) __hip_atomic_store(&cs[c].p, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    loc = 0.0;
+    if (nsum > 0)
+      for (int c = k0; c < k1; ++c) loc += ld(&cs[c].p);
+    block_excl_scan2<DR_THREADS>(loc, 0.0, sh.scr, before, unused0, S, unused1);
   }
   int32_t token = -1;
   if (!(S > 0.0)) {
@@ -600,7 +624,6 @@ void draw_kernel(DrawArgs a) {
     // the sub-chunk holding t: the first thread whose run reaches t searches its
     // run; when rounding leaves t above every prefix, the last sub-chunk with
     // weight is taken
-    const double loc = use_p ? lp : lw, before = use_p ? bp : bw;
     int cand, lastw;
     block_first_last<DR_THREADS>(loc > 0.0 && before + loc >= t, loc > 0.0, sh.iscr, cand, lastw);
     const int who = cand < DR_THREADS ? cand : lastw;
@@ -629,26 +652,8 @@ void draw_kernel(DrawArgs a) {
     const int s0 = sh.sel_sub * DRAW_SUB;
     const double tl = wk.u_final * S - sh.sel_before;
     const int x0 = s0 + tid * GRP;
-    Group<Elem> tg, dg;
-    if (x0 < a.V) {
-      load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
-      if (r.drow) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
-    }
-    if (dmask) {
-      mark_bans(sh.bmd, DRAW_SUB, dbl, dnb, dban0, s0, a.V);
-      if (x0 < a.V) mask_group<Elem>(dg, bm_group(sh.bmd, x0 - s0));
-    }
-    if (tpen || dpen) {
-      mark_pen(sh.bmp, DRAW_SUB, hist, H, props, n, s0, a.V);
-      if (x0 < a.V) {
-        if (tpen) penalize_group<Elem>(tg, bm_group(sh.bmp, x0 - s0), rq.pt);
-        if (dpen) penalize_group<Elem>(dg, bm_group(sh.bmp, x0 - s0), rq.pd);
-      }
-    }
-    if (nb > 0) mark_bans(sh.bm, DRAW_SUB, bl, nb, ban0, s0, a.V);
     double v[GRP];
-    const uint32_t km = x0 < a.V ? kept_mask<Elem>(r, tg, nb > 0 ? bm_group(sh.bm, x0 - s0) : 0u) : 0u;
-    group_values<Elem>(r, tg, dg, km, sh.etab, use_p, v);
+    sub_values(s0, use_p, v);
     double lsum = 0.0;
 #pragma unroll
     for (int e = 0; e < GRP; ++e) lsum += v[e];

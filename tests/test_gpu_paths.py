@@ -118,6 +118,25 @@ def test_zero_residual_falls_back_to_p():
     assert np.all(got["flags"] & oracle.FLAG_TOKEN_RANGE)
 
 
+@pytest.mark.parametrize("name, samp", [("c5", (1.0, 0, 1.0)), ("c5", (0.8, 0, 0.9)),
+                                         ("c5f32", (1.0, 0, 1.0))])
+def test_zero_residual_at_full_vocabulary(name, samp):
+    # p == q on every row of c5's vocabulary, c5's bans on both rows, and a
+    # rejection forced at position 1: the draw's stream sums only the
+    # residual, so the selecting workgroup makes the p sums of all 75
+    # sub-chunks itself before it draws from p
+    wl = pu.make(name, B=3, gamma=3, seed=78)
+    g = wl.cfg.gamma
+    wl.draft = wl.target[:, :g].copy()
+    if wl.target_bits is not None:
+        wl.draft_bits = wl.target_bits[:, :g].copy()
+    xs = pu.oracle_proposals(wl, draft_sampler=samp)
+    xs[:, 1] = wl.cfg.V + 1
+    got, _ = _check(wl, xs, samp, banned=wl.banned, where=f"zero residual {name} {samp}")
+    assert np.all(got["flags"] & oracle.FLAG_RESIDUAL_ZERO)
+    assert np.all(got["num_accepted"] <= 1)
+
+
 def test_explicit_uniforms_at_the_ends():
     V, B, gamma = 2000, 8, 3
     wl = pu.make("c3a", B=B, gamma=gamma, V=V, boost="none", seed=76)
