@@ -57,6 +57,25 @@ __device__ __forceinline__ float group_val(const Group<Elem>& g, int j) {
   return __uint_as_float(g.w[j >> 2][j & 3]);
 }
 
+// group_val for an index known only at run time: selects instead of a
+// dynamically indexed register array (which would go through scratch).
+template <typename Elem>
+__device__ __forceinline__ float group_val_dyn(const Group<Elem>& g, int j) {
+  if constexpr (sizeof(Elem) == 2) {
+    const uint32_t d01 = (j & 2) ? g.w[0][1] : g.w[0][0];
+    const uint32_t d23 = (j & 2) ? g.w[0][3] : g.w[0][2];
+    const uint32_t d = (j & 4) ? d23 : d01;
+    return bf16_to_f32((j & 1) ? d >> 16 : d & 0xFFFFu);
+  } else {
+    const bool hi = (j & 4) != 0;
+    const uint32_t d0 = hi ? g.w[1][0] : g.w[0][0], d1 = hi ? g.w[1][1] : g.w[0][1];
+    const uint32_t d2 = hi ? g.w[1][2] : g.w[0][2], d3 = hi ? g.w[1][3] : g.w[0][3];
+    const uint32_t d01 = (j & 1) ? d1 : d0;
+    const uint32_t d23 = (j & 1) ? d3 : d2;
+    return __uint_as_float((j & 2) ? d23 : d01);
+  }
+}
+
 // exp(a) in fp64 for a <= about 0, table-driven (P. T. P. Tang, "Table-driven
 // implementation of the exponential function in IEEE floating-point
 // arithmetic", ACM TOMS 15(2), 1989): a = (256 k' + j) ln2 / 256 + r with

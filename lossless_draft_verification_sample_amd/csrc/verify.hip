@@ -362,17 +362,14 @@ void draw_kernel(DrawArgs a) {
       uint32_t pos = incl - cnt;
 #pragma unroll
       for (int k = 0; k < GPL; ++k) {
-        if (!km[k]) continue;
-#pragma unroll
-        for (int e = 0; e < GRP; ++e) {   // static token index: the group stays in registers
-          if ((km[k] >> e) & 1u) {
-            KeptTok t;
-            t.x = sbase + (lane + k * WAVE) * GRP + e;
-            t.zt = group_val<Elem>(tg[k], e);
-            t.zd = r.drow ? group_val<Elem>(dg[k], e) : 0.0f;
-            t.pad = 0;
-            sh.kt[wv][pos++] = t;
-          }
+        for (uint32_t m = km[k]; m; m &= m - 1u) {   // one iteration per kept token
+          const int e = __ffs(m) - 1;
+          KeptTok t;
+          t.x = sbase + (lane + k * WAVE) * GRP + e;
+          t.zt = group_val_dyn<Elem>(tg[k], e);
+          t.zd = r.drow ? group_val_dyn<Elem>(dg[k], e) : 0.0f;
+          t.pad = 0;
+          sh.kt[wv][pos++] = t;
         }
       }
       wave_sync_lds();
@@ -516,18 +513,17 @@ void draw_kernel(DrawArgs a) {
           publish(sl, sw);
           continue;
         }
+        // one iteration per kept token of the lane (the wave runs as many as
+        // its busiest lane needs, usually one or two)
         int pos = qlen + (int)(incl - cnt);
 #pragma unroll
         for (int k = 0; k < GPL; ++k) {
-          if (!km[k]) continue;
-#pragma unroll
-          for (int e = 0; e < GRP; ++e) {
-            if ((km[k] >> e) & 1u) {
-              QueuedTok t;
-              t.x = sbase + (lane + k * WAVE) * GRP + e;
-              t.z = group_val<Elem>(tg[k], e);
-              sh.q[wv][pos++] = t;
-            }
+          for (uint32_t m = km[k]; m; m &= m - 1u) {
+            const int e = __ffs(m) - 1;
+            QueuedTok t;
+            t.x = sbase + (lane + k * WAVE) * GRP + e;
+            t.z = group_val_dyn<Elem>(tg[k], e);
+            sh.q[wv][pos++] = t;
           }
         }
         qlen += total;
