@@ -206,20 +206,19 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, Shared& sh, int wv,
         qlen = 0;
       }
       if (total <= OV_QCAP) {
-        // queue the kept tokens in ascending token order of the wave's groups
+        // queue the kept tokens in ascending token order of the wave's groups,
+        // one iteration per kept token of the lane (the wave runs as many as
+        // its busiest lane needs)
         int pos = qlen + (int)(incl - cnt);
 #pragma unroll
         for (int k = 0; k < OV_GPL; ++k) {
-          if (!km[k]) continue;
           const Group<Elem>& lg = LEAD == 1 ? dg[k] : tg[k];
-#pragma unroll
-          for (int e = 0; e < GRP; ++e) {
-            if ((km[k] >> e) & 1u) {
-              QueuedTok t;
-              t.x = sbase + (lane + k * WAVE) * GRP + e;
-              t.z = group_val<Elem>(lg, e);
-              sh.q[wv][pos++] = t;
-            }
+          for (uint32_t m = km[k]; m; m &= m - 1u) {
+            const int e = __ffs(m) - 1;
+            QueuedTok t;
+            t.x = sbase + (lane + k * WAVE) * GRP + e;
+            t.z = group_val_dyn<Elem>(lg, e);
+            sh.q[wv][pos++] = t;
           }
         }
         qlen += total;
