@@ -38,8 +38,9 @@ struct Layout {
 
 // Draw workgroups per request (nwg), each over spw consecutive sub-chunks.
 // A draw that may weigh every token of its row (a target sampler that keeps
-// everything, or a mixed batch, whose samplers only the device sees) is fp64
-// work on every token: one sub-chunk per wave, so that every wave takes part.
+// everything, or per-request target samplers, which only the device sees) is
+// fp64 work on every token: one sub-chunk per wave, so that every wave takes
+// part.
 // Otherwise (a plain batch whose target sampler truncates) a draw weighs a few
 // thousand tokens at most and extra workgroups only add their setup: about
 // DRAW_TARGET_WGS in total, each over at most DRAW_SPW_MAX sub-chunks.
@@ -270,9 +271,9 @@ int sample_impl(const void* target_logits, const void* draft_logits, sv_dtype dt
     a.gamma = gamma;
     a.V = V;
     a.nsub = L.nsub;
-    const bool mixed = req.gammas || req.ts || req.ds || req.banned_d || req.pen_t ||
-                       req.pen_d || req.history;
-    const bool dense = mixed || (target.top_k == 0 && target.top_p >= 1.0f);
+    // per-request target samplers are only visible on the device; otherwise
+    // every request uses the call's own
+    const bool dense = req.ts || (target.top_k == 0 && target.top_p >= 1.0f);
     int64_t spw, nwg;
     draw_split(L.nsub, B, dense, &spw, &nwg);
     a.spw = (int)spw;
