@@ -281,7 +281,12 @@ __global__ __launch_bounds__(DR_THREADS, sizeof(Elem) == 2 ? (MIXED ? 4 : 1) : 2
 void draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
-  const int b = blockIdx.x / a.nwg, part = blockIdx.x % a.nwg;
+  // A plain batch's grid is part-major (part p of every request before part
+  // p + 1: the draws finish closer together); a mixed batch's stays
+  // request-major, so that the workgroups of a heavy request start together.
+  const int nreq = (int)(gridDim.x / (unsigned)a.nwg);
+  const int b = MIXED ? blockIdx.x / a.nwg : blockIdx.x % nreq;
+  const int part = MIXED ? blockIdx.x % a.nwg : blockIdx.x / nreq;
   const int g = a.gamma, G1 = g + 1;
   const int sub0 = part * a.spw;
   const int nsl = min(a.spw, a.nsub - sub0);
