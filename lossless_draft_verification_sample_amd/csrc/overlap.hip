@@ -258,7 +258,10 @@ template <typename Elem, bool MIXED>
 __global__ __launch_bounds__(OV_THREADS) void overlap_kernel(OverlapArgs a) {
   __shared__ OverlapShared<MIXED> sh;
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid & (WAVE - 1);
-  const int pair = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
+  // part-major grid in a plain batch (part p of every pair before part p + 1)
+  const int npairs = (int)(gridDim.x / (unsigned)a.parts);
+  const int pair = MIXED ? blockIdx.x / a.parts : blockIdx.x % npairs;
+  const int part = MIXED ? blockIdx.x % a.parts : blockIdx.x / npairs;
   const int g = a.gamma, G1 = g + 1, RPR = 2 * g + 1;
   const int b = pair / g, i = pair % g;
   ReqInfo rq;
