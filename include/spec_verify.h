@@ -218,7 +218,7 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
  * the process ends. The call allocates nothing. Sizes whose
  * spec_verify_workspace_bytes exceed SV_NOALLOC_SCRATCH_BYTES return
  * SV_ESCRATCH (c5-sized batches, B = 128, gamma = 8, V = 151936, need about
- * 0.3 MB). The first call on a device resolves that device's array address
+ * 4.0 MB). The first call on a device resolves that device's array address
  * (SV_EHIP if it cannot). Every call on one GPU shares its array: calls that
  * may overlap on one GPU (different streams, or different host threads)
  * race and must be serialised by the caller; calls in order on one stream are

@@ -31,7 +31,7 @@ constexpr size_t WS_ALIGN = 256;
 size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
-  size_t stats, unif, sums, tickets, ov_partial, ov_tickets, total;
+  size_t stats, unif, sums, lcount, lx, lw, tickets, ov_partial, ov_tickets, total;
   int nsub;
   int ov_spp, ov_parts;
 };
@@ -87,6 +87,12 @@ bool layout(int32_t B, int32_t gamma, int32_t V, Layout* L) {
   off = align_up(off + (size_t)B * (size_t)(gamma + 1) * sizeof(double));
   L->sums = off;
   off = align_up(off + (size_t)B * (size_t)nsub * sizeof(sv::ChunkSums));
+  L->lcount = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sizeof(int32_t));
+  L->lx = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sv::DRAW_LIST * sizeof(int32_t));
+  L->lw = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sv::DRAW_LIST * sizeof(double));
   L->tickets = off;
   off = align_up(off + (size_t)B * sizeof(int32_t));
   L->ov_partial = off;
@@ -287,6 +293,9 @@ int sample_impl(const void* target_logits, const void* draft_logits, sv_dtype dt
     a.stats = stats;
     a.uniforms = uniforms ? uniforms : unif;
     a.sums = sums;
+    a.lcount = (int32_t*)(ws + L.lcount);
+    a.lx = (int32_t*)(ws + L.lx);
+    a.lw = (double*)(ws + L.lw);
     a.tickets = tickets;
     a.out_tokens = out_tokens;
     a.out_num_accepted = out_num_accepted;

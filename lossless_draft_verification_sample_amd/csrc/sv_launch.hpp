@@ -15,6 +15,9 @@ constexpr int DRAW_SUB = 2048;
 constexpr int DRAW_SPW_MAX = 16;
 constexpr int DRAW_TARGET_WGS = 1024;   // about four draw workgroups per CU
 constexpr int DRAW_WAVES = 4;           // waves per draw workgroup
+// kept tokens a draw workgroup lists per sub-chunk of a truncated row (more:
+// the selection rescans the sub-chunk)
+constexpr int DRAW_LIST = 32;
 
 // Per-position overlap: every (request, position) pair is split into `parts`
 // workgroups of at most OV_SPW_MAX sub-chunks, about OV_TARGET_WGS in total.
@@ -56,6 +59,9 @@ struct DrawArgs {
   const RowStat* stats;
   const double* uniforms;     // [B][gamma+1]: the caller's, or those of the row pass
   ChunkSums* sums;            // [B][nsub]
+  int32_t* lcount;            // [B][nsub]: tokens listed, DRAW_LIST + 1 when not listed
+  int32_t* lx;                // [B][nsub][DRAW_LIST]: their ids
+  double* lw;                 // [B][nsub][DRAW_LIST]: their draw weights
   int32_t* tickets;           // [B], zero on entry
   int32_t* out_tokens;
   int32_t* out_num_accepted;

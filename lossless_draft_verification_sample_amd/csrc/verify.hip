@@ -17,10 +17,13 @@
 //
 // Work split: each request gets `nwg` workgroups, each owning `spw` consecutive
 // sub-chunks of DRAW_SUB tokens. Every workgroup repeats the (tiny) acceptance
-// walk to learn n, sums the draw weights of its sub-chunks and publishes them;
-// the last workgroup of the request to finish (an arrival counter) locates the
-// sub-chunk holding u * S, rescans it and writes the request's outputs.
+// walk to learn n, sums the draw weights of its sub-chunks and publishes them
+// (at a truncated target row of a plain batch, with a list of each sub-chunk's
+// weighted tokens when it has at most DRAW_LIST); the last workgroup of the
+// request to finish (an arrival counter) locates the sub-chunk holding u * S,
+// picks the token from its list or rescans it, and writes the outputs.
 
+#include <climits>
 #include <type_traits>
 
 #include "sv_launch.hpp"
@@ -193,12 +196,21 @@ __device__ __forceinline__ Walk accept_walk(const DrawArgs& a, int b, int gq) {
 }
 
 constexpr int DR_QCAP = 4 * WAVE;   // queued kept tokens per wave: one batch of 4 reads per lane
+static_assert(DRAW_LIST <= WAVE, "a sub-chunk's list is read by one wave, one entry per lane");
+
+// A listed token of the selected sub-chunk, placed in token order.
+struct ListTok {
+  int32_t x;
+  int32_t pad;
+  double w;
+};
 
 struct DrawShared {
   double etab[256];
   union {
     KeptTok kt[DR_NW][WAVE];          // bonus draws and untruncated targets
     QueuedTok q[DR_NW][DR_QCAP];      // rejections at a truncated target
+    ListTok lt[DRAW_LIST];            // the selection's list, after the stream
   };
   uint32_t bm[DRAW_SPW_MAX * DRAW_SUB / 32];
   uint32_t bmd[DRAW_SPW_MAX * DRAW_SUB / 32];   // draft-only bans (mixed batches)
@@ -345,6 +357,9 @@ void draw_kernel(DrawArgs a) {
   //   streamed alongside) the weights come from registers: through a per-wave
   //   compaction when at most 64 tokens are kept, in place when more are.
   const bool sparse = r.ts.tau > -INFINITY;
+  // kept-token lists of the sub-chunks for the selection (truncated target
+  // rows of plain batches; in mixed batches they measured slower)
+  const bool listing = !MIXED && sparse;
   const bool queued = sparse && r.drow;
   // the kept tokens of the wave's groups of one sub-chunk, and their number
   auto sub_mask = [&](int sbase, const Group<Elem>(&tg)[GPL], uint32_t(&km)[GPL]) {
@@ -357,11 +372,25 @@ void draw_kernel(DrawArgs a) {
     }
     return cnt;
   };
+  // Appends (x, w) of the lanes with `on` set to sub-chunk c's list at
+  // positions base, base + 1, ... in lane order (stores past DRAW_LIST are
+  // dropped); returns the new length. Same publication as the sums.
+  auto list_put = [&](int64_t c, int base, bool on, int32_t x, double w) {
+    const uint64_t m = __ballot(on);
+    const int j = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (on && j < DRAW_LIST) {
+      __hip_atomic_store(&a.lx[c * DRAW_LIST + j], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.lw[c * DRAW_LIST + j], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return base + (int)__popcll(m);
+  };
   // the weight sum of those kept tokens from registers, added to sw
   auto sub_sums = [&](int sbase, const Group<Elem>(&tg)[GPL], const Group<Elem>(&dg)[GPL],
-                      const uint32_t(&km)[GPL], uint32_t cnt, double& sw) {
+                      const uint32_t(&km)[GPL], uint32_t cnt, double& sw, int& nl) {
     const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
     const uint32_t total = lane63(incl);
+    nl = 0;
     if (total == 0u) return;
     if (total <= (uint32_t)WAVE) {
       uint32_t pos = incl - cnt;
@@ -378,15 +407,21 @@ void draw_kernel(DrawArgs a) {
         }
       }
       wave_sync_lds();
+      int32_t x = -1;
+      double w = 0.0;
       if ((uint32_t)lane < total) {
         const KeptTok t = sh.kt[wv][lane];
-        sw += tok_w(r, t.zt, t.zd, sh.etab);
+        x = t.x;
+        w = tok_w(r, t.zt, t.zd, sh.etab);
+        sw += w;
       }
       wave_sync_lds();
+      if (listing) nl = list_put((int64_t)b * a.nsub + sbase / DRAW_SUB, 0, w > 0.0, x, w);
     } else {
 #pragma unroll
       for (int k = 0; k < GPL; ++k)
         if (km[k]) sw += group_wsum<Elem>(r, tg[k], dg[k], km[k], sh.etab);
+      nl = DRAW_LIST + 1;
     }
   };
   // A sub-chunk's weight sum goes out as soon as its wave has it (the p sums,
@@ -398,11 +433,17 @@ void draw_kernel(DrawArgs a) {
   // so they are visible device-wide before the ticket is taken. The reader
   // uses agent-scope atomic loads. (A release on the ticket would also write
   // back the whole L2, once per workgroup, for nothing.)
-  auto publish = [&](int sl, double sw) {
+  // When listing, next to the sum goes the length nl of the sub-chunk's list
+  // of tokens with w > 0 (DRAW_LIST + 1: not listed), so that the selection
+  // can pick from the list instead of reading the sub-chunk again.
+  // (Untruncated rows keep nearly every token: no lists.)
+  auto publish = [&](int sl, double sw, int nl) {
     sw = wave_total(sw);
-    if (lane == 0)
-      __hip_atomic_store(&a.sums[(int64_t)b * a.nsub + sub0 + sl].w, sw, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+      const int64_t c = (int64_t)b * a.nsub + sub0 + sl;
+      __hip_atomic_store(&a.sums[c].w, sw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (listing) __hip_atomic_store(&a.lcount[c], nl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   };
   // The wave's sub-chunks, specialised by how the draft row is read: 0 =
   // queued reads at a truncated target, 1 = none (bonus draw), 2 = streamed.
@@ -462,11 +503,17 @@ void draw_kernel(DrawArgs a) {
       for (int u = 0; u < QU; ++u) qw[u] = qx[u] >= 0 ? tok_w(r, qt[u], qd[u], sh.etab) : 0.0;
       for (int sl = pend_lo; sl <= pend_hi; sl += DR_NW) {
         const int lo = tok0 + sl * DRAW_SUB;
+        const int64_t c = (int64_t)b * a.nsub + sub0 + sl;
         double sw = 0.0;
+        int nl = 0;
 #pragma unroll
-        for (int u = 0; u < QU; ++u)
-          if (qx[u] >= lo && qx[u] < lo + DRAW_SUB) sw += qw[u];
-        publish(sl, sw);
+        for (int u = 0; u < QU; ++u) {
+          if (u * WAVE >= qlen) break;
+          const bool in = qx[u] >= lo && qx[u] < lo + DRAW_SUB;
+          if (in) sw += qw[u];
+          if (listing) nl = list_put(c, nl, in && qw[u] > 0.0, qx[u], qw[u]);
+        }
+        publish(sl, sw, nl);
       }
       wave_sync_lds();
       qlen = 0;
@@ -494,8 +541,9 @@ void draw_kernel(DrawArgs a) {
       const uint32_t cnt = sub_mask(sbase, tg, km);
       if constexpr (MODE != 0) {
         double sw = 0.0;
-        sub_sums(sbase, tg, dg, km, cnt, sw);
-        publish(sl, sw);
+        int nl;
+        sub_sums(sbase, tg, dg, km, cnt, sw, nl);
+        publish(sl, sw, nl);
       } else {
         const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
         const int total = (int)lane63(incl);
@@ -515,7 +563,7 @@ void draw_kernel(DrawArgs a) {
 #pragma unroll
           for (int k = 0; k < GPL; ++k)
             if (km[k]) sw += group_wsum<Elem>(r, tg[k], dg[k], km[k], sh.etab);
-          publish(sl, sw);
+          publish(sl, sw, DRAW_LIST + 1);
           continue;
         }
         // one iteration per kept token of the lane (the wave runs as many as
@@ -559,6 +607,7 @@ void draw_kernel(DrawArgs a) {
   uint32_t flags = wk.flags;
   ChunkSums* cs = a.sums + (int64_t)b * a.nsub;
   auto ld = [](double* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto ldi = [](int32_t* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   // Per-token values of sub-chunk s0, one group of GRP tokens per thread: w,
   // or p when use_p (0 outside the target's kept set). The sub-chunk's bitmaps
   // are built here, with barriers: every thread calls this.
@@ -649,8 +698,51 @@ void draw_kernel(DrawArgs a) {
     __syncthreads();
   }
   if (S > 0.0 && sh.sel_sub < 0) flags |= FLAG_EMPTY;   // no sub-chunk with weight
-  if (S > 0.0 && sh.sel_sub >= 0) {
-    const int s0 = sh.sel_sub * DRAW_SUB;
+  // The selected sub-chunk's residual weights come from its list when the
+  // stream listed them: wave 0 loads the list (with its length), puts it in
+  // token order and picks; otherwise the sub-chunk is read again.
+  const int sel = S > 0.0 ? sh.sel_sub : -1;
+  const int64_t csel = (int64_t)b * a.nsub + sel;
+  int nl = DRAW_LIST + 1;
+  int32_t lxv = INT_MAX;
+  double lwv = 0.0;
+  if (S > 0.0 && sel >= 0 && !use_p && listing) {
+    nl = ldi(&a.lcount[csel]);
+    if (wv == 0 && lane < DRAW_LIST) {
+      lxv = ldi(&a.lx[csel * DRAW_LIST + lane]);
+      lwv = ld(&a.lw[csel * DRAW_LIST + lane]);
+    }
+  }
+  if (S > 0.0 && sel >= 0 && nl <= DRAW_LIST) {
+    if (wv == 0) {
+      const double tl = wk.u_final * S - sh.sel_before;
+      const bool on = lane < nl;
+      if (!on) lxv = INT_MAX;            // listed ids are distinct and below V
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < DRAW_LIST; ++j) rank += __shfl(lxv, j, WAVE) < lxv ? 1 : 0;
+      if (on) {
+        sh.lt[rank].x = lxv;
+        sh.lt[rank].w = lwv;
+      }
+      wave_sync_lds();
+      int32_t sx = -1;
+      double sw = 0.0;
+      if (on) {
+        sx = sh.lt[lane].x;
+        sw = sh.lt[lane].w;
+      }
+      const double incl = wave_incl_scan(sw);
+      // the first listed token reaching tl; the last one when rounding leaves
+      // tl above the list's total
+      const uint64_t reach = __ballot(on && incl >= tl);
+      const uint64_t has = __ballot(on);
+      const int pl = reach ? __ffsll((unsigned long long)reach) - 1
+                           : (has ? 63 - __clzll((long long)has) : -1);
+      token = pl >= 0 ? __shfl(sx, pl, WAVE) : -1;
+    }
+  } else if (S > 0.0 && sel >= 0) {
+    const int s0 = sel * DRAW_SUB;
     const double tl = wk.u_final * S - sh.sel_before;
     const int x0 = s0 + tid * GRP;
     double v[GRP];

@@ -54,10 +54,13 @@ def test_workspace_bytes(lib):
     assert a > 0 and a % 256 == 0
     assert ws(1, 4, 1000) > 0
     # room for the row statistics (32 B per row), the uniforms (8 B per slot),
-    # the draw's sub-chunk sums (16 B per 2048 tokens per request) and the
-    # per-request arrival counters
+    # the draw's sub-chunk sums (16 B per 2048 tokens per request) and lists
+    # of up to 32 kept tokens per sub-chunk (a 4-byte length, 4-byte ids,
+    # 8-byte weights), and the per-request arrival counters
     B, g, V = 128, 8, 151936
-    assert a >= B * (2 * g + 1) * 32 + B * (g + 1) * 8 + B * -(-V // 2048) * 16 + B * 4
+    nsub = -(-V // 2048)
+    assert a >= (B * (2 * g + 1) * 32 + B * (g + 1) * 8 + B * nsub * 16
+                 + B * nsub * (4 + 32 * 12) + B * 4)
     for bad in [(0, 4, 10), (1, 0, 10), (1, 64, 10), (1, 4, 0), (2**30, 63, 10)]:
         assert ws(*bad) == 0, bad
 

@@ -181,3 +181,37 @@ def test_dense_truncated_targets_at_a_rejection(k):
     xs = pu.oracle_proposals(wl, draft_sampler=samp)
     got, ref = _check(wl, xs, samp, seed=9, where=f"top-k {k}")
     assert np.any(got["num_accepted"] < gamma)      # rejections take the queued path
+
+
+@pytest.mark.parametrize("K", [1, 31, 32, 33, 64])
+def test_residual_draw_from_one_crowded_sub_chunk(K):
+    # target rows keep their top K tokens, all in the second sub-chunk of 2048
+    # tokens and at distinct values; the draft rows are low there, so the
+    # proposals are rejected at once and every kept token carries residual
+    # weight p. The selecting workgroup draws from that sub-chunk's list of K
+    # weighted tokens (in lane order; a list holds 32 at most, longer ones are
+    # read again from the rows). Sixteen requests draw at sixteen uniforms.
+    from lossless_draft_verification_sample_amd import synth
+    V, B, gamma = 3 * 2048 + 100, 16, 2
+    wl = pu.make("c3a", B=B, gamma=gamma, V=V, boost="none", target_sd=1.0, draft_sd=1.0,
+                 seed=80 + K)
+    rng = np.random.default_rng(80 + K)
+    t, d = wl.target.copy(), wl.draft.copy()
+    for b in range(B):
+        for i in range(gamma + 1):
+            pos = 2048 + rng.choice(2048, K, replace=False)
+            t[b, i, pos] = 20.0 + 0.125 * rng.choice(96, K, replace=False)
+            if i < gamma:
+                d[b, i, pos] = -10.0
+    wl.target_bits = synth.f32_to_bf16_bits(t)
+    wl.draft_bits = synth.f32_to_bf16_bits(d)
+    wl.target = synth.bf16_bits_to_f32(wl.target_bits)
+    wl.draft = synth.bf16_bits_to_f32(wl.draft_bits)
+    samp = (1.0, K, 1.0)
+    xs = pu.oracle_proposals(wl, draft_sampler=samp)
+    got, _ = _check(wl, xs, samp, seed=11, offset=2, where=f"crowded sub-chunk K={K}")
+    assert np.all(got["num_accepted"] == 0)
+    picked = got["tokens"][:, 0]
+    assert np.all((picked >= 2048) & (picked < 4096))
+    if K > 1:
+        assert len(set(picked.tolist())) > 1
