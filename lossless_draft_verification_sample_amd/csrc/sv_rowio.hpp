@@ -24,12 +24,14 @@ struct Group {
   u32x4 w[sizeof(Elem) == 2 ? 1 : 2];
 };
 
-template <typename Elem>
+// NT: the aligned bf16 load is nontemporal.
+template <typename Elem, bool NT = false>
 __device__ __forceinline__ void load_group(const void* row, int x0, int V, bool vec, Group<Elem>& g) {
   const Elem* e = (const Elem*)row;
   if constexpr (sizeof(Elem) == 2) {
     if (vec) {
-      g.w[0] = *(const u32x4*)(e + x0);   // V % 8 == 0 on this path
+      const u32x4* p = (const u32x4*)(e + x0);   // V % 8 == 0 on this path
+      g.w[0] = NT ? __builtin_nontemporal_load(p) : *p;
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -178,11 +180,13 @@ struct alignas(8) QueuedTok {
   float z;   // the leading row's logit
 };
 
-// One logit of a row as float (a single-element read).
+// One logit of a row as float (a single-element read). Nontemporal: these
+// gathers hit scattered cache lines that nothing reads again, and so they do
+// not displace the lines of the rows being streamed.
 template <typename Elem>
 __device__ __forceinline__ float load_logit(const void* row, int x) {
-  if constexpr (sizeof(Elem) == 2) return bf16_to_f32(((const uint16_t*)row)[x]);
-  return ((const float*)row)[x];
+  if constexpr (sizeof(Elem) == 2) return bf16_to_f32(__builtin_nontemporal_load((const uint16_t*)row + x));
+  return __builtin_nontemporal_load((const float*)row + x);
 }
 
 // Orders a wave's LDS writes before its later LDS reads (and the reverse).

@@ -34,6 +34,10 @@ namespace sv {
 constexpr int DR_THREADS = 256;
 constexpr int DR_NW = DR_THREADS / WAVE;
 static_assert(DR_NW == DRAW_WAVES, "the host sizes dense draw splits by this");
+// bf16 rows are read with nontemporal loads (measured faster in this kernel;
+// fp32 rows, slower)
+template <typename Elem>
+constexpr bool DR_NT = sizeof(Elem) == 2;
 constexpr int GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
 static_assert(DRAW_SUB == DR_THREADS * GRP, "one group of GRP logits per thread per sub-chunk");
 
@@ -456,8 +460,8 @@ void draw_kernel(DrawArgs a) {
       for (int k = 0; k < GPL; ++k) {
         const int x0 = sbase + (lane + k * WAVE) * GRP;
         if (x0 < a.V) {
-          load_group<Elem>(r.trow, x0, a.V, a.vec, tn[k]);
-          if constexpr (MODE == 2) load_group<Elem>(r.drow, x0, a.V, a.vec, dn[k]);
+          load_group<Elem, DR_NT<Elem>>(r.trow, x0, a.V, a.vec, tn[k]);
+          if constexpr (MODE == 2) load_group<Elem, DR_NT<Elem>>(r.drow, x0, a.V, a.vec, dn[k]);
         }
       }
     };
@@ -555,7 +559,7 @@ void draw_kernel(DrawArgs a) {
           for (int k = 0; k < GPL; ++k) {
             if (!km[k]) continue;
             const int x0 = sbase + (lane + k * WAVE) * GRP;
-            load_group<Elem>(r.drow, x0, a.V, a.vec, dg[k]);
+            load_group<Elem, DR_NT<Elem>>(r.drow, x0, a.V, a.vec, dg[k]);
             if (dmask) mask_group<Elem>(dg[k], bm_group(sh.bmd, x0 - tok0));
             if (dpen) penalize_group<Elem>(dg[k], bm_group(sh.bmp, x0 - tok0), rq.pd);
           }
@@ -615,8 +619,8 @@ void draw_kernel(DrawArgs a) {
     const int x0 = s0 + tid * GRP;
     Group<Elem> tg, dg;
     if (x0 < a.V) {
-      load_group<Elem>(r.trow, x0, a.V, a.vec, tg);
-      if (r.drow && !use_p) load_group<Elem>(r.drow, x0, a.V, a.vec, dg);
+      load_group<Elem, DR_NT<Elem>>(r.trow, x0, a.V, a.vec, tg);
+      if (r.drow && !use_p) load_group<Elem, DR_NT<Elem>>(r.drow, x0, a.V, a.vec, dg);
     }
     if (dmask && !use_p) {
       mark_bans(sh.bmd, DRAW_SUB, dbl, dnb, dban0, s0, a.V);
