@@ -31,6 +31,11 @@
 
 namespace sv {
 
+// bf16 rows are streamed with nontemporal loads (measured faster, and the
+// next kernels find the caches less disturbed)
+template <typename Elem>
+constexpr bool OV_NT = sizeof(Elem) == 2;
+
 constexpr int OV_THREADS = 256;
 constexpr int OV_NW = OV_THREADS / WAVE;
 constexpr int OV_GPL = DRAW_SUB / GRP / WAVE;   // groups per lane when a wave owns a sub-chunk
@@ -136,8 +141,8 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, Shared& sh, int wv,
     for (int k = 0; k < OV_GPL; ++k) {
       const int x0 = sbase + (lane + k * WAVE) * GRP;
       if (x0 < r.V) {
-        if constexpr (FULL_T) load_group<Elem>(r.trow, x0, r.V, r.vec, tn[k]);
-        if constexpr (FULL_D) load_group<Elem>(r.drow, x0, r.V, r.vec, dn[k]);
+        if constexpr (FULL_T) load_group<Elem, OV_NT<Elem>>(r.trow, x0, r.V, r.vec, tn[k]);
+        if constexpr (FULL_D) load_group<Elem, OV_NT<Elem>>(r.drow, x0, r.V, r.vec, dn[k]);
       }
     }
   };
@@ -230,7 +235,7 @@ __device__ __forceinline__ double ov_stream(const OvPair& r, Shared& sh, int wv,
           if (!km[k]) continue;
           const int x0 = sbase + (lane + k * WAVE) * GRP;
           Group<Elem> og;
-          load_group<Elem>(orow, x0, r.V, r.vec, og);
+          load_group<Elem, OV_NT<Elem>>(orow, x0, r.V, r.vec, og);
           if (open_) penalize_group<Elem>(og, pen_bits(x0 - r.tok0), oth);
           const Group<Elem>& lg = LEAD == 1 ? dg[k] : tg[k];
           const uint32_t ob = obits(x0 - r.tok0);
