@@ -198,7 +198,7 @@ __device__ __forceinline__ void for_each_elem(const Elem* rowp, int V, F&& f) {
 #pragma unroll
     for (int u = 0; u < GEN_U; ++u) {
       const int k = k0 + u * RS_THREADS;
-      if (k < nchunk) v[u] = body[k];
+      if (k < nchunk) v[u] = __builtin_nontemporal_load(body + k);   // streamed: nontemporal
     }
   };
   auto run = [&](const u32x4(&v)[GEN_U], int k0) {
