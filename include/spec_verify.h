@@ -215,11 +215,14 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, sv_d
  * harnesses that forbid hipMalloc). Arguments, outputs and errors are those of
  * spec_verify_sample; the workspace is a static device array of
  * SV_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held until
- * the process ends. The call allocates nothing. Sizes whose
- * spec_verify_workspace_bytes exceed SV_NOALLOC_SCRATCH_BYTES return
- * SV_ESCRATCH (c5-sized batches, B = 128, gamma = 8, V = 151936, need about
- * 4.0 MB). The first call on a device resolves that device's array address
- * (SV_EHIP if it cannot). Every call on one GPU shares its array: calls that
+ * the process ends. The call allocates nothing. When
+ * spec_verify_workspace_bytes exceeds SV_NOALLOC_SCRATCH_BYTES, the call runs
+ * without the final draw's lists of kept tokens (the last part of that size:
+ * 388 bytes per request and 2048-token sub-chunk), with the same outputs;
+ * sizes whose remaining workspace still exceeds the array return SV_ESCRATCH
+ * (c5-sized batches, B = 128, gamma = 8, V = 151936, need about 4.0 MB with
+ * the lists and 0.3 MB without). The first call on a device resolves that
+ * device's array address (SV_EHIP if it cannot). Every call on one GPU shares its array: calls that
  * may overlap on one GPU (different streams, or different host threads)
  * race and must be serialised by the caller; calls in order on one stream are
  * safe. Nothing needs clearing: every call initialises what it reads. */

@@ -31,7 +31,10 @@ constexpr size_t WS_ALIGN = 256;
 size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 struct Layout {
-  size_t stats, unif, sums, lcount, lx, lw, tickets, ov_partial, ov_tickets, total;
+  size_t stats, unif, sums, tickets, ov_partial, ov_tickets;
+  size_t base;                // bytes up to here: everything but the draw's lists
+  size_t lcount, lx, lw;      // the draw's kept-token lists (optional)
+  size_t total;
   int nsub;
   int ov_spp, ov_parts;
 };
@@ -87,18 +90,19 @@ bool layout(int32_t B, int32_t gamma, int32_t V, Layout* L) {
   off = align_up(off + (size_t)B * (size_t)(gamma + 1) * sizeof(double));
   L->sums = off;
   off = align_up(off + (size_t)B * (size_t)nsub * sizeof(sv::ChunkSums));
-  L->lcount = off;
-  off = align_up(off + (size_t)B * (size_t)nsub * sizeof(int32_t));
-  L->lx = off;
-  off = align_up(off + (size_t)B * (size_t)nsub * sv::DRAW_LIST * sizeof(int32_t));
-  L->lw = off;
-  off = align_up(off + (size_t)B * (size_t)nsub * sv::DRAW_LIST * sizeof(double));
   L->tickets = off;
   off = align_up(off + (size_t)B * sizeof(int32_t));
   L->ov_partial = off;
   off = align_up(off + (size_t)pairs * (size_t)parts * sizeof(double));
   L->ov_tickets = off;
   off = align_up(off + (size_t)pairs * sizeof(int32_t));
+  L->base = off;
+  L->lcount = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sizeof(int32_t));
+  L->lx = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sv::DRAW_LIST * sizeof(int32_t));
+  L->lw = off;
+  off = align_up(off + (size_t)B * (size_t)nsub * sv::DRAW_LIST * sizeof(double));
   L->total = off;
   return true;
 }
@@ -221,13 +225,20 @@ int sample_impl(const void* target_logits, const void* draft_logits, sv_dtype dt
   if (((uintptr_t)target_logits % es) || ((uintptr_t)draft_logits % es)) return SV_EINVAL;
   Layout L;
   if (!layout(B, gamma, V, &L)) return SV_ESIZE;
+  // The static scratch holds the draw's lists when they fit; larger sizes run
+  // without them (the selection then rereads its sub-chunk: same results).
+  bool lists = true;
   if (use_scratch) {
-    if (L.total > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ESCRATCH;
+    if (L.total > (size_t)SV_NOALLOC_SCRATCH_BYTES) {
+      if (L.base > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ESCRATCH;
+      lists = false;
+    }
     const int rc = scratch_ptr(&workspace);
     if (rc != SV_OK) return rc;
     workspace_bytes = SV_NOALLOC_SCRATCH_BYTES;
   }
-  if (!workspace || ((uintptr_t)workspace % WS_ALIGN) || workspace_bytes < L.total)
+  if (!workspace || ((uintptr_t)workspace % WS_ALIGN) ||
+      workspace_bytes < (lists ? L.total : L.base))
     return SV_EWORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
@@ -293,9 +304,9 @@ int sample_impl(const void* target_logits, const void* draft_logits, sv_dtype dt
     a.stats = stats;
     a.uniforms = uniforms ? uniforms : unif;
     a.sums = sums;
-    a.lcount = (int32_t*)(ws + L.lcount);
-    a.lx = (int32_t*)(ws + L.lx);
-    a.lw = (double*)(ws + L.lw);
+    a.lcount = lists ? (int32_t*)(ws + L.lcount) : nullptr;
+    a.lx = lists ? (int32_t*)(ws + L.lx) : nullptr;
+    a.lw = lists ? (double*)(ws + L.lw) : nullptr;
     a.tickets = tickets;
     a.out_tokens = out_tokens;
     a.out_num_accepted = out_num_accepted;

@@ -59,7 +59,8 @@ struct DrawArgs {
   const RowStat* stats;
   const double* uniforms;     // [B][gamma+1]: the caller's, or those of the row pass
   ChunkSums* sums;            // [B][nsub]
-  int32_t* lcount;            // [B][nsub]: tokens listed, DRAW_LIST + 1 when not listed
+  int32_t* lcount;            // [B][nsub]: tokens listed, DRAW_LIST + 1 when not listed;
+                              // nullptr: no lists (every selection rereads its sub-chunk)
   int32_t* lx;                // [B][nsub][DRAW_LIST]: their ids
   double* lw;                 // [B][nsub][DRAW_LIST]: their draw weights
   int32_t* tickets;           // [B], zero on entry

@@ -290,9 +290,11 @@ __device__ __forceinline__ void mask_group(Group<Elem>& g, uint32_t bits) {
 
 // MIXED: per-request draft lengths, samplers (greedy requests included),
 // draft ban lists and repetition penalties; the plain variant carries none of
-// that logic. The bf16 MIXED variant is held to 128 VGPRs (four waves per
-// SIMD, so all workgroups of a launch stay resident; one spill).
-template <typename Elem, bool MIXED>
+// that logic. LISTS: the kept-token lists are in use (plain batches whose
+// workspace holds them; a run-time test of the pointer instead cost c5's
+// draw 2 µs). The bf16 MIXED variant is held to 128 VGPRs (four waves per
+// SIMD, so all workgroups of a launch stay resident).
+template <typename Elem, bool MIXED, bool LISTS>
 __global__ __launch_bounds__(DR_THREADS, sizeof(Elem) == 2 ? (MIXED ? 4 : 1) : 2)
 void draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
@@ -362,8 +364,10 @@ void draw_kernel(DrawArgs a) {
   //   compaction when at most 64 tokens are kept, in place when more are.
   const bool sparse = r.ts.tau > -INFINITY;
   // kept-token lists of the sub-chunks for the selection (truncated target
-  // rows of plain batches; in mixed batches they measured slower)
-  const bool listing = !MIXED && sparse;
+  // rows of plain batches, when the workspace holds them; in mixed batches
+  // they measured slower)
+  static_assert(!(MIXED && LISTS), "mixed batches take no lists");
+  const bool listing = LISTS && sparse;
   const bool queued = sparse && r.drow;
   // the kept tokens of the wave's groups of one sub-chunk, and their number
   auto sub_mask = [&](int sbase, const Group<Elem>(&tg)[GPL], uint32_t(&km)[GPL]) {
@@ -788,16 +792,21 @@ int launch_draw(const DrawArgs& a, int B, hipStream_t st) {
   const dim3 grid((unsigned)(a.nwg * B)), block(DR_THREADS);
   const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d || a.req.pen_t ||
                      a.req.pen_d || a.req.history;
+  const bool lists = a.lcount != nullptr;
   if (a.bf16) {
     if (mixed)
-      hipLaunchKernelGGL((draw_kernel<uint16_t, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<uint16_t, true, false>), grid, block, 0, st, a);
+    else if (lists)
+      hipLaunchKernelGGL((draw_kernel<uint16_t, false, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((draw_kernel<uint16_t, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<uint16_t, false, false>), grid, block, 0, st, a);
   } else {
     if (mixed)
-      hipLaunchKernelGGL((draw_kernel<float, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<float, true, false>), grid, block, 0, st, a);
+    else if (lists)
+      hipLaunchKernelGGL((draw_kernel<float, false, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((draw_kernel<float, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<float, false, false>), grid, block, 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

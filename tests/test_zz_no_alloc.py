@@ -86,3 +86,36 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
                                         None, None, torch.cuda.current_stream().cuda_stream)
     assert rc == L.SV_ESCRATCH
     assert "scratch" in lib.spec_verify_strerror(rc).decode()
+
+
+def test_noalloc_beyond_the_draw_lists():
+    # B = 700, V = 64000: everything but the draw's kept-token lists fits the
+    # scratch array, the lists do not, so the no-alloc call runs without them
+    # (its selections reread their sub-chunks) while the workspace call uses
+    # them; the outputs must agree. A smaller call follows, with lists again.
+    import torch
+    from lossless_draft_verification_sample_amd import _lib as L
+    lib = L.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    for k, (B, gamma, V) in enumerate([(700, 2, 64000), (40, 3, 64000)]):
+        print(f"[noalloc] B={B} gamma={gamma} V={V} random bf16 logits", flush=True)
+        gen.manual_seed(321 + k)
+        t = (torch.randn((B, gamma + 1, V), generator=gen, device=dev) * 3).to(torch.bfloat16)
+        d = (torch.randn((B, gamma, V), generator=gen, device=dev) * 3).to(torch.bfloat16)
+        xs = torch.randint(0, V, (B, gamma), generator=gen, device=dev, dtype=torch.int32)
+        bans = torch.randint(-2, V, (B, 16), generator=gen, device=dev, dtype=torch.int32)
+        need = lib.spec_verify_workspace_bytes(B, gamma, V)
+        assert (need > L.SV_NOALLOC_SCRATCH_BYTES) == (k == 0)
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+        samp = (0.8, 0, 0.9)
+        ref = _outs(torch, B, gamma, dev)
+        got = _outs(torch, B, gamma, dev)
+        assert _call(lib, False, t, d, xs, bans, samp, 9, k, ref, ws, stream) == L.SV_OK
+        assert _call(lib, True, t, d, xs, bans, samp, 9, k, got, None, stream) == L.SV_OK
+        torch.cuda.synchronize()
+        for key in ref:
+            assert torch.equal(got[key], ref[key]), (B, key)
+        n = got["n"].cpu().numpy()
+        assert np.all((n >= 0) & (n <= gamma)) and np.any(n < gamma)
