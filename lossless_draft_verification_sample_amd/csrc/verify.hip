@@ -290,11 +290,14 @@ __device__ __forceinline__ void mask_group(Group<Elem>& g, uint32_t bits) {
 
 // MIXED: per-request draft lengths, samplers (greedy requests included),
 // draft ban lists and repetition penalties; the plain variant carries none of
-// that logic. LISTS: the kept-token lists are in use (plain batches whose
-// workspace holds them; a run-time test of the pointer instead cost c5's
-// draw 2 µs). The bf16 MIXED variant is held to 128 VGPRs (four waves per
-// SIMD, so all workgroups of a launch stay resident).
-template <typename Elem, bool MIXED, bool LISTS>
+// that logic. Plain batches also choose at launch (DR_*): whether the
+// kept-token lists are in use (the workspace holds them; a run-time test of
+// the pointer instead cost c5's draw 2 µs), or whether the target sampler
+// truncates nothing, so that the code for truncated rows is left out (c3a
+// and c3b 0.4-0.5 µs faster). The bf16 MIXED variant is held to 128 VGPRs
+// (four waves per SIMD, so all workgroups of a launch stay resident).
+constexpr int DR_NOLIST = 0, DR_LISTS = 1, DR_UNTRUNC = 2;
+template <typename Elem, bool MIXED, int KIND>
 __global__ __launch_bounds__(DR_THREADS, sizeof(Elem) == 2 ? (MIXED ? 4 : 1) : 2)
 void draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
@@ -362,12 +365,13 @@ void draw_kernel(DrawArgs a) {
   // - Otherwise (the bonus draw, or an untruncated target whose draft row is
   //   streamed alongside) the weights come from registers: through a per-wave
   //   compaction when at most 64 tokens are kept, in place when more are.
-  const bool sparse = r.ts.tau > -INFINITY;
+  // (a target sampler that truncates nothing leaves tau at -inf)
+  const bool sparse = KIND != DR_UNTRUNC && r.ts.tau > -INFINITY;
   // kept-token lists of the sub-chunks for the selection (truncated target
   // rows of plain batches, when the workspace holds them; in mixed batches
   // they measured slower)
-  static_assert(!(MIXED && LISTS), "mixed batches take no lists");
-  const bool listing = LISTS && sparse;
+  static_assert(!MIXED || KIND == DR_NOLIST, "mixed batches take the general variant");
+  const bool listing = KIND == DR_LISTS && sparse;
   const bool queued = sparse && r.drow;
   // the kept tokens of the wave's groups of one sub-chunk, and their number
   auto sub_mask = [&](int sbase, const Group<Elem>(&tg)[GPL], uint32_t(&km)[GPL]) {
@@ -792,21 +796,26 @@ int launch_draw(const DrawArgs& a, int B, hipStream_t st) {
   const dim3 grid((unsigned)(a.nwg * B)), block(DR_THREADS);
   const bool mixed = a.req.gammas || a.req.ts || a.req.ds || a.req.banned_d || a.req.pen_t ||
                      a.req.pen_d || a.req.history;
-  const bool lists = a.lcount != nullptr;
+  const bool untrunc = a.st.top_k == 0 && a.st.top_p >= 1.0f;
+  const int kind = untrunc ? DR_UNTRUNC : (a.lcount ? DR_LISTS : DR_NOLIST);
   if (a.bf16) {
     if (mixed)
-      hipLaunchKernelGGL((draw_kernel<uint16_t, true, false>), grid, block, 0, st, a);
-    else if (lists)
-      hipLaunchKernelGGL((draw_kernel<uint16_t, false, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<uint16_t, true, DR_NOLIST>), grid, block, 0, st, a);
+    else if (kind == DR_UNTRUNC)
+      hipLaunchKernelGGL((draw_kernel<uint16_t, false, DR_UNTRUNC>), grid, block, 0, st, a);
+    else if (kind == DR_LISTS)
+      hipLaunchKernelGGL((draw_kernel<uint16_t, false, DR_LISTS>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((draw_kernel<uint16_t, false, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<uint16_t, false, DR_NOLIST>), grid, block, 0, st, a);
   } else {
     if (mixed)
-      hipLaunchKernelGGL((draw_kernel<float, true, false>), grid, block, 0, st, a);
-    else if (lists)
-      hipLaunchKernelGGL((draw_kernel<float, false, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<float, true, DR_NOLIST>), grid, block, 0, st, a);
+    else if (kind == DR_UNTRUNC)
+      hipLaunchKernelGGL((draw_kernel<float, false, DR_UNTRUNC>), grid, block, 0, st, a);
+    else if (kind == DR_LISTS)
+      hipLaunchKernelGGL((draw_kernel<float, false, DR_LISTS>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((draw_kernel<float, false, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((draw_kernel<float, false, DR_NOLIST>), grid, block, 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
