@@ -215,3 +215,17 @@ def test_residual_draw_from_one_crowded_sub_chunk(K):
     assert np.all((picked >= 2048) & (picked < 4096))
     if K > 1:
         assert len(set(picked.tolist())) > 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_truncating_sampler_that_keeps_everything(dtype):
+    # top-k above V: the sampler truncates nothing, yet the batch is drawn by
+    # the kernel for truncating samplers, whose rejections take the queued
+    # mode; every sub-chunk then overflows the queue and is evaluated in place
+    V, B, gamma = 5000, 6, 3
+    wl = pu.make("c3a", B=B, gamma=gamma, V=V, dtype=dtype, boost="none", target_sd=1.0,
+                 draft_sd=1.0, seed=81)
+    samp = (0.9, V + 5, 1.0)
+    xs = pu.oracle_proposals(wl, draft_sampler=samp)
+    got, _ = _check(wl, xs, samp, seed=4, where=f"top-k above V {dtype}")
+    assert np.any(got["num_accepted"] < gamma)
