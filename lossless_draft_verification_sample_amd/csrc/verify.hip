@@ -113,6 +113,17 @@ __device__ __forceinline__ double group_wsum(const DrawRow& r, const Group<Elem>
   return sw;
 }
 
+// Sum of p over the kept tokens of a group.
+template <typename Elem>
+__device__ __forceinline__ double group_psum(const DrawRow& r, const Group<Elem>& tg, uint32_t km,
+                                             const double* tab) {
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < GRP; ++e)
+    if ((km >> e) & 1u) s += tok_p(r, group_val<Elem>(tg, e), tab);
+  return s;
+}
+
 // Per-token draw weights of a group: w, or p when `use_p` (0 outside the mask).
 template <typename Elem>
 __device__ __forceinline__ void group_values(const DrawRow& r, const Group<Elem>& tg,
@@ -436,8 +447,11 @@ void draw_kernel(DrawArgs a) {
       nl = DRAW_LIST + 1;
     }
   };
-  // A sub-chunk's weight sum goes out as soon as its wave has it (the p sums,
-  // needed only when the residual has no mass, are left to the selection).
+  // A sub-chunk's weight sum goes out as soon as its wave has it. At a
+  // rejection, a sub-chunk without residual mass also publishes its p sum
+  // (lane_p() gives the lane's part, computed only then): when no sub-chunk
+  // has any, the draw falls back to p and finds every p sum published. (Made
+  // by the selecting workgroup alone instead, c5's 75 p sums took 50-90 µs.)
   // Publication
   // without a release fence: agent-scope atomic stores, which the hardware
   // writes through to the device-coherent level; every writer waits for its
@@ -449,12 +463,16 @@ void draw_kernel(DrawArgs a) {
   // of tokens with w > 0 (DRAW_LIST + 1: not listed), so that the selection
   // can pick from the list instead of reading the sub-chunk again.
   // (Untruncated rows keep nearly every token: no lists.)
-  auto publish = [&](int sl, double sw, int nl) {
+  auto publish = [&](int sl, double sw, int nl, auto&& lane_p) {
     sw = wave_total(sw);
+    const bool need_p = r.drow != nullptr && !(sw > 0.0);
+    double sp = 0.0;
+    if (need_p) sp = wave_total(lane_p());
     if (lane == 0) {
       const int64_t c = (int64_t)b * a.nsub + sub0 + sl;
       __hip_atomic_store(&a.sums[c].w, sw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (listing) __hip_atomic_store(&a.lcount[c], nl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (need_p) __hip_atomic_store(&a.sums[c].p, sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
   // The wave's sub-chunks, specialised by how the draft row is read: 0 =
@@ -525,7 +543,15 @@ void draw_kernel(DrawArgs a) {
           if (in) sw += qw[u];
           if (listing) nl = list_put(c, nl, in && qw[u] > 0.0, qx[u], qw[u]);
         }
-        publish(sl, sw, nl);
+        publish(sl, sw, nl, [&]() {
+          // from the queue in LDS (the registers of the batch are not kept for this)
+          double sp = 0.0;
+          for (int j = lane; j < qlen; j += WAVE) {
+            const QueuedTok t = sh.q[wv][j];
+            if (t.x >= lo && t.x < lo + DRAW_SUB) sp += tok_p(r, t.z, sh.etab);
+          }
+          return sp;
+        });
       }
       wave_sync_lds();
       qlen = 0;
@@ -551,11 +577,18 @@ void draw_kernel(DrawArgs a) {
       if (sl + DR_NW < nsl) issue(sl + DR_NW);
       uint32_t km[GPL];
       const uint32_t cnt = sub_mask(sbase, tg, km);
+      auto lane_p = [&]() {
+        double sp = 0.0;
+#pragma unroll
+        for (int k = 0; k < GPL; ++k)
+          if (km[k]) sp += group_psum<Elem>(r, tg[k], km[k], sh.etab);
+        return sp;
+      };
       if constexpr (MODE != 0) {
         double sw = 0.0;
         int nl;
         sub_sums(sbase, tg, dg, km, cnt, sw, nl);
-        publish(sl, sw, nl);
+        publish(sl, sw, nl, lane_p);
       } else {
         const uint32_t incl = wave_scan_dpp(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
         const int total = (int)lane63(incl);
@@ -575,7 +608,7 @@ void draw_kernel(DrawArgs a) {
 #pragma unroll
           for (int k = 0; k < GPL; ++k)
             if (km[k]) sw += group_wsum<Elem>(r, tg[k], dg[k], km[k], sh.etab);
-          publish(sl, sw, DRAW_LIST + 1);
+          publish(sl, sw, DRAW_LIST + 1, lane_p);
           continue;
         }
         // one iteration per kept token of the lane (the wave runs as many as
@@ -653,29 +686,14 @@ void draw_kernel(DrawArgs a) {
   for (int c = k0; c < k1; ++c) loc += ld(&cs[c].w);
   block_excl_scan2<DR_THREADS>(loc, 0.0, sh.scr, before, unused0, S, unused1);
   // Fall back to p when the residual has no mass (p and q then agree on every
-  // token). The stream summed only the residual, so the p sums of the
-  // sub-chunks are made here, one sub-chunk at a time.
+  // token): the stream published the p sum of every sub-chunk (none had
+  // residual mass), before the arrival tickets.
   bool use_p = false;
   if (!(S > 0.0) && n < g) {
     flags |= FLAG_RESIDUAL_ZERO;
     use_p = true;
-    // an empty target row keeps nothing: every p sum is 0
-    const int nsum = (r.ts.flags & FLAG_EMPTY) ? 0 : a.nsub;
-    for (int c = 0; c < nsum; ++c) {
-      double v[GRP];
-      sub_values(c * DRAW_SUB, true, v);
-      double ls = 0.0;
-#pragma unroll
-      for (int e = 0; e < GRP; ++e) ls += v[e];
-      double pb, tot;
-      block_excl_scan2<DR_THREADS>(ls, 0.0, sh.scr, pb, unused0, tot, unused1);
-      if (tid == 0) __hip_atomic_store(&cs[c].p, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
     loc = 0.0;
-    if (nsum > 0)
-      for (int c = k0; c < k1; ++c) loc += ld(&cs[c].p);
+    for (int c = k0; c < k1; ++c) loc += ld(&cs[c].p);
     block_excl_scan2<DR_THREADS>(loc, 0.0, sh.scr, before, unused0, S, unused1);
   }
   int32_t token = -1;

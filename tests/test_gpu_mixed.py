@@ -327,3 +327,42 @@ def test_penalty_at_the_history_limit(dtype, V):
                               banned, None, None, hist, pen_t, pen_d, dtype)
     _compare(got, ref, f"history limit {dtype}")
     assert not np.any(got["flags"] & oracle.FLAG_BAD_PARAM)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_residual_with_penalties(dtype):
+    # p == q on every row (same logits, samplers, bans and penalties on both
+    # sides) and a rejection forced at position 1: the residual has no mass,
+    # so the selecting workgroup makes the penalized p sums of all 35
+    # sub-chunks (three batches of at most 16, the last one ragged) and draws
+    # from p
+    V, B, g = 70001, 6, 3
+    wl = pu.make("c5", B=B, gamma=g, V=V, dtype=dtype, seed=131)
+    wl.draft = wl.target[:, :g].copy()
+    if wl.target_bits is not None:
+        wl.draft_bits = wl.target_bits[:, :g].copy()
+    rng = np.random.default_rng(132)
+    choices = [(0.8, 0, 0.9), (1.0, 0, 1.0), (0.7, 50, 1.0), (1.3, 0, 0.95), (0.9, 300, 0.8),
+               (1.1, 0, 1.0)]
+    ts = [choices[b % len(choices)] for b in range(B)]
+    gammas = np.full(B, g, np.int32)
+    banned = rng.integers(-1, V, (B, 24)).astype(np.int32)
+    hist, pen_t, _ = _penalty_setup(wl, seed=133)
+    pen_t = np.array([1.3, 2.0, 1.0, 1.5, 1.2, 1.8], np.float32)
+    xs = np.zeros((B, g), dtype=np.int32)
+    for b in range(B):
+        tb = [t for t in banned[b].tolist() if t >= 0]
+        for i in range(g):
+            pen = [t for t in np.concatenate([hist[b], xs[b, :i]]).tolist() if 0 <= t < V]
+            q = oracle.row_distribution(wl.draft[b, i].astype(np.float64), oracle.Sampler(*ts[b]),
+                                        tb, pen, float(pen_t[b]), dtype).p
+            xs[b, i] = oracle.sample_categorical(q, 1.0 - rng.random())[0]
+    xs[:, 1] = V + 1
+    got = _run_pen(wl, xs, ts, ts, gammas, banned, None, hist, pen_t, pen_t)
+    u = pu.philox_uniforms(4, 2, B, g)
+    ref = oracle.verify_batch(wl.target.astype(np.float64), wl.draft.astype(np.float64), xs, u,
+                              [oracle.Sampler(*s) for s in ts], [oracle.Sampler(*s) for s in ts],
+                              banned, None, gammas, hist, pen_t, pen_t, dtype)
+    _compare(got, ref, f"zero residual with penalties {dtype}")
+    assert np.all(got["flags"] & oracle.FLAG_RESIDUAL_ZERO)
+    assert np.all(got["num_accepted"] == 1)
