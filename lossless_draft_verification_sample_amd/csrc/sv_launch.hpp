@@ -13,7 +13,10 @@ namespace sv {
 // and the selection rescans a single sub-chunk.
 constexpr int DRAW_SUB = 2048;
 constexpr int DRAW_SPW_MAX = 16;
-constexpr int DRAW_TARGET_WGS = 1024;   // about four draw workgroups per CU
+// about 3.5 draw workgroups per CU: below the four per CU that can be resident,
+// so that a launch runs in one round with room to spare (1,024 for c5, 8 per
+// request, was 0.9 µs slower; B = 96 at 1,024 needed 1,056 and a second round)
+constexpr int DRAW_TARGET_WGS = 896;
 constexpr int DRAW_WAVES = 4;           // waves per draw workgroup
 // kept tokens a draw workgroup lists per sub-chunk of a truncated row (more:
 // the selection rescans the sub-chunk)
